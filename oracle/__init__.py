@@ -1,0 +1,23 @@
+"""CPU oracle for the quantized-weight GEMM (test infrastructure only).
+
+This package is the plain, slow, obviously correct definition of what the GPU
+library computes. It is used by ``tests/``, by ``__graft_entry__.smoke()`` and by
+the ``cpu_baseline`` leg of ``bench.py`` -- never by the library itself, which
+fails loudly if its HIP build is missing.
+
+* ``oracle.ref``     -- dequantize-then-matmul in fp64 (and exact integers for
+                        W4A8), following the MARLIN abstract's problem statement
+                        (fp16 activations times 4-bit weights, batched), the
+                        OdysseyLLM abstract (W4A8) and the 2-bit page's mixed
+                        2/4-bit groups.
+* ``oracle.layout``  -- an independent implementation of the repacked weight
+                        blob byte layout, for byte-exact checks of the GPU repack.
+* ``oracle.compare`` -- the fp16 output tolerance rule.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against values that
+do not come from the oracle itself (exact rational brute force, closed forms,
+hand-derived golden files, invariants). Nothing here shares code with the HIP
+library; inputs come from the separate ``synth`` module.
+"""
+
+from . import compare, layout, ref  # noqa: F401

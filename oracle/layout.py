@@ -1,0 +1,228 @@
+"""Independent implementation of the repacked weight blob layout (CPU, NumPy).
+
+The GPU repack reorders codes and scales into the order in which the GEMM
+kernels consume them (the "matrix preprocessing that optimizes data layout for
+subsequent computations" of the arbitrary-precision Tensor Core page, and the
+"memory alignment consideration" of the 2-bit page). This module builds the same
+bytes from the canonical arrays with NumPy index arithmetic, written from the
+layout specification alone, so the GPU blob can be compared byte for byte.
+
+Layout specification (all integers little-endian; G = K/128 groups,
+NB = N/16 column blocks, G8 = ceil(G/8); lane l in 0..63 has column
+c = l % 16 and quarter h = l // 16; every region starts at a multiple of 256
+bytes and its size is rounded up to 256):
+
+W4A16 (format 1)
+  codes   NB*G chunks of 1024 B, chunk (b, g) at (b*G + g)*1024. Lane l owns
+          16 B at +16*l: words t = 0..3. Word t holds the codes of
+          k = 128*g + 32*h + 8*t + e (e = 0..7), column n = 16*b + c, with
+          element e in nibble sigma(e): sigma(e) = e/2 for even e and
+          4 + (e-1)/2 for odd e.
+  scales  fp16 at index ((b*G8 + g8)*16 + c)*8 + j  = s[8*g8 + j][16*b + c]
+          (0 where 8*g8 + j >= G).
+
+W4A8 (format 2)
+  codes   same chunk geometry; element e of word t in nibble tau(e):
+          tau(e) = 2*e for e < 4 and 2*(e-4) + 1 for e >= 4; the nibble holds
+          the biased code (q mod 16) XOR 8 = q + 8 in 0..15.
+  gscales int8 at index ((b*G8 + g8)*16 + c)*8 + j = s_g[8*g8 + j][16*b + c].
+  cscales fp16[N] = s_c[n].
+
+W2W4 mixed (format 3)
+  base    NB*G chunks of 512 B, chunk (b, g) at (b*G + g)*512. Lane l owns 8 B
+          at +8*l: words s = 0, 1. For slot p = 0..7 let e = sigma^-1(p); bits
+          [4p, 4p+1] hold lo2 of the code at k = 128*g + 32*h + 8*(2s) + e and
+          bits [4p+2, 4p+3] hold lo2 of the code at k + 8 (word 2s+1).
+          lo2 = code & 3.
+  desc    8 B per chunk (b, g) at (b*G + g)*8: u32 off, u32 mask. mask bit c is
+          set when group (g, 16*b + c) is 4-bit; off is the count of 4-bit
+          groups in all chunks before (b, g) in (b*G + g) order.
+  scales  as W4A16.
+  high    for every 4-bit group (g, n = 16*b + c): 32 B at
+          32*(off(b, g) + rank(c)), rank(c) = set mask bits below c; quarter h
+          at +8*h holds 2 words in the base-plane arrangement but with
+          hi2 = (code >> 2) & 3.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128
+
+FMT_W4A16 = 1
+FMT_W4A8 = 2
+FMT_W2W4 = 3
+
+
+def _align256(x: int) -> int:
+    return (x + 255) // 256 * 256
+
+
+def _sigma(e: int) -> int:
+    return e // 2 if e % 2 == 0 else 4 + (e - 1) // 2
+
+
+def _sigma_inv(p: int) -> int:
+    return 2 * p if p < 4 else 2 * (p - 4) + 1
+
+
+def _tau(e: int) -> int:
+    return 2 * e if e < 4 else 2 * (e - 4) + 1
+
+
+def _codes_by_lane(q: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Rearrange codes ``[K][N]`` into ``[NB][G][lane=16h+c][t][e]``.
+
+    k = 128*g + 32*h + 8*t + e, n = 16*b + c.
+    """
+    G, NB = K // GROUP, N // 16
+    x = np.asarray(q).reshape(G, 4, 4, 8, NB, 16)      # g, h, t, e, b, c
+    x = x.transpose(4, 0, 1, 5, 2, 3)                  # b, g, h, c, t, e
+    return x.reshape(NB, G, 64, 4, 8)
+
+
+def _scale_region(values: np.ndarray, G: int, N: int, dtype) -> bytes:
+    """``[G][N]`` -> ``[NB][G8][16][8]`` (zero padded in g)."""
+    NB, G8 = N // 16, (G + 7) // 8
+    pad = np.zeros((G8 * 8, N), dtype=dtype)
+    pad[:G] = np.asarray(values).astype(dtype)
+    x = pad.reshape(G8, 8, NB, 16).transpose(2, 0, 3, 1)  # b, g8, c, j
+    return np.ascontiguousarray(x).tobytes()
+
+
+def _pad_to(buf: bytes, size: int) -> bytes:
+    assert len(buf) <= size
+    return buf + bytes(size - len(buf))
+
+
+def _unpack_nibbles(qw: np.ndarray) -> np.ndarray:
+    qw = np.asarray(qw, dtype=np.uint32)
+    Kq, N = qw.shape
+    out = np.empty((Kq, 8, N), dtype=np.uint32)
+    for j in range(8):
+        out[:, j, :] = (qw >> np.uint32(4 * j)) & np.uint32(0xF)
+    return out.reshape(Kq * 8, N)
+
+
+def _check_shape(K: int, N: int):
+    if K % GROUP or N % 64 or K <= 0 or N <= 0:
+        raise ValueError("K must be a positive multiple of 128 and N of 64")
+
+
+# --------------------------------------------------------------------------- sizes
+def packed_bytes(fmt: int, K: int, N: int, n4: int = 0) -> int:
+    _check_shape(K, N)
+    G, NB = K // GROUP, N // 16
+    G8 = (G + 7) // 8
+    if fmt == FMT_W4A16:
+        return _align256(NB * G * 1024) + _align256(NB * G8 * 256)
+    if fmt == FMT_W4A8:
+        return _align256(NB * G * 1024) + _align256(NB * G8 * 128) + _align256(2 * N)
+    if fmt == FMT_W2W4:
+        return (_align256(NB * G * 512) + _align256(NB * G * 8) + _align256(NB * G8 * 256)
+                + _align256(32 * n4))
+    raise ValueError("unknown format")
+
+
+# --------------------------------------------------------------------------- W4A16
+def blob_w4a16(qw: np.ndarray, scales: np.ndarray) -> bytes:
+    qw = np.asarray(qw, dtype=np.uint32)
+    K, N = qw.shape[0] * 8, qw.shape[1]
+    _check_shape(K, N)
+    G, NB = K // GROUP, N // 16
+    q = _codes_by_lane(_unpack_nibbles(qw), K, N)         # [NB][G][64][4][8]
+    words = np.zeros(q.shape[:4], dtype=np.uint32)
+    for e in range(8):
+        words |= q[..., e].astype(np.uint32) << np.uint32(4 * _sigma(e))
+    codes = _pad_to(words.astype("<u4").tobytes(), _align256(NB * G * 1024))
+    sc = _pad_to(_scale_region(np.asarray(scales, dtype=np.float16), G, N, np.float16),
+                 _align256(NB * ((G + 7) // 8) * 256))
+    out = codes + sc
+    assert len(out) == packed_bytes(FMT_W4A16, K, N)
+    return out
+
+
+# --------------------------------------------------------------------------- W4A8
+def blob_w4a8(qw: np.ndarray, group_scales: np.ndarray, chan_scales: np.ndarray) -> bytes:
+    qw = np.asarray(qw, dtype=np.uint32)
+    K, N = qw.shape[0] * 8, qw.shape[1]
+    _check_shape(K, N)
+    G, NB = K // GROUP, N // 16
+    biased = _unpack_nibbles(qw) ^ np.uint32(8)            # two's complement q -> q + 8
+    q = _codes_by_lane(biased, K, N)
+    words = np.zeros(q.shape[:4], dtype=np.uint32)
+    for e in range(8):
+        words |= q[..., e].astype(np.uint32) << np.uint32(4 * _tau(e))
+    codes = _pad_to(words.astype("<u4").tobytes(), _align256(NB * G * 1024))
+    gs = _pad_to(_scale_region(np.asarray(group_scales, dtype=np.int8), G, N, np.int8),
+                 _align256(NB * ((G + 7) // 8) * 128))
+    cs = _pad_to(np.asarray(chan_scales, dtype=np.float16).tobytes(), _align256(2 * N))
+    out = codes + gs + cs
+    assert len(out) == packed_bytes(FMT_W4A8, K, N)
+    return out
+
+
+# --------------------------------------------------------------------------- W2W4
+def _bitmap_mask(bitmap: np.ndarray, G: int, N: int) -> np.ndarray:
+    bitmap = np.asarray(bitmap, dtype=np.uint32)
+    n = np.arange(N)
+    return ((bitmap[:G, n // 32] >> (n % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+def _two_bit_words(plane: np.ndarray) -> np.ndarray:
+    """``[NB][G][64][4][8]`` 2-bit values -> ``[NB][G][64][2]`` u32 words."""
+    out = np.zeros(plane.shape[:3] + (2,), dtype=np.uint32)
+    for s in range(2):
+        for p in range(8):
+            e = _sigma_inv(p)
+            out[..., s] |= plane[..., 2 * s, e].astype(np.uint32) << np.uint32(4 * p)
+            out[..., s] |= plane[..., 2 * s + 1, e].astype(np.uint32) << np.uint32(4 * p + 2)
+    return out
+
+
+def blob_w2w4(codes_u8: np.ndarray, bitmap: np.ndarray, scales: np.ndarray) -> bytes:
+    codes_u8 = np.asarray(codes_u8, dtype=np.uint8)
+    K, N = codes_u8.shape
+    _check_shape(K, N)
+    G, NB = K // GROUP, N // 16
+    G8 = (G + 7) // 8
+    mask = _bitmap_mask(bitmap, G, N)                      # [G][N]
+    q = _codes_by_lane(codes_u8, K, N)                     # [NB][G][64][4][8]
+    base = _two_bit_words(q & np.uint8(3))                 # [NB][G][64][2]
+    high = _two_bit_words((q >> np.uint8(2)) & np.uint8(3))
+    # descriptors in chunk order b*G + g
+    m_bg = mask.reshape(G, NB, 16).transpose(1, 0, 2)      # [NB][G][16]
+    cnt = m_bg.sum(axis=2).ravel()
+    off = np.concatenate([[0], np.cumsum(cnt)[:-1]]).astype(np.uint32)
+    bits = (m_bg.astype(np.uint32) << np.arange(16, dtype=np.uint32)).sum(axis=2).ravel()
+    desc = np.stack([off, bits.astype(np.uint32)], axis=1).astype("<u4")
+    n4 = int(cnt.sum())
+    # high plane: quarter pieces of 4-bit groups in (b, g, c) order
+    hi_words = high.reshape(NB, G, 4, 16, 2).transpose(0, 1, 3, 2, 4)   # b, g, c, h, s
+    sel = hi_words[m_bg]                                    # [n4][4][2] in (b, g, c) order
+    hbytes = sel.astype("<u4").tobytes()
+    out = (_pad_to(base.astype("<u4").tobytes(), _align256(NB * G * 512))
+           + _pad_to(desc.tobytes(), _align256(NB * G * 8))
+           + _pad_to(_scale_region(np.asarray(scales, dtype=np.float16), G, N, np.float16),
+                     _align256(NB * G8 * 256))
+           + _pad_to(hbytes, _align256(32 * n4)))
+    assert len(out) == packed_bytes(FMT_W2W4, K, N, n4)
+    return out
+
+
+# --------------------------------------------------------------------------- decoding
+def decode_w4a16(blob: bytes, K: int, N: int):
+    """Inverse of ``blob_w4a16``: returns (codes uint8[K][N], scales fp16[G][N])."""
+    G, NB = K // GROUP, N // 16
+    G8 = (G + 7) // 8
+    raw = np.frombuffer(blob, dtype=np.uint8)
+    words = raw[:NB * G * 1024].view("<u4").reshape(NB, G, 64, 4)
+    q = np.zeros((NB, G, 64, 4, 8), dtype=np.uint8)
+    for e in range(8):
+        q[..., e] = (words >> np.uint32(4 * _sigma(e))) & 0xF
+    codes = q.reshape(NB, G, 4, 16, 4, 8).transpose(1, 2, 4, 5, 0, 3).reshape(K, N)
+    s0 = _align256(NB * G * 1024)
+    sc = raw[s0:s0 + NB * G8 * 256].view(np.float16).reshape(NB, G8, 16, 8)
+    scales = sc.transpose(1, 3, 0, 2).reshape(G8 * 8, N)[:G]
+    return codes, scales

@@ -1,0 +1,162 @@
+"""Seeded generators for the quantized-GEMM workloads.
+
+Every tensor is drawn from its own ``numpy`` generator, seeded from a
+``SeedSequence`` of (seed, workload kind, shape, tensor id). Weight tensors do
+not depend on M, so one weight set serves a whole sweep over batch sizes.
+
+Canonical formats (the bytes both the oracle and the GPU library read):
+
+* 4-bit codes: ``uint32[K/8][N]``; nibble ``j`` (bits 4j..4j+3) of word
+  ``[r][n]`` is the code of weight ``(k = 8r + j, n)``. W4A16 codes are
+  unsigned 0..15; W4A8 codes are two's-complement int4 in -8..7.
+* mixed 2/4-bit codes: ``uint8[K][N]``, one code per byte (0..15 or 0..3).
+* group scales: one value per (group of 128 consecutive k, column n):
+  ``float16[K/128][N]`` (W4A16, mixed) or ``int8[K/128][N]`` (W4A8).
+* precision bitmap: ``uint32[K/128][ceil(N/32)]``; bit ``n % 32`` of word
+  ``[g][n // 32]`` is 1 when group (g, n) holds 4-bit codes.
+
+Value distributions follow the workloads of the MARLIN paper (4-bit weights,
+fp16 activations, batched decode), OdysseyLLM's W4A8 setting, and the
+"Enabling Fast 2-bit LLM on GPUs" page (a small fraction of large-range groups
+kept at 4 bits); the numeric ranges are this library's stated workload recipe.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128
+
+_KIND_W4A16 = 1
+_KIND_W4A8 = 2
+_KIND_W2W4 = 3
+
+
+def rng_for(seed: int, *tags: int) -> np.random.Generator:
+    """Independent generator for one tensor, keyed by ``(seed, *tags)``."""
+    return np.random.default_rng(np.random.SeedSequence([int(seed)] + [int(t) for t in tags]))
+
+
+def pack_nibbles_u32(codes: np.ndarray) -> np.ndarray:
+    """Pack ``uint8[K][N]`` codes (low 4 bits used) into ``uint32[K/8][N]``.
+
+    Nibble j of output word [r][n] receives codes[8r + j][n].
+    """
+    codes = np.asarray(codes)
+    K, N = codes.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    c = (codes.astype(np.uint32) & np.uint32(0xF)).reshape(K // 8, 8, N)
+    out = np.zeros((K // 8, N), dtype=np.uint32)
+    for j in range(8):
+        out |= c[:, j, :] << np.uint32(4 * j)
+    return out
+
+
+def _fp16_normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32).astype(np.float16)
+
+
+def _fp16_uniform(rng: np.random.Generator, lo: float, hi: float, shape) -> np.ndarray:
+    return rng.uniform(lo, hi, size=shape).astype(np.float16)
+
+
+def w4a16_problem(M: int, K: int, N: int, seed: int = 0, weights: bool = True,
+                  activations: bool = True) -> dict:
+    """W4A16 workload: fp16 A ~ N(0,1); uint4 codes uniform 0..15 (zero point 8);
+    fp16 scales uniform in [0.005, 0.02], one per (group of 128 k, column)."""
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    out = {"M": M, "K": K, "N": N, "zero": 8}
+    if activations:
+        out["A"] = _fp16_normal(rng_for(seed, _KIND_W4A16, 0, M, K), (M, K))
+    if weights:
+        q = rng_for(seed, _KIND_W4A16, 1, K, N).integers(0, 16, size=(K, N), dtype=np.uint8)
+        out["codes"] = pack_nibbles_u32(q)
+        out["scales"] = _fp16_uniform(rng_for(seed, _KIND_W4A16, 2, K, N), 0.005, 0.02,
+                                      (K // GROUP, N))
+    return out
+
+
+def w4a8_problem(M: int, K: int, N: int, seed: int = 0) -> dict:
+    """W4A8 workload: int8 A uniform in [-127, 127] with a per-token fp16 scale
+    uniform in [0.01, 0.03]; signed int4 weights uniform in [-8, 7]; int8 group
+    scales uniform in [1, 16] per (group of 128 k, column); fp16 per-column scale
+    uniform in [5e-4, 1e-3]."""
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    A = rng_for(seed, _KIND_W4A8, 0, M, K).integers(-127, 128, size=(M, K), dtype=np.int16)
+    a_scale = _fp16_uniform(rng_for(seed, _KIND_W4A8, 1, M, K), 0.01, 0.03, (M,))
+    q = rng_for(seed, _KIND_W4A8, 2, K, N).integers(-8, 8, size=(K, N), dtype=np.int16)
+    s_g = rng_for(seed, _KIND_W4A8, 3, K, N).integers(1, 17, size=(K // GROUP, N), dtype=np.int16)
+    s_c = _fp16_uniform(rng_for(seed, _KIND_W4A8, 4, K, N), 5e-4, 1e-3, (N,))
+    return {
+        "M": M, "K": K, "N": N,
+        "A": A.astype(np.int8),
+        "a_scale": a_scale,
+        # two's-complement nibbles: the low 4 bits of the int16 value
+        "codes": pack_nibbles_u32((q & 0xF).astype(np.uint8)),
+        "group_scales": s_g.astype(np.int8),
+        "chan_scales": s_c,
+    }
+
+
+def select_4bit_groups(latent: np.ndarray, frac: float = 0.10) -> np.ndarray:
+    """Choose which (group, column) pairs keep 4-bit codes.
+
+    Following the 2-bit page's recipe of giving 4 bits only to a small fraction of
+    groups with the largest weight range: rank groups by (max - min) of their 128
+    latent values, keep the ``round(frac * G * N)`` largest, ties broken toward the
+    lower linear index ``g * N + n``. Returns ``bool[G][N]``.
+    """
+    K, N = latent.shape
+    G = K // GROUP
+    blk = latent.reshape(G, GROUP, N)
+    rng_ = (blk.max(axis=1) - blk.min(axis=1)).astype(np.float64).ravel()
+    n4 = int(round(frac * G * N))
+    # stable sort on -range keeps the lower linear index first among equal ranges
+    order = np.argsort(-rng_, kind="stable")
+    mask = np.zeros(G * N, dtype=bool)
+    mask[order[:n4]] = True
+    return mask.reshape(G, N)
+
+
+def bitmap_from_mask(mask: np.ndarray) -> np.ndarray:
+    """``bool[G][N]`` -> ``uint32[G][ceil(N/32)]`` with bit n%32 of word n//32."""
+    G, N = mask.shape
+    W = (N + 31) // 32
+    out = np.zeros((G, W), dtype=np.uint32)
+    for n in range(N):
+        out[:, n // 32] |= mask[:, n].astype(np.uint32) << np.uint32(n % 32)
+    return out
+
+
+def w2w4_problem(M: int, K: int, N: int, seed: int = 0, frac4: float = 0.10,
+                 mask: np.ndarray | None = None) -> dict:
+    """Mixed 2/4-bit workload: fp16 A ~ N(0,1); groups of 128 k per column; the
+    ``frac4`` fraction of groups with the largest latent range get 4-bit codes
+    uniform in 0..15 (zero point 8), the rest 2-bit codes uniform in 0..3 (zero
+    point 2); fp16 scales uniform in [0.005, 0.02]. ``mask`` overrides the
+    selection (``bool[K/128][N]``)."""
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    G = K // GROUP
+    A = _fp16_normal(rng_for(seed, _KIND_W2W4, 0, M, K), (M, K))
+    if mask is None:
+        latent = rng_for(seed, _KIND_W2W4, 1, K, N).standard_normal(size=(K, N), dtype=np.float32)
+        mask = select_4bit_groups(latent, frac4)
+    mask = np.asarray(mask, dtype=bool)
+    r = rng_for(seed, _KIND_W2W4, 2, K, N)
+    c4 = r.integers(0, 16, size=(K, N), dtype=np.uint8)
+    c2 = (c4 & np.uint8(3))  # independent low bits of a uniform 0..15 draw are uniform 0..3
+    wide = np.repeat(mask, GROUP, axis=0)
+    codes = np.where(wide, c4, c2).astype(np.uint8)
+    scales = _fp16_uniform(rng_for(seed, _KIND_W2W4, 3, K, N), 0.005, 0.02, (G, N))
+    return {
+        "M": M, "K": K, "N": N,
+        "A": A,
+        "codes": codes,
+        "scales": scales,
+        "mask": mask,
+        "bitmap": bitmap_from_mask(mask),
+    }
