@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 quantized-weight GEMM on one MI355X.
+
+Metric: W4A16 GEMM TFLOP/s and fraction of the HBM roofline versus batch size
+M = 1..128 on the K x N = 8192 x 28672 layer (70B-class MLP up-projection) and
+its transpose 28672 x 8192 (down-projection).
+
+One step = one pass of the hot path over the whole sweep: for both shapes and
+every M in {1, 2, 4, 8, 16, 32, 64, 128}, one C = A * dequant(W) launch through
+the C ABI (16 launches). Inputs are seeded synthetic tensors with the workload's
+distributions (fp16 A ~ N(0,1); uint4 codes uniform with zero point 8; fp16
+group scales uniform in [0.005, 0.02], g = 128), resident in HBM before timing.
+The weight blob rotates over several copies (more bytes than the 256 MB
+Infinity Cache) so every launch streams its weights from HBM.
+
+Prints one JSON line. ``value`` is the aggregate TFLOP/s of the timed steps;
+``per_m`` gives each launch's own time, TFLOP/s and roofline fractions
+(kernel-only durations from HIP events around bursts of back-to-back launches);
+``roofline`` describes the launch that takes the largest share of the step;
+``cpu_baseline`` times the NumPy oracle on a bounded sample of the same work.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 MFMA, published
+SHAPES = [(8192, 28672), (28672, 8192)]
+MS = [1, 2, 4, 8, 16, 32, 64, 128]
+METRIC = "W4A16 GEMM TFLOP/s and % HBM roofline vs M=1–128, K×N=8192×28672"
+
+
+def alg_bytes(M, K, N):
+    """Bytes the method must move: 4-bit codes, fp16 group scales, A and C."""
+    return K * N // 2 + (K // 128) * N * 2 + M * K * 2 + M * N * 2
+
+
+def alg_flops(M, K, N):
+    return 2 * M * K * N
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--burst", type=int, default=40, help="launches per per-kernel timing burst")
+    ap.add_argument("--rotate-mb", type=int, default=640, help="minimum bytes of distinct weight copies")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--shapes", default="all", choices=["all", "up", "down"])
+    return ap.parse_args()
+
+
+def cpu_baseline(target_s: float) -> dict:
+    """The NumPy oracle as it stands, on a bounded sample of the step's work:
+    the full M sweep on both shapes restricted to the first n_cols output
+    columns (n_cols grown until the sample takes about target_s seconds)."""
+    from oracle import ref
+    from synth import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    n_cols = 256
+    while True:
+        flops = 0
+        t0 = time.perf_counter()
+        for (K, N) in SHAPES:
+            p = gen.w4a16_problem(128, K, n_cols, seed=0)
+            for M in MS:
+                ref.gemm_w4a16(p["A"][:M], p["codes"], p["scales"])
+                flops += alg_flops(M, K, n_cols)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or n_cols >= 8192:
+            break
+        n_cols *= 2
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 dequantize+matmul of the M sweep {MS} on both shapes, first {n_cols} "
+                  f"output columns ({flops / 1e9:.2f} GFLOP, {dt:.2f} s; includes input generation)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not "
+                                   "supported (N-sharding would split the layer's columns across GPUs)"}))
+        sys.exit(2)
+
+    import torch
+
+    import bit_weight_quantized_qgemm_amd as qg
+    from synth import gen
+
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = qg.lib()
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    shapes = SHAPES if args.shapes == "all" else ([SHAPES[0]] if args.shapes == "up" else [SHAPES[1]])
+
+    # ---- inputs resident in HBM
+    cases = []   # (K, N, M, blobs, A, C, ws)
+    for (K, N) in shapes:
+        p = gen.w4a16_problem(128, K, N, seed=0)
+        codes = torch.from_numpy(p["codes"].view(np.int32)).to(dev)
+        scales = torch.from_numpy(p["scales"]).to(dev)
+        blob = qg.repack_w4a16(codes, scales)
+        del codes, scales
+        reps = max(1, math.ceil(args.rotate_mb * 2**20 / blob.numel()))
+        blobs = [blob] + [blob.clone() for _ in range(reps - 1)]
+        A_all = torch.from_numpy(p["A"]).to(dev)
+        for M in MS:
+            A = A_all[:M].contiguous()
+            C = torch.empty((M, N), dtype=torch.float16, device=dev)
+            wsb = qg.workspace_bytes(qg.FMT_W4A16, M, K, N)
+            ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)
+            cases.append(dict(K=K, N=N, M=M, blobs=blobs, A=A, C=C, ws=ws, wsb=wsb,
+                              plan=qg.plan(qg.FMT_W4A16, M, K, N)))
+    torch.cuda.synchronize()
+
+    def launch(cs, i):
+        b = cs["blobs"][i % len(cs["blobs"])]
+        st = L.qgemm_w4a16(ctypes.c_void_p(cs["A"].data_ptr()), cs["K"], ctypes.c_void_p(b.data_ptr()),
+                           ctypes.c_void_p(cs["C"].data_ptr()), cs["N"], cs["M"], cs["K"], cs["N"],
+                           ctypes.c_void_p(cs["ws"].data_ptr()), cs["ws"].numel(), sptr)
+        if st != 0:
+            raise RuntimeError(f"qgemm_w4a16 failed: {st} {L.qgemm_last_error().decode()}")
+
+    def step(i):
+        for cs in cases:
+            launch(cs, i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = e0.elapsed_time(e1) / args.steps
+    step_flops = sum(alg_flops(c["M"], c["K"], c["N"]) for c in cases)
+    value = step_flops / (step_ms * 1e-3) / 1e12
+
+    # ---- per-launch kernel durations (bursts of back-to-back launches)
+    per_m = []
+    for cs in cases:
+        for i in range(3):
+            launch(cs, i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(args.burst):
+            launch(cs, i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / args.burst
+        M, K, N = cs["M"], cs["K"], cs["N"]
+        byt, fl = alg_bytes(M, K, N), alg_flops(M, K, N)
+        gbs = byt / (us * 1e-6) / 1e9
+        tf = fl / (us * 1e-6) / 1e12
+        roof_us = max(byt / (HBM_PEAK_GBS * 1e9), fl / (FP16_PEAK_TFLOPS * 1e12)) * 1e6
+        per_m.append({"shape": f"{K}x{N}", "M": M, "us": round(us, 2), "tflops": round(tf, 2),
+                      "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(tf / FP16_PEAK_TFLOPS, 4),
+                      "roofline_frac": round(roof_us / us, 4),
+                      "plan": {k: cs["plan"][k] for k in ("mb", "nb", "splits", "gps", "mt", "waves")}})
+
+    dom = max(per_m, key=lambda r: r["us"])
+    dM = dom["M"]
+    dK, dN = (int(x) for x in dom["shape"].split("x"))
+    mfma_bound = alg_flops(dM, dK, dN) / (FP16_PEAK_TFLOPS * 1e12) > alg_bytes(dM, dK, dN) / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / FP16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = f"w4a16 M={dM} {dom['shape']}"
+    roof["us_per_launch"] = dom["us"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "W4A16 GEMM, K x N = 8192 x 28672 and 28672 x 8192, "
+                               "M in {1,2,4,8,16,32,64,128}, g=128 fp16 scales, zero point 8",
+                   "launches_per_step": len(cases),
+                   "weight_copies_rotated": len(cases[0]["blobs"]),
+                   "wall_s_timed": round(wall, 3)},
+        "roofline": roof,
+        "per_m": per_m,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,238 @@
+"""Thin Python binding of the gfx950 quantized-weight GEMM library (libqgemm.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/qgemm.h``. PyTorch provides device memory
+and the current HIP stream. Importing this package does not need a GPU; calling
+anything that launches work needs an MI355X (gfx950) and the built library,
+and raises if either is missing -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FMT_W4A16", "FMT_W4A8", "FMT_W2W4", "QgemmError", "lib", "lib_path", "packed_bytes",
+    "workspace_bytes", "plan", "set_plan_override", "repack", "repack_w4a16", "repack_w4a8",
+    "repack_w2w4", "w4a16", "w4a8", "w2w4_mixed", "Workspace", "EXPORTED_SYMBOLS",
+]
+
+FMT_W4A16 = 1
+FMT_W4A8 = 2
+FMT_W2W4 = 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+_lib = None
+
+EXPORTED_SYMBOLS = (
+    "qgemm_status_str", "qgemm_last_error", "qgemm_version", "qgemm_packed_bytes",
+    "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16", "qgemm_w4a8", "qgemm_w2w4_mixed",
+    "qgemm_plan", "qgemm_set_plan_override",
+)
+
+
+class QgemmError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {_status_name(status)} ({status}){': ' + detail if detail else ''}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqgemm.so (built in-tree by ``build.py``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: run `python -m bit_weight_quantized_qgemm_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, u64p, vp = ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p
+        L.qgemm_status_str.restype = ctypes.c_char_p
+        L.qgemm_status_str.argtypes = [ctypes.c_int]
+        L.qgemm_last_error.restype = ctypes.c_char_p
+        L.qgemm_last_error.argtypes = []
+        L.qgemm_version.restype = ctypes.c_int
+        L.qgemm_packed_bytes.argtypes = [ctypes.c_int, i64, i64, vp, u64p]
+        L.qgemm_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, u64p]
+        L.qgemm_repack.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.qgemm_w4a16.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
+        L.qgemm_w4a8.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+        L.qgemm_w2w4_mixed.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
+        L.qgemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+        L.qgemm_set_plan_override.argtypes = [ctypes.c_int, ctypes.c_int]
+        for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
+                     "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_name(status: int) -> str:
+    try:
+        return lib().qgemm_status_str(status).decode()
+    except ImportError:
+        return "QGEMM_STATUS"
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        detail = lib().qgemm_last_error().decode()
+        raise QgemmError(status, where, detail)
+
+
+# ----------------------------------------------------------------------------- host-only queries
+def _bitmap_ptr(bitmap):
+    if bitmap is None:
+        return None, None
+    import numpy as np
+    arr = np.ascontiguousarray(np.asarray(bitmap, dtype=np.uint32))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def packed_bytes(fmt: int, K: int, N: int, bitmap=None) -> int:
+    keep, ptr = _bitmap_ptr(bitmap)
+    out = ctypes.c_size_t(0)
+    _check(lib().qgemm_packed_bytes(fmt, K, N, ptr, ctypes.byref(out)), "qgemm_packed_bytes")
+    del keep
+    return out.value
+
+
+def workspace_bytes(fmt: int, M: int, K: int, N: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qgemm_workspace_bytes(fmt, M, K, N, ctypes.byref(out)), "qgemm_workspace_bytes")
+    return out.value
+
+
+def plan(fmt: int, M: int, K: int, N: int) -> dict:
+    arr = (ctypes.c_int64 * 8)()
+    _check(lib().qgemm_plan(fmt, M, K, N, arr), "qgemm_plan")
+    keys = ("kernel", "mb", "nb", "splits", "gps", "mt", "nt", "waves")
+    return dict(zip(keys, list(arr)))
+
+
+def set_plan_override(nb_per_wave: int = 0, groups_per_split: int = 0):
+    _check(lib().qgemm_set_plan_override(nb_per_wave, groups_per_split), "qgemm_set_plan_override")
+
+
+# ----------------------------------------------------------------------------- device helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device=None):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _require_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensor must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+class Workspace:
+    """Zero-initialised split-K workspace, grown on demand, one per device.
+
+    The kernels leave the counter region zero after each completed call, so the
+    buffer is cleared only when it is (re)allocated.
+    """
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+        buf = self._bufs.get(key)
+        if nbytes == 0:
+            return None, 0
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            self._bufs[key] = buf
+        return buf, buf.numel()
+
+
+_default_ws = Workspace()
+
+
+# ----------------------------------------------------------------------------- repack
+def repack(fmt: int, K: int, N: int, codes, group_scales, chan_scales=None, bitmap=None):
+    """Repack canonical weights (device tensors) into a new uint8 blob tensor."""
+    torch = _torch()
+    _require_cuda(codes, group_scales, chan_scales)
+    nbytes = packed_bytes(fmt, K, N, bitmap)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    keep, bptr = _bitmap_ptr(bitmap)
+    _check(lib().qgemm_repack(fmt, K, N, _ptr(codes), _ptr(group_scales), _ptr(chan_scales), bptr,
+                              _ptr(out), nbytes, _stream_ptr(codes.device)), "qgemm_repack")
+    del keep
+    return out
+
+
+def repack_w4a16(codes, scales):
+    """codes: int32 [K/8][N] (canonical nibbles), scales: fp16 [K/128][N]."""
+    K, N = codes.shape[0] * 8, codes.shape[1]
+    return repack(FMT_W4A16, K, N, codes, scales)
+
+
+def repack_w4a8(codes, group_scales, chan_scales):
+    K, N = codes.shape[0] * 8, codes.shape[1]
+    return repack(FMT_W4A8, K, N, codes, group_scales, chan_scales)
+
+
+def repack_w2w4(codes_u8, scales, bitmap):
+    K, N = codes_u8.shape
+    return repack(FMT_W2W4, K, N, codes_u8, scales, bitmap=bitmap)
+
+
+# ----------------------------------------------------------------------------- GEMMs
+def _gemm_out(M, N, device, out):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=device)
+    return out
+
+
+def w4a16(A, blob, K: int, N: int, out=None, workspace: Workspace | None = None):
+    """C = A @ dequant(W) with a W4A16 blob; A fp16 [M][K] on the GPU."""
+    _require_cuda(A, blob)
+    M = A.shape[0]
+    out = _gemm_out(M, N, A.device, out)
+    ws, wsb = (workspace or _default_ws).get(workspace_bytes(FMT_W4A16, M, K, N), A.device)
+    _check(lib().qgemm_w4a16(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K, N,
+                             _ptr(ws), wsb, _stream_ptr(A.device)), "qgemm_w4a16")
+    return out
+
+
+def w4a8(A_i8, a_scale, blob, K: int, N: int, out=None, acc_out=None,
+         workspace: Workspace | None = None):
+    """W4A8 GEMM; returns C (fp16) and fills acc_out (int32 [M][N]) when given."""
+    _require_cuda(A_i8, a_scale, blob, acc_out)
+    M = A_i8.shape[0]
+    out = _gemm_out(M, N, A_i8.device, out)
+    ws, wsb = (workspace or _default_ws).get(workspace_bytes(FMT_W4A8, M, K, N), A_i8.device)
+    _check(lib().qgemm_w4a8(_ptr(A_i8), A_i8.stride(0), _ptr(a_scale), _ptr(blob), _ptr(out),
+                            out.stride(0), _ptr(acc_out), M, K, N, _ptr(ws), wsb,
+                            _stream_ptr(A_i8.device)), "qgemm_w4a8")
+    return out
+
+
+def w2w4_mixed(A, blob, K: int, N: int, out=None, workspace: Workspace | None = None):
+    _require_cuda(A, blob)
+    M = A.shape[0]
+    out = _gemm_out(M, N, A.device, out)
+    ws, wsb = (workspace or _default_ws).get(workspace_bytes(FMT_W2W4, M, K, N), A.device)
+    _check(lib().qgemm_w2w4_mixed(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K,
+                                  N, _ptr(ws), wsb, _stream_ptr(A.device)), "qgemm_w2w4_mixed")
+    return out

@@ -1,0 +1,406 @@
+// C-ABI front end: argument validation (before any HIP call), blob layout, work
+// planning and kernel dispatch. See include/qgemm.h for the contract.
+#include "qgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "qgemm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_force_nb{0};
+std::atomic<int> g_force_gps{0};
+
+constexpr int64_t kMaxM = 65535;
+constexpr int64_t kMaxKN = int64_t(1) << 20;
+constexpr int64_t kMaxKW4A8 = 16384;
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return QGEMM_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool valid_fmt(int fmt) { return fmt == QGEMM_FMT_W4A16 || fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W2W4; }
+
+int check_kn(int fmt, int64_t K, int64_t N) {
+  if (K <= 0 || K % qg::kGroup != 0 || K > kMaxKN) return QGEMM_ERR_SHAPE;
+  if (N <= 0 || N % 64 != 0 || N > kMaxKN) return QGEMM_ERR_SHAPE;
+  if (fmt == QGEMM_FMT_W4A8 && K > kMaxKW4A8) return QGEMM_ERR_SHAPE;
+  return QGEMM_OK;
+}
+
+// The current device must be a gfx950 GPU; cached per device ordinal.
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) {
+      if (it->second != QGEMM_OK) g_last_error = "current device is not gfx950";
+      return it->second;
+    }
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  const int st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? QGEMM_OK : QGEMM_ERR_DEVICE;
+  if (st != QGEMM_OK) g_last_error = std::string("device arch ") + prop.gcnArchName + " is not gfx950";
+  std::lock_guard<std::mutex> lk(mu);
+  cache[dev] = st;
+  return st;
+}
+
+int64_t count_bits(const uint32_t* bitmap, int64_t G, int64_t N, bool* stray) {
+  const int64_t W = (N + 31) / 32;
+  int64_t n = 0;
+  *stray = false;
+  for (int64_t g = 0; g < G; ++g)
+    for (int64_t w = 0; w < W; ++w) {
+      uint32_t v = bitmap[g * W + w];
+      const int64_t valid = std::min<int64_t>(32, N - 32 * w);
+      if (valid < 32 && (v >> valid) != 0) *stray = true;
+      n += __builtin_popcount(v);
+    }
+  return n;
+}
+
+}  // namespace
+
+namespace qg {
+
+BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4) {
+  BlobLayout L;
+  L.K = K;
+  L.N = N;
+  L.G = K / kGroup;
+  L.NB = N / 16;
+  L.G8 = (L.G + 7) / 8;
+  const size_t chunks = (size_t)(L.NB * L.G);
+  if (fmt == QGEMM_FMT_W4A16) {
+    L.codes = 0;
+    L.scales = align256(chunks * 1024);
+    L.total = L.scales + align256((size_t)L.NB * L.G8 * 256);
+  } else if (fmt == QGEMM_FMT_W4A8) {
+    L.codes = 0;
+    L.scales = align256(chunks * 1024);
+    L.aux = L.scales + align256((size_t)L.NB * L.G8 * 128);
+    L.total = L.aux + align256((size_t)N * 2);
+  } else {
+    L.codes = 0;
+    L.aux = align256(chunks * 512);
+    L.scales = L.aux + align256(chunks * 8);
+    L.high = L.scales + align256((size_t)L.NB * L.G8 * 256);
+    L.total = L.high + align256((size_t)n4 * 32);
+  }
+  return L;
+}
+
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
+  Plan pl;
+  const int G = (int)(K / kGroup);
+  pl.kernel = 1;
+  pl.mb = M <= 16 ? 1 : 2;
+  pl.mt = (int)((M + 16 * pl.mb - 1) / (16 * pl.mb));
+  if (pl.mt < 1) pl.mt = 1;
+  const int force_nb = g_force_nb.load();
+  const int force_gps = g_force_gps.load();
+  const int cands[3] = {4, 2, 1};
+  for (int ci = 0; ci < 3; ++ci) {
+    const int nb = force_nb ? force_nb : cands[ci];
+    const int64_t nt = N / (16 * nb);
+    const int64_t base = nt * pl.mt;
+    int gps;
+    if (force_gps) {
+      gps = force_gps;
+    } else {
+      const int64_t want = std::max<int64_t>(1, kTargetWaves / base);
+      gps = (int)((G + want - 1) / want);
+      gps = std::max(8, (gps + 7) / 8 * 8);
+    }
+    if (gps >= G) gps = G;
+    const int splits = (G + gps - 1) / gps;
+    pl.nb = nb;
+    pl.nt = (int)nt;
+    pl.gps = gps;
+    pl.splits = splits;
+    pl.waves = base * splits;
+    if (force_nb || pl.waves >= kTargetWaves / 2) break;
+  }
+  if (pl.splits > 1) {
+    pl.counter_bytes = align256((size_t)pl.mt * pl.nt * 4);
+    pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * M * N * 4);
+  }
+  (void)fmt;
+  return pl;
+}
+
+}  // namespace qg
+
+extern "C" {
+
+const char* qgemm_status_str(int status) {
+  switch (status) {
+    case QGEMM_OK: return "QGEMM_OK";
+    case QGEMM_ERR_NULL: return "QGEMM_ERR_NULL";
+    case QGEMM_ERR_SHAPE: return "QGEMM_ERR_SHAPE";
+    case QGEMM_ERR_ALIGN: return "QGEMM_ERR_ALIGN";
+    case QGEMM_ERR_WORKSPACE: return "QGEMM_ERR_WORKSPACE";
+    case QGEMM_ERR_FORMAT: return "QGEMM_ERR_FORMAT";
+    case QGEMM_ERR_RANGE: return "QGEMM_ERR_RANGE";
+    case QGEMM_ERR_ALIAS: return "QGEMM_ERR_ALIAS";
+    case QGEMM_ERR_HIP: return "QGEMM_ERR_HIP";
+    case QGEMM_ERR_DEVICE: return "QGEMM_ERR_DEVICE";
+    case QGEMM_ERR_SIZE: return "QGEMM_ERR_SIZE";
+    default: return "QGEMM_ERR_UNKNOWN";
+  }
+}
+
+const char* qgemm_last_error(void) { return g_last_error.c_str(); }
+
+int qgemm_version(void) { return 100; }
+
+int qgemm_packed_bytes(int fmt, int64_t K, int64_t N, const uint32_t* bitmap_host, size_t* bytes) {
+  if (!valid_fmt(fmt)) return QGEMM_ERR_FORMAT;
+  if (!bytes) return QGEMM_ERR_NULL;
+  int st = check_kn(fmt, K, N);
+  if (st) return st;
+  int64_t n4 = 0;
+  if (fmt == QGEMM_FMT_W2W4) {
+    if (!bitmap_host) return QGEMM_ERR_NULL;
+    bool stray = false;
+    n4 = count_bits(bitmap_host, K / qg::kGroup, N, &stray);
+    if (stray) return QGEMM_ERR_RANGE;
+  }
+  *bytes = qg::blob_layout(fmt, K, N, n4).total;
+  return QGEMM_OK;
+}
+
+int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* bytes) {
+  if (!valid_fmt(fmt)) return QGEMM_ERR_FORMAT;
+  if (!bytes) return QGEMM_ERR_NULL;
+  int st = check_kn(fmt, K, N);
+  if (st) return st;
+  if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
+  *bytes = M == 0 ? 0 : qg::make_plan(fmt, M, K, N).ws_bytes;
+  return QGEMM_OK;
+}
+
+int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out8) {
+  if (!valid_fmt(fmt)) return QGEMM_ERR_FORMAT;
+  if (!out8) return QGEMM_ERR_NULL;
+  int st = check_kn(fmt, K, N);
+  if (st) return st;
+  if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
+  const qg::Plan pl = qg::make_plan(fmt, M, K, N);
+  const int64_t v[8] = {pl.kernel, pl.mb, pl.nb, pl.splits, pl.gps, pl.mt, pl.nt, pl.waves};
+  std::memcpy(out8, v, sizeof(v));
+  return QGEMM_OK;
+}
+
+int qgemm_set_plan_override(int nb_per_wave, int groups_per_split) {
+  if (!(nb_per_wave == 0 || nb_per_wave == 1 || nb_per_wave == 2 || nb_per_wave == 4))
+    return QGEMM_ERR_RANGE;
+  if (groups_per_split < 0 || groups_per_split % 8 != 0) return QGEMM_ERR_RANGE;
+  g_force_nb.store(nb_per_wave);
+  g_force_gps.store(groups_per_split);
+  return QGEMM_OK;
+}
+
+int qgemm_repack(int fmt, int64_t K, int64_t N, const void* codes, const void* group_scales,
+                 const void* chan_scales, const uint32_t* bitmap_host, void* packed,
+                 size_t packed_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return QGEMM_ERR_FORMAT;
+  if (!codes || !group_scales || !packed) return QGEMM_ERR_NULL;
+  if (fmt == QGEMM_FMT_W4A8 && !chan_scales) return QGEMM_ERR_NULL;
+  if (fmt == QGEMM_FMT_W2W4 && !bitmap_host) return QGEMM_ERR_NULL;
+  int st = check_kn(fmt, K, N);
+  if (st) return st;
+  const int64_t G = K / qg::kGroup;
+  int64_t n4 = 0;
+  if (fmt == QGEMM_FMT_W2W4) {
+    bool stray = false;
+    n4 = count_bits(bitmap_host, G, N, &stray);
+    if (stray) return QGEMM_ERR_RANGE;
+  }
+  const qg::BlobLayout L = qg::blob_layout(fmt, K, N, n4);
+  if (packed_bytes != L.total) return QGEMM_ERR_SIZE;
+  if (!aligned(packed, 16) || !aligned(codes, fmt == QGEMM_FMT_W2W4 ? 1 : 4) ||
+      !aligned(group_scales, fmt == QGEMM_FMT_W4A8 ? 1 : 2) || (chan_scales && !aligned(chan_scales, 2)))
+    return QGEMM_ERR_ALIGN;
+  const size_t code_bytes = fmt == QGEMM_FMT_W2W4 ? (size_t)(K * N) : (size_t)(K / 2 * N);
+  const size_t gs_bytes = (size_t)(G * N) * (fmt == QGEMM_FMT_W4A8 ? 1 : 2);
+  if (overlap(packed, L.total, codes, code_bytes) || overlap(packed, L.total, group_scales, gs_bytes) ||
+      (fmt == QGEMM_FMT_W4A8 && overlap(packed, L.total, chan_scales, (size_t)N * 2)))
+    return QGEMM_ERR_ALIAS;
+  st = check_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // padding and alignment gaps are defined as zero bytes
+  hipError_t e = qg::launch_zero_fill(packed, L.total, s);
+  if (e != hipSuccess) return hip_fail(e, "zero fill");
+  if (fmt == QGEMM_FMT_W4A16) {
+    e = qg::launch_repack_w4a16(L, codes, group_scales, packed, s);
+  } else if (fmt == QGEMM_FMT_W4A8) {
+    e = qg::launch_repack_w4a8(L, codes, group_scales, chan_scales, packed, s);
+  } else {
+    // per-chunk descriptors: (high-plane slot offset, 16-bit column mask)
+    std::vector<uint32_t> desc((size_t)L.NB * L.G * 2);
+    const int64_t W = (N + 31) / 32;
+    uint32_t off = 0;
+    for (int64_t b = 0; b < L.NB; ++b)
+      for (int64_t g = 0; g < G; ++g) {
+        const uint32_t word = bitmap_host[g * W + (16 * b) / 32];
+        const uint32_t m16 = (word >> ((16 * b) % 32)) & 0xFFFFu;
+        desc[(size_t)(b * G + g) * 2] = off;
+        desc[(size_t)(b * G + g) * 2 + 1] = m16;
+        off += (uint32_t)__builtin_popcount(m16);
+      }
+    e = hipMemcpyAsync(static_cast<char*>(packed) + L.aux, desc.data(), desc.size() * 4,
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = qg::launch_repack_w2w4(L, codes, group_scales, packed, s);
+    if (e != hipSuccess) return hip_fail(e, "repack launch");
+    e = hipStreamSynchronize(s);   // keeps the host descriptor table alive until consumed
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  }
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  return QGEMM_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct GemmCall {
+  int fmt;
+  const void* A;
+  int64_t lda;
+  const void* a_scale;
+  const void* packed;
+  void* C;
+  int64_t ldc;
+  int32_t* acc_out;
+  int64_t M, K, N;
+  void* ws;
+  size_t ws_bytes;
+  void* stream;
+};
+
+int run_gemm(const GemmCall& g) {
+  if (!valid_fmt(g.fmt)) return QGEMM_ERR_FORMAT;
+  int st = check_kn(g.fmt, g.K, g.N);
+  if (st) return st;
+  if (g.M < 0 || g.M > kMaxM) return QGEMM_ERR_SHAPE;
+  if (g.M == 0) return QGEMM_OK;
+  if (!g.A || !g.packed || !g.C) return QGEMM_ERR_NULL;
+  if (g.fmt == QGEMM_FMT_W4A8 && !g.a_scale) return QGEMM_ERR_NULL;
+  const int64_t aelt = g.fmt == QGEMM_FMT_W4A8 ? 1 : 2;
+  if (!aligned(g.A, 16) || !aligned(g.packed, 16) || !aligned(g.C, 16)) return QGEMM_ERR_ALIGN;
+  if (g.lda < g.K || (g.lda * aelt) % 16 != 0) return QGEMM_ERR_ALIGN;
+  if (g.ldc < g.N || g.ldc % 8 != 0) return QGEMM_ERR_ALIGN;
+  if (g.a_scale && !aligned(g.a_scale, 2)) return QGEMM_ERR_ALIGN;
+  if (g.acc_out && !aligned(g.acc_out, 4)) return QGEMM_ERR_ALIGN;
+  const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N);
+  if (pl.ws_bytes > 0) {
+    if (!g.ws) return QGEMM_ERR_NULL;
+    if (g.ws_bytes < pl.ws_bytes) return QGEMM_ERR_WORKSPACE;
+    if (!aligned(g.ws, 16)) return QGEMM_ERR_ALIGN;
+  }
+  // the fixed-size part of the blob (everything before a mixed blob's high plane)
+  const qg::BlobLayout L = qg::blob_layout(g.fmt, g.K, g.N, 0);
+  const size_t blob_fixed = g.fmt == QGEMM_FMT_W2W4 ? L.high : L.total;
+  const size_t c_bytes = (size_t)((g.M - 1) * g.ldc + g.N) * 2;
+  const size_t a_bytes = (size_t)((g.M - 1) * g.lda + g.K) * aelt;
+  const size_t acc_bytes = g.acc_out ? (size_t)(g.M * g.N) * 4 : 0;
+  if (overlap(g.C, c_bytes, g.A, a_bytes) || overlap(g.C, c_bytes, g.packed, blob_fixed) ||
+      (pl.ws_bytes && overlap(g.C, c_bytes, g.ws, pl.ws_bytes)) ||
+      (g.a_scale && overlap(g.C, c_bytes, g.a_scale, (size_t)g.M * 2)) ||
+      (g.acc_out && (overlap(g.acc_out, acc_bytes, g.C, c_bytes) ||
+                     overlap(g.acc_out, acc_bytes, g.A, a_bytes) ||
+                     overlap(g.acc_out, acc_bytes, g.packed, blob_fixed) ||
+                     (pl.ws_bytes && overlap(g.acc_out, acc_bytes, g.ws, pl.ws_bytes)))))
+    return QGEMM_ERR_ALIAS;
+  st = check_device();
+  if (st) return st;
+
+  qg::GemmArgs a{};
+  const char* blob = static_cast<const char*>(g.packed);
+  a.A = g.A;
+  a.codes = blob + L.codes;
+  a.scales = blob + L.scales;
+  a.aux = blob + L.aux;
+  a.high = blob + L.high;
+  a.a_scale = g.a_scale;
+  a.C = g.C;
+  a.acc_out = g.acc_out;
+  a.lda = g.lda;
+  a.ldc = g.ldc;
+  a.M = (int)g.M;
+  a.K = (int)g.K;
+  a.N = (int)g.N;
+  a.G = (int)L.G;
+  a.G8 = (int)L.G8;
+  a.splits = pl.splits;
+  a.gps = pl.gps;
+  a.mt = pl.mt;
+  a.nt = pl.nt;
+  if (pl.ws_bytes) {
+    a.counters = static_cast<uint32_t*>(g.ws);
+    a.partial = static_cast<char*>(g.ws) + pl.counter_bytes;
+  }
+  hipStream_t s = static_cast<hipStream_t>(g.stream);
+  hipError_t e;
+  if (g.fmt == QGEMM_FMT_W4A16) e = qg::launch_w4a16(pl, a, s);
+  else if (g.fmt == QGEMM_FMT_W4A8) e = qg::launch_w4a8(pl, a, s);
+  else e = qg::launch_w2w4(pl, a, s);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return QGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemm_w4a16(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M,
+                int64_t K, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_gemm({QGEMM_FMT_W4A16, A, lda, nullptr, packed, C, ldc, nullptr, M, K, N, workspace,
+                   workspace_bytes, stream});
+}
+
+int qgemm_w4a8(const void* A, int64_t lda, const void* a_scale, const void* packed, void* C,
+               int64_t ldc, int32_t* acc_out, int64_t M, int64_t K, int64_t N, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return run_gemm({QGEMM_FMT_W4A8, A, lda, a_scale, packed, C, ldc, acc_out, M, K, N, workspace,
+                   workspace_bytes, stream});
+}
+
+int qgemm_w2w4_mixed(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc,
+                     int64_t M, int64_t K, int64_t N, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return run_gemm({QGEMM_FMT_W2W4, A, lda, nullptr, packed, C, ldc, nullptr, M, K, N, workspace,
+                   workspace_bytes, stream});
+}
+
+}  // extern "C"

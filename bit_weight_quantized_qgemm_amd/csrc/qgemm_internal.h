@@ -1,0 +1,77 @@
+// Host-side internals shared by the C-ABI front end and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kGroup = 128;          // k per quantization group
+constexpr int kWave = 64;            // lanes per wavefront (CDNA)
+constexpr int kWavesPerBlock = 4;    // one wave per SIMD of a CU
+constexpr int kCUs = 256;            // MI355X compute units (8 XCDs x 32)
+constexpr int kTargetWaves = kCUs * 8;
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Blob region offsets (bytes) for one weight shape; see the layout notes in
+// repack.hip. All regions start on 256-byte boundaries.
+struct BlobLayout {
+  int64_t K = 0, N = 0, G = 0, NB = 0, G8 = 0;
+  size_t codes = 0;    // W4A16/W4A8 1 KB chunks; W2W4 512 B base chunks
+  size_t scales = 0;   // fp16 (W4A16, W2W4) or int8 (W4A8) group scales
+  size_t aux = 0;      // W4A8: fp16 channel scales; W2W4: per-chunk descriptors
+  size_t high = 0;     // W2W4: 4-bit high plane
+  size_t total = 0;
+};
+
+BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4);
+
+// Work decomposition of one GEMM call.
+struct Plan {
+  int kernel = 0;        // 1 = skinny streaming kernel
+  int mb = 1;            // 16-row blocks per wave
+  int nb = 4;            // 16-column blocks per wave
+  int splits = 1;        // k-splits
+  int gps = 0;           // groups per split (multiple of 8, except when splits == 1)
+  int mt = 1;            // m-tiles
+  int nt = 1;            // n-tiles
+  int64_t waves = 0;     // waves launched
+  size_t counter_bytes = 0;
+  size_t ws_bytes = 0;   // total workspace (0 when splits == 1)
+};
+
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N);
+
+// Arguments of every GEMM kernel (passed by value).
+struct GemmArgs {
+  const void* A;
+  const void* codes;      // chunk region
+  const void* scales;     // group-scale region
+  const void* aux;        // W4A8: fp16 channel scales; W2W4: descriptors
+  const void* high;       // W2W4: high plane
+  const void* a_scale;    // W4A8: fp16 per-row scales
+  void* C;
+  int32_t* acc_out;       // W4A8, nullable
+  void* partial;          // split-K partials [splits][M][N] (fp32 or int32)
+  uint32_t* counters;     // per (m-tile, n-tile) arrival counters
+  int64_t lda, ldc;
+  int M, K, N, G, G8;
+  int splits, gps, mt, nt;
+};
+
+hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);
+hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
+hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);
+
+hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_repack_w4a16(const BlobLayout& L, const void* codes, const void* scales,
+                               void* packed, hipStream_t s);
+hipError_t launch_repack_w4a8(const BlobLayout& L, const void* codes, const void* gscales,
+                              const void* cscales, void* packed, hipStream_t s);
+// desc (already uploaded into the blob's descriptor region) gives the high-plane slots.
+hipError_t launch_repack_w2w4(const BlobLayout& L, const void* codes, const void* scales,
+                              void* packed, hipStream_t s);
+
+}  // namespace qg

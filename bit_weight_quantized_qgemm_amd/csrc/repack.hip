@@ -1,0 +1,203 @@
+// Offline weight repacking into the order the GEMM kernels stream (the "matrix
+// preprocessing that optimizes data layout" of the arbitrary-precision Tensor Core
+// page; the 2-bit page's "memory alignment consideration" for mixed 2/4-bit
+// groups).
+//
+// Blob layout (G = K/128 groups, NB = N/16 column blocks, G8 = ceil(G/8); lane l
+// of a 64-wide wave has column c = l % 16 and k-quarter h = l / 16; regions start
+// on 256-byte boundaries):
+//
+//  W4A16 codes : chunk (b, g) of 1024 B at (b*G + g)*1024; lane l owns 16 B at
+//                +16l = words t = 0..3; word t holds the 8 codes of
+//                k = 128g + 32h + 8t + e (e = 0..7) of column n = 16b + c, element
+//                e in nibble sigma(e) = e/2 (e even) or 4 + (e-1)/2 (e odd), so
+//                that one AND/OR per nibble pair yields two fp16 lanes in k order.
+//                That is exactly the v_mfma_f32_16x16x32_f16 B-operand of lane l
+//                for k-step t, with the group's k permuted identically in A.
+//  scales      : fp16 [NB][G8][16][8]: lane c loads the scales of 8 groups at once.
+//  W4A8 codes  : same chunks; element e of word t in nibble tau(e) = 2e (e < 4) or
+//                2(e-4) + 1 (e >= 4) so that (w & 0x0F0F0F0F) and
+//                ((w >> 4) & 0x0F0F0F0F) are the int8 B-operand bytes in k order;
+//                the nibble holds q + 8 (0..15).
+//  W4A8 scales : int8 group scales [NB][G8][16][8], then fp16 channel scales [N].
+//  W2W4 base   : chunk (b, g) of 512 B; lane l owns 8 B = words s = 0, 1; bits
+//                [4p, 4p+1] of word s = low 2 bits of the code at slot p of W4A16
+//                word 2s, bits [4p+2, 4p+3] = same for word 2s+1.
+//  W2W4 desc   : per chunk (b, g): u32 off, u32 mask16 (bit c = column 16b + c is
+//                a 4-bit group; off = 4-bit groups in all earlier chunks).
+//  W2W4 high   : per 4-bit group, 32 B at 32*(off + rank(c)), quarter h at +8h,
+//                the upper 2 code bits in the base-plane arrangement.
+#include "qgemm_device.h"
+#include "qgemm_internal.h"
+
+#include <algorithm>
+
+namespace qg {
+namespace {
+
+__device__ __forceinline__ int sigma(int e) { return (e & 1) ? 4 + (e >> 1) : (e >> 1); }
+__device__ __forceinline__ int sigma_inv(int p) { return p < 4 ? 2 * p : 2 * (p - 4) + 1; }
+__device__ __forceinline__ int tau(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
+
+// canonical word (nibble e = code of k = 8r + e) -> blob word under a slot map
+template <bool kTau>
+__device__ __forceinline__ uint32_t permute_nibbles(uint32_t src) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int slot = kTau ? tau(e) : sigma(e);
+    out |= ((src >> (4 * e)) & 0xFu) << (4 * slot);
+  }
+  return out;
+}
+
+// One thread per (chunk, lane): 4 words of W4A16 / W4A8 codes.
+template <bool kW4A8>
+__global__ void repack_codes_u4(const uint32_t* __restrict__ codes, uint32_t* __restrict__ out,
+                                int G, int N, int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int lane = (int)(tid & 63);
+  const int64_t chunk = tid >> 6;
+  const int b = (int)(chunk / G), g = (int)(chunk % G);
+  const int c = lane & 15, h = lane >> 4;
+  const int n = 16 * b + c;
+  u32x4 w;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    // canonical word row r = k/8 with k = 128g + 32h + 8t
+    uint32_t src = codes[(size_t)(16 * g + 4 * h + t) * N + n];
+    if (kW4A8) src ^= 0x88888888u;   // two's-complement q -> q + 8 in every nibble
+    w[t] = permute_nibbles<kW4A8>(src);
+  }
+  reinterpret_cast<u32x4*>(out)[tid] = w;
+}
+
+// One thread per (block, 8-group set, column): 8 group scales of one column.
+template <typename T>
+__global__ void repack_scales(const T* __restrict__ s, T* __restrict__ out, int G, int G8, int N,
+                              int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int c = (int)(tid % 16);
+  const int64_t bg = tid / 16;
+  const int b = (int)(bg / G8), g8 = (int)(bg % G8);
+  const int n = 16 * b + c;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int g = 8 * g8 + j;
+    out[tid * 8 + j] = g < G ? s[(size_t)g * N + n] : T(0);
+  }
+}
+
+__global__ void copy_halves(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+// One thread per (chunk, lane) of the mixed format: base words and, for 4-bit
+// groups, the high words at the slot the descriptor table assigns.
+__global__ void repack_w2w4_kernel(const uint8_t* __restrict__ codes, const u32x2* __restrict__ desc,
+                                   u32x2* __restrict__ base, u32x2* __restrict__ high, int G, int N,
+                                   int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int lane = (int)(tid & 63);
+  const int64_t chunk = tid >> 6;
+  const int g = (int)(chunk % G);
+  const int c = lane & 15, h = lane >> 4;
+  const int n = 16 * (int)(chunk / G) + c;
+  u32x2 lo = {0u, 0u}, hi = {0u, 0u};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int e = sigma_inv(p);
+      const int k0 = 128 * g + 32 * h + 16 * s + e;   // W4A16 word 2s
+      const uint32_t q0 = codes[(size_t)k0 * N + n];
+      const uint32_t q1 = codes[(size_t)(k0 + 8) * N + n];   // word 2s + 1
+      lo[s] |= ((q0 & 3u) << (4 * p)) | ((q1 & 3u) << (4 * p + 2));
+      hi[s] |= (((q0 >> 2) & 3u) << (4 * p)) | (((q1 >> 2) & 3u) << (4 * p + 2));
+    }
+  }
+  base[tid] = lo;
+  const u32x2 d = desc[chunk];
+  if ((d[1] >> c) & 1u) {
+    const uint32_t rank = __builtin_popcount(d[1] & ((1u << c) - 1u));
+    high[(size_t)(d[0] + rank) * 4 + h] = hi;
+  }
+}
+
+__global__ void zero_fill16(u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+inline unsigned grid_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
+
+}  // namespace
+
+hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);   // blob sizes are multiples of 256
+  const unsigned grid = (unsigned)std::min<int64_t>(4096, (n16 + 255) / 256);
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_fill16, dim3(grid), dim3(256), 0, s, static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_w4a16(const BlobLayout& L, const void* codes, const void* scales,
+                               void* packed, hipStream_t s) {
+  char* out = static_cast<char*>(packed);
+  const int64_t nc = L.NB * L.G * 64;
+  hipLaunchKernelGGL((repack_codes_u4<false>), dim3(grid_for(nc, 256)), dim3(256), 0, s,
+                     static_cast<const uint32_t*>(codes), reinterpret_cast<uint32_t*>(out + L.codes),
+                     (int)L.G, (int)L.N, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ns = L.NB * L.G8 * 16;
+  hipLaunchKernelGGL((repack_scales<uint16_t>), dim3(grid_for(ns, 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(scales), reinterpret_cast<uint16_t*>(out + L.scales),
+                     (int)L.G, (int)L.G8, (int)L.N, ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_w4a8(const BlobLayout& L, const void* codes, const void* gscales,
+                              const void* cscales, void* packed, hipStream_t s) {
+  char* out = static_cast<char*>(packed);
+  const int64_t nc = L.NB * L.G * 64;
+  hipLaunchKernelGGL((repack_codes_u4<true>), dim3(grid_for(nc, 256)), dim3(256), 0, s,
+                     static_cast<const uint32_t*>(codes), reinterpret_cast<uint32_t*>(out + L.codes),
+                     (int)L.G, (int)L.N, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ns = L.NB * L.G8 * 16;
+  hipLaunchKernelGGL((repack_scales<int8_t>), dim3(grid_for(ns, 256)), dim3(256), 0, s,
+                     static_cast<const int8_t*>(gscales), reinterpret_cast<int8_t*>(out + L.scales),
+                     (int)L.G, (int)L.G8, (int)L.N, ns);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(copy_halves, dim3(grid_for(L.N, 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(cscales), reinterpret_cast<uint16_t*>(out + L.aux),
+                     (int)L.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_w2w4(const BlobLayout& L, const void* codes, const void* scales,
+                              void* packed, hipStream_t s) {
+  char* out = static_cast<char*>(packed);
+  const int64_t nc = L.NB * L.G * 64;
+  hipLaunchKernelGGL(repack_w2w4_kernel, dim3(grid_for(nc, 256)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(codes), reinterpret_cast<const u32x2*>(out + L.aux),
+                     reinterpret_cast<u32x2*>(out + L.codes), reinterpret_cast<u32x2*>(out + L.high),
+                     (int)L.G, (int)L.N, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ns = L.NB * L.G8 * 16;
+  hipLaunchKernelGGL((repack_scales<uint16_t>), dim3(grid_for(ns, 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(scales), reinterpret_cast<uint16_t*>(out + L.scales),
+                     (int)L.G, (int)L.G8, (int)L.N, ns);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,178 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) quantized-weight GEMM library.
+ *
+ * The library computes C[M,N] = A[M,K] * dequant(Wq)[K,N] for small-to-medium
+ * batches (M = 1..128 is the design range; larger M is accepted), the
+ * "mixed-precision auto-regressive linear" layer of the MARLIN paper (abstract:
+ * weights compressed to about 4 bits per element, batched decode with 1..128
+ * parallel clients, memory-bound up to batch 16..32). Three weight formats:
+ *
+ *   W4A16  fp16 activations; unsigned 4-bit codes q (0..15) with an implicit
+ *          zero point 8 and one fp16 scale s per group of 128 consecutive k of
+ *          one output column: W[k,n] = (q[k,n] - 8) * s[k/128, n].
+ *   W4A8   int8 activations with one fp16 scale per row (token); signed int4
+ *          weights q (-8..7) with an int8 scale per group of 128 k and an fp16
+ *          scale per output column (the W4A8 setting of the OdysseyLLM /
+ *          FastGEMM abstract): acc[m,n] = sum_k A[m,k] * q[k,n] * s_g[k/128,n]
+ *          exactly in int32, C[m,n] = fp16(acc * a_scale[m] * s_c[n]).
+ *   W2W4   mixed 2/4-bit groups (the "Enabling Fast 2-bit LLM on GPUs" page,
+ *          abstract: only a small fraction of large-range groups keep 4 bits,
+ *          stored with memory alignment in mind): per group of 128 k of one
+ *          column either 4-bit codes (zero 8) or 2-bit codes (zero 2), one fp16
+ *          scale per group, a host bitmap marking the 4-bit groups.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
+ *     The caller allocates and owns every buffer and keeps it alive until the
+ *     work queued on `stream` has finished. The library never allocates or
+ *     frees memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ *     work; results are valid after the caller synchronizes the stream. A fault
+ *     inside a kernel surfaces at that synchronization, not as a return code.
+ *   - Matrices are row-major with a leading dimension in elements (lda, ldc).
+ *   - Return value: QGEMM_OK (0) or a negative qgemm_status. Arguments are fully
+ *     validated before any HIP call; a call that fails validation enqueues
+ *     nothing and writes nothing. No C++ exception crosses this boundary.
+ *   - Shapes: K > 0 a multiple of 128, N > 0 a multiple of 64, 0 <= M <= 65535
+ *     (M == 0 returns QGEMM_OK without launching anything).
+ *   - Pointers: 16-byte aligned; lda, ldc multiples of 8 (fp16) or 16 (int8).
+ *   - Concurrent calls that share one workspace race; give each stream its own.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qgemm_status {
+  QGEMM_OK = 0,
+  QGEMM_ERR_NULL = -1,      /* a required pointer is NULL */
+  QGEMM_ERR_SHAPE = -2,     /* K, N or M outside the accepted range */
+  QGEMM_ERR_ALIGN = -3,     /* pointer or leading dimension misaligned / too small */
+  QGEMM_ERR_WORKSPACE = -4, /* workspace smaller than qgemm_workspace_bytes() */
+  QGEMM_ERR_FORMAT = -5,    /* unknown format id */
+  QGEMM_ERR_RANGE = -6,     /* an argument value outside its documented range */
+  QGEMM_ERR_ALIAS = -7,     /* output overlaps an input */
+  QGEMM_ERR_HIP = -8,       /* a HIP runtime call failed (see qgemm_last_error) */
+  QGEMM_ERR_DEVICE = -9,    /* current device is not a gfx950 GPU */
+  QGEMM_ERR_SIZE = -10      /* blob size does not match qgemm_packed_bytes() */
+} qgemm_status;
+
+typedef enum qgemm_fmt {
+  QGEMM_FMT_W4A16 = 1,
+  QGEMM_FMT_W4A8 = 2,
+  QGEMM_FMT_W2W4 = 3
+} qgemm_fmt;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qgemm_status_str(int status);
+
+/* Text describing the last QGEMM_ERR_HIP / QGEMM_ERR_DEVICE of the calling
+ * thread ("" if none). Valid until the thread's next library call. */
+const char* qgemm_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int qgemm_version(void);
+
+/*
+ * Size in bytes of the repacked weight blob for (fmt, K, N).
+ * For QGEMM_FMT_W2W4 the size depends on how many groups are 4-bit, so
+ * bitmap_host (uint32[K/128][ceil(N/32)], HOST memory, bit n%32 of word
+ * [g][n/32] set = group (g, n) is 4-bit) is required; it is ignored (may be
+ * NULL) for the other formats. Bits for columns >= N must be 0 (QGEMM_ERR_RANGE).
+ */
+int qgemm_packed_bytes(int fmt, int64_t K, int64_t N, const uint32_t* bitmap_host,
+                       size_t* bytes);
+
+/*
+ * Workspace bytes one GEMM call of this shape needs (split-K partial sums and
+ * per-tile arrival counters; 0 when the plan does not split K). The workspace
+ * must be filled with zero bytes ONCE before its first use; every completed
+ * call leaves its counter region zero again, so it can be reused without
+ * clearing. A larger workspace is always accepted.
+ */
+int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* bytes);
+
+/*
+ * Offline weight preprocessing (the "matrix preprocessing that optimizes data
+ * layout for subsequent computations" of the arbitrary-precision Tensor Core
+ * page's abstract): rewrites canonical codes and scales into the blob the GEMM
+ * kernels stream, laid out in gfx950 MFMA operand order (one 1 KB, fully
+ * coalesced wave load per 16 columns x 128 k for the 4-bit formats).
+ *
+ *   W4A16: codes        uint32[K/8][N], nibble j of word [r][n] = code of
+ *                       k = 8r + j (0..15)
+ *          group_scales fp16[K/128][N]; chan_scales and bitmap_host unused.
+ *   W4A8:  codes        uint32[K/8][N], two's-complement int4 nibbles (-8..7)
+ *          group_scales int8[K/128][N] (any int8 value)
+ *          chan_scales  fp16[N]
+ *   W2W4:  codes        uint8[K][N], one code per byte; 0..15 for 4-bit groups,
+ *                       0..3 for 2-bit groups (higher bits of 2-bit-group codes
+ *                       are ignored)
+ *          group_scales fp16[K/128][N]
+ *          bitmap_host  HOST uint32[K/128][ceil(N/32)] (see qgemm_packed_bytes)
+ *
+ * packed must hold exactly qgemm_packed_bytes() bytes (QGEMM_ERR_SIZE
+ * otherwise) and must not overlap the inputs. W4A16 and W4A8 repacks are fully
+ * asynchronous. The W2W4 repack uploads a small per-tile offset table computed
+ * on the host from bitmap_host and synchronizes `stream` once before returning.
+ */
+int qgemm_repack(int fmt, int64_t K, int64_t N, const void* codes, const void* group_scales,
+                 const void* chan_scales, const uint32_t* bitmap_host, void* packed,
+                 size_t packed_bytes, void* stream);
+
+/*
+ * W4A16 GEMM: C[M,N] (fp16, row-major, leading dimension ldc >= N) =
+ * A[M,K] (fp16, lda >= K) * dequant(packed) with fp32 accumulation and one
+ * round-to-nearest-even conversion of each output to fp16. packed is a
+ * QGEMM_FMT_W4A16 blob of shape (K, N). workspace: see qgemm_workspace_bytes.
+ * Results are deterministic (bit-identical run to run).
+ */
+int qgemm_w4a16(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc,
+                int64_t M, int64_t K, int64_t N, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * W4A8 GEMM: A int8[M][lda], a_scale fp16[M], packed a QGEMM_FMT_W4A8 blob.
+ * acc[m,n] = sum_k A[m,k] * q[k,n] * s_g[k/128,n] is computed exactly in int32
+ * (K <= 16384 guarantees no overflow for any int8 inputs; larger K is
+ * QGEMM_ERR_SHAPE). C fp16[M][ldc] = fp16(float(acc) * a_scale[m] * s_c[n]).
+ * acc_out (nullable) receives the int32 accumulators, int32[M][N] dense.
+ */
+int qgemm_w4a8(const void* A, int64_t lda, const void* a_scale, const void* packed, void* C,
+               int64_t ldc, int32_t* acc_out, int64_t M, int64_t K, int64_t N,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Mixed 2/4-bit GEMM: like qgemm_w4a16 but packed is a QGEMM_FMT_W2W4 blob; each
+ * group dequantizes with zero point 8 (4-bit) or 2 (2-bit) as recorded in it.
+ */
+int qgemm_w2w4_mixed(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc,
+                     int64_t M, int64_t K, int64_t N, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * Work decomposition actually used for a call of this shape (for tests and
+ * tuning). Fills out[0..7] = {kernel id, row blocks of 16 per wave (MB),
+ * column blocks of 16 per wave (NB), k-splits, groups per split, m-tiles,
+ * n-tiles, waves launched}. Host-only; no HIP call.
+ */
+int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out8);
+
+/*
+ * Override the automatic plan for calls on the calling process: column blocks
+ * per wave (1, 2 or 4) and groups per k-split (a positive multiple of 8), or
+ * 0 to restore automatic choice. For tests of the split-K reduction and for
+ * tuning sweeps; affects qgemm_workspace_bytes and qgemm_plan too.
+ */
+int qgemm_set_plan_override(int nb_per_wave, int groups_per_split);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

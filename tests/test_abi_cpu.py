@@ -1,0 +1,172 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol declared in
+include/qgemm.h, validates arguments before any HIP call, and plans work that
+covers every (m-tile, n-tile, group) exactly once. No kernel is launched."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_weight_quantized_qgemm_amd as qg
+from oracle import layout
+from synth import gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WS, ERR_FMT, ERR_RANGE, ERR_ALIAS, ERR_HIP, ERR_DEV, ERR_SIZE = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+
+CONFIG_SHAPES = [(1024, 1024), (4096, 4096), (4096, 11008), (11008, 4096), (8192, 28672),
+                 (28672, 8192)]
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qg.lib_path()):
+        pytest.fail("libqgemm.so is not built: run python -m bit_weight_quantized_qgemm_amd.build")
+    return qg.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(qgemm_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 11
+    assert sorted(qg.EXPORTED_SYMBOLS) == names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.qgemm_version() >= 100
+    assert L.qgemm_status_str(-4).decode() == "QGEMM_ERR_WORKSPACE"
+    assert L.qgemm_status_str(12345).decode() == "QGEMM_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("K,N", CONFIG_SHAPES + [(128, 64), (1152, 320)])
+def test_packed_bytes_match_independent_layout(K, N):
+    assert qg.packed_bytes(qg.FMT_W4A16, K, N) == layout.packed_bytes(layout.FMT_W4A16, K, N)
+    if K <= 16384:
+        assert qg.packed_bytes(qg.FMT_W4A8, K, N) == layout.packed_bytes(layout.FMT_W4A8, K, N)
+    mask = np.zeros((K // 128, N), dtype=bool)
+    mask.ravel()[::7] = True
+    bm = gen.bitmap_from_mask(mask)
+    assert qg.packed_bytes(qg.FMT_W2W4, K, N, bm) == layout.packed_bytes(layout.FMT_W2W4, K, N,
+                                                                         int(mask.sum()))
+
+
+def _st(L, fn, *args):
+    return getattr(L, fn)(*args)
+
+
+def test_shape_and_format_validation(L):
+    out = ctypes.c_size_t(0)
+    assert L.qgemm_packed_bytes(7, 1024, 1024, None, ctypes.byref(out)) == ERR_FMT
+    assert L.qgemm_packed_bytes(1, 1000, 1024, None, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_packed_bytes(1, 1024, 96, None, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_packed_bytes(1, 0, 64, None, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_packed_bytes(1, 1024, 64, None, None) == ERR_NULL
+    assert L.qgemm_packed_bytes(2, 16384, 64, None, ctypes.byref(out)) == OK
+    assert L.qgemm_packed_bytes(2, 16512, 64, None, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_packed_bytes(3, 1024, 64, None, ctypes.byref(out)) == ERR_NULL
+    assert L.qgemm_workspace_bytes(1, -1, 1024, 64, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_workspace_bytes(1, 65536, 1024, 64, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_workspace_bytes(1, 0, 1024, 64, ctypes.byref(out)) == OK and out.value == 0
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_gemm_validation_order_without_gpu(L):
+    A, P, C, W = _fake(0x10000000), _fake(0x20000000), _fake(0x30000000), _fake(0x40000000)
+    M, K, N = 16, 4096, 4096
+    ws = qg.workspace_bytes(qg.FMT_W4A16, M, K, N)
+    # M == 0 is a no-op even with NULL pointers
+    assert L.qgemm_w4a16(None, K, None, None, N, 0, K, N, None, 0, None) == OK
+    assert L.qgemm_w4a16(None, K, P, C, N, M, K, N, W, ws, None) == ERR_NULL
+    assert L.qgemm_w4a16(A, K, P, C, N, M, 1000, N, W, ws, None) == ERR_SHAPE
+    assert L.qgemm_w4a16(_fake(0x10000008), K, P, C, N, M, K, N, W, ws, None) == ERR_ALIGN
+    assert L.qgemm_w4a16(A, K - 8, P, C, N, M, K, N, W, ws, None) == ERR_ALIGN   # lda < K
+    assert L.qgemm_w4a16(A, K + 4, P, C, N, M, K, N, W, ws, None) == ERR_ALIGN   # lda*2 % 16
+    assert L.qgemm_w4a16(A, K, P, C, N - 8, M, K, N, W, ws, None) == ERR_ALIGN   # ldc < N
+    if ws:
+        assert L.qgemm_w4a16(A, K, P, C, N, M, K, N, W, ws - 1, None) == ERR_WS
+        assert L.qgemm_w4a16(A, K, P, C, N, M, K, N, None, 0, None) == ERR_NULL
+    # C overlapping A
+    assert L.qgemm_w4a16(A, K, P, _fake(0x10000000 + 256), N, M, K, N, W, ws, None) == ERR_ALIAS
+    # W4A8 needs a_scale and K <= 16384
+    w8 = qg.workspace_bytes(qg.FMT_W4A8, M, K, N)
+    assert L.qgemm_w4a8(A, K, None, P, C, N, None, M, K, N, W, w8, None) == ERR_NULL
+    assert L.qgemm_w4a8(A, K, _fake(0x50000000), P, C, N, None, M, 16512, N, W, w8, None) == ERR_SHAPE
+    assert L.qgemm_w4a8(A, K + 8, _fake(0x50000000), P, C, N, None, M, K, N, W, w8, None) == ERR_ALIGN
+    assert L.qgemm_w4a8(A, K, _fake(0x50000000), P, C, N, _fake(0x30000000), M, K, N, W, w8,
+                        None) == ERR_ALIAS   # acc_out overlaps C
+    # valid arguments reach the device check: without a gfx950 GPU that is an error, not a crash
+    st = L.qgemm_w4a16(A, K, P, C, N, M, K, N, W, ws, None)
+    if st != OK:
+        assert st in (ERR_HIP, ERR_DEV)
+        assert len(L.qgemm_last_error()) > 0
+
+
+def test_repack_validation_without_gpu(L):
+    K, N = 1024, 1024
+    nb = qg.packed_bytes(qg.FMT_W4A16, K, N)
+    codes, sc, out = _fake(0x10000000), _fake(0x20000000), _fake(0x30000000)
+    assert L.qgemm_repack(9, K, N, codes, sc, None, None, out, nb, None) == ERR_FMT
+    assert L.qgemm_repack(1, K, N, None, sc, None, None, out, nb, None) == ERR_NULL
+    assert L.qgemm_repack(2, K, N, codes, sc, None, None, out, nb, None) == ERR_NULL
+    assert L.qgemm_repack(3, K, N, codes, sc, None, None, out, nb, None) == ERR_NULL
+    assert L.qgemm_repack(1, K, N, codes, sc, None, None, out, nb - 256, None) == ERR_SIZE
+    assert L.qgemm_repack(1, K, N, codes, sc, None, None, _fake(0x30000008), nb, None) == ERR_ALIGN
+    assert L.qgemm_repack(1, K, N, codes, sc, None, None, _fake(0x10000000 + 4096), nb, None) == ERR_ALIAS
+
+
+@pytest.mark.parametrize("K,N", CONFIG_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 17, 32, 64, 100, 128])
+def test_plan_covers_every_unit_once(K, N, M):
+    G = K // 128
+    p = qg.plan(qg.FMT_W4A16, M, K, N)
+    assert p["nb"] in (1, 2, 4) and p["mb"] in (1, 2)
+    assert p["nt"] * p["nb"] * 16 == N
+    assert p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
+    assert p["waves"] == p["nt"] * p["mt"] * p["splits"]
+    if p["splits"] > 1:
+        assert p["gps"] % 8 == 0
+    # group ranges of the splits tile [0, G) exactly
+    cover = np.zeros(G, dtype=int)
+    for s in range(p["splits"]):
+        g0 = s * p["gps"]
+        g1 = min(G, g0 + p["gps"])
+        assert g1 > g0
+        cover[g0:g1] += 1
+    assert np.all(cover == 1)
+    ws = qg.workspace_bytes(qg.FMT_W4A16, M, K, N)
+    if p["splits"] == 1:
+        assert ws == 0
+    else:
+        assert ws >= p["splits"] * M * N * 4 + p["mt"] * p["nt"] * 4
+
+
+def test_plan_override(L):
+    try:
+        assert L.qgemm_set_plan_override(3, 0) == ERR_RANGE
+        assert L.qgemm_set_plan_override(1, 12) == ERR_RANGE
+        qg.set_plan_override(2, 8)
+        p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
+        assert p["nb"] == 2 and p["gps"] == 8 and p["splits"] == 4
+        qg.set_plan_override(1, 64)     # more than G groups -> one split
+        p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
+        assert p["splits"] == 1 and p["gps"] == 32
+    finally:
+        qg.set_plan_override(0, 0)
+    assert qg.plan(qg.FMT_W4A16, 16, 4096, 4096)["nb"] in (1, 2, 4)
+
+
+def test_binding_needs_built_library_and_no_cpu_path():
+    import inspect
+    src = inspect.getsource(qg)
+    assert "oracle" not in src and "numpy.matmul" not in src and "torch.matmul" not in src

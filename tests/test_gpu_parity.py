@@ -1,0 +1,331 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: repacked blobs byte-identical to the independent layout oracle; W4A8 int32
+accumulators bit-identical; one-hot activations reproduce fp16((q - z) * s)
+bit-exactly; every fp16 GEMM output within
+    max|e| <= 2e-3 * sqrt(K) * rms(C_ref)  and  ||e||_F / ||C_ref||_F <= 1e-3.
+Full-size layers are checked on sampled columns the oracle computes one by one,
+in the same launch configuration the benchmark times.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_quantized_qgemm_amd as qg
+from oracle import compare, layout, ref
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _t(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def upload_w4a16(p):
+    return qg.repack_w4a16(_t(p["codes"].view(np.int32)), _t(p["scales"]))
+
+
+def upload_w4a8(p):
+    return qg.repack_w4a8(_t(p["codes"].view(np.int32)), _t(p["group_scales"]), _t(p["chan_scales"]))
+
+
+def upload_w2w4(p):
+    return qg.repack_w2w4(_t(p["codes"]), _t(p["scales"]), p["bitmap"])
+
+
+def _ok(C_gpu, C_ref, K, what):
+    r = compare.check_fp16(C_gpu, C_ref, K)
+    assert r["ok"], (what, r)
+    return r
+
+
+@pytest.fixture(autouse=True)
+def _reset_plan():
+    qg.set_plan_override(0, 0)
+    yield
+    qg.set_plan_override(0, 0)
+
+
+# ----------------------------------------------------------------------------- repack bytes
+@pytest.mark.parametrize("K,N", [(128, 64), (1152, 320), (1024, 1024), (4096, 11008)])
+def test_repack_w4a16_bytes(K, N):
+    _say("repack w4a16", K, N)
+    p = gen.w4a16_problem(1, K, N, seed=K ^ N, activations=False)
+    blob = upload_w4a16(p).cpu().numpy().tobytes()
+    assert blob == layout.blob_w4a16(p["codes"], p["scales"])
+
+
+@pytest.mark.parametrize("K,N", [(128, 64), (1152, 320), (4096, 11008)])
+def test_repack_w4a8_bytes(K, N):
+    _say("repack w4a8", K, N)
+    p = gen.w4a8_problem(1, K, N, seed=3)
+    blob = upload_w4a8(p).cpu().numpy().tobytes()
+    assert blob == layout.blob_w4a8(p["codes"], p["group_scales"], p["chan_scales"])
+
+
+@pytest.mark.parametrize("K,N,frac", [(128, 64, 0.1), (1152, 320, 0.3), (4096, 4096, 0.1),
+                                      (1024, 256, 0.0), (1024, 256, 1.0)])
+def test_repack_w2w4_bytes(K, N, frac):
+    _say("repack w2w4", K, N, frac)
+    p = gen.w2w4_problem(1, K, N, seed=5, frac4=frac)
+    blob = upload_w2w4(p).cpu().numpy().tobytes()
+    assert blob == layout.blob_w2w4(p["codes"], p["bitmap"], p["scales"])
+
+
+# ----------------------------------------------------------------------------- W4A16
+def _one_hot(M, K, rng):
+    ks = rng.choice(K, size=M, replace=False)
+    A = np.zeros((M, K), dtype=np.float16)
+    A[np.arange(M), ks] = 1.0
+    return A, ks
+
+
+@pytest.mark.parametrize("M,K,N,force", [(16, 1024, 1024, None), (5, 4096, 256, (1, 8)),
+                                         (32, 1152, 320, (2, 8)), (20, 8192, 128, (4, 16))])
+def test_w4a16_one_hot_bit_exact(M, K, N, force):
+    _say("w4a16 one-hot", M, K, N, force)
+    rng = np.random.default_rng(M * 7 + K)
+    p = gen.w4a16_problem(1, K, N, seed=M + K, activations=False)
+    A, ks = _one_hot(M, K, rng)
+    if force:
+        qg.set_plan_override(*force)
+    blob = upload_w4a16(p)
+    C = qg.w4a16(_t(A), blob, K, N).cpu().numpy()
+    q = ref.unpack_u4(p["codes"])
+    expect = ((q[ks] - 8).astype(np.float64) * p["scales"][ks // 128].astype(np.float64)).astype(np.float16)
+    assert np.array_equal(C.view(np.uint16), expect.view(np.uint16))
+
+
+def test_w4a16_identity_block_and_zero_point():
+    _say("w4a16 identity / constant 8")
+    K, N = 1024, 512
+    p = gen.w4a16_problem(1, K, N, seed=2, activations=False)
+    A = np.zeros((16, K), dtype=np.float16)
+    A[:, 256:272] = np.eye(16, dtype=np.float16)
+    C = qg.w4a16(_t(A), upload_w4a16(p), K, N).cpu().numpy()
+    q = ref.unpack_u4(p["codes"])
+    expect = ((q[256:272] - 8) * p["scales"][2].astype(np.float64)).astype(np.float16)
+    assert np.array_equal(C.view(np.uint16), expect.view(np.uint16))
+    # constant code 8 gives exactly zero for any activations
+    codes8 = gen.pack_nibbles_u32(np.full((K, N), 8, dtype=np.uint8))
+    blob8 = qg.repack_w4a16(_t(codes8.view(np.int32)), _t(p["scales"]))
+    A2 = gen.w4a16_problem(16, K, N, seed=3, weights=False)["A"]
+    C8 = qg.w4a16(_t(A2), blob8, K, N).cpu().numpy()
+    assert np.all(C8 == 0)
+
+
+def test_w4a16_config_small():
+    _say("w4a16 M=16 K=1024 N=1024")
+    p = gen.w4a16_problem(16, 1024, 1024, seed=0)
+    blob = upload_w4a16(p)
+    A = _t(p["A"])
+    C1 = qg.w4a16(A, blob, 1024, 1024)
+    C2 = qg.w4a16(A, blob, 1024, 1024)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), 1024, "cfg0")
+
+
+@pytest.mark.parametrize("K,N", [(4096, 4096), (4096, 11008), (11008, 4096)])
+def test_w4a16_7b_layers(K, N):
+    p = gen.w4a16_problem(128, K, N, seed=1)
+    blob = upload_w4a16(p)
+    Cref = ref.gemm_w4a16(p["A"], p["codes"], p["scales"])
+    for M in (1, 16, 32, 64, 128):
+        _say("w4a16 7B layer", M, K, N, qg.plan(qg.FMT_W4A16, M, K, N))
+        A = _t(p["A"][:M])
+        C = qg.w4a16(A, blob, K, N).cpu().numpy()
+        _ok(C, Cref[:M], K, (M, K, N))
+
+
+def _sample_cols(N, rng, n=96):
+    edge = [0, 1, 15, 16, 63, 64, 255, 256, N - 65, N - 64, N - 17, N - 16, N - 1]
+    return np.unique(np.concatenate([rng.choice(N, size=n, replace=False), edge]))
+
+
+@pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192)])
+def test_w4a16_70b_layer_sampled(K, N):
+    p = gen.w4a16_problem(128, K, N, seed=2)
+    blob = upload_w4a16(p)
+    rng = np.random.default_rng(K)
+    cols = _sample_cols(N, rng)
+    Cref = ref.gemm_w4a16(p["A"], p["codes"], p["scales"], cols=cols)
+    for M in (1, 2, 4, 8, 16, 32, 64, 128):
+        _say("w4a16 70B layer", M, K, N, qg.plan(qg.FMT_W4A16, M, K, N))
+        C = qg.w4a16(_t(p["A"][:M]), blob, K, N).cpu().numpy()
+        assert np.all(np.isfinite(C))
+        _ok(C[:, cols], Cref[:M], K, (M, K, N))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 7, 15, 17, 31, 33, 47, 100])
+def test_w4a16_ragged_m(M):
+    K, N = 1280, 192                     # G = 10: a partial 8-group scale block
+    _say("w4a16 ragged", M, K, N)
+    p = gen.w4a16_problem(M, K, N, seed=M)
+    C = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N).cpu().numpy()
+    _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, M)
+
+
+@pytest.mark.parametrize("nb,gps", [(1, 8), (2, 8), (4, 8), (1, 16), (4, 24), (2, 0), (4, 0)])
+@pytest.mark.parametrize("M", [16, 20])
+def test_w4a16_forced_splits(nb, gps, M):
+    K, N = 4096, 1024
+    _say("w4a16 forced", nb, gps, M)
+    p = gen.w4a16_problem(M, K, N, seed=11)
+    blob = upload_w4a16(p)
+    qg.set_plan_override(nb, gps)
+    A = _t(p["A"])
+    C1 = qg.w4a16(A, blob, K, N)
+    C2 = qg.w4a16(A, blob, K, N)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, (nb, gps, M))
+
+
+def test_w4a16_strided_and_guard_bands():
+    _say("w4a16 strides + guards")
+    M, K, N = 9, 1024, 256
+    p = gen.w4a16_problem(M, K, N, seed=4)
+    blob = upload_w4a16(p)
+    Abig = torch.zeros((M, K + 64), dtype=torch.float16, device=DEV)
+    Abig[:, :K] = _t(p["A"])
+    sentinel = -12345.0
+    Cbig = torch.full((M + 2, N + 64), sentinel, dtype=torch.float16, device=DEV)
+    out = Cbig[1:M + 1, :N]
+    L = qg.lib()
+    import ctypes
+    ws = torch.zeros(max(1, qg.workspace_bytes(qg.FMT_W4A16, M, K, N)), dtype=torch.uint8, device=DEV)
+    st = L.qgemm_w4a16(ctypes.c_void_p(Abig.data_ptr()), K + 64, ctypes.c_void_p(blob.data_ptr()),
+                       ctypes.c_void_p(out.data_ptr()), N + 64, M, K, N,
+                       ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    Cb = Cbig.cpu().numpy()
+    _ok(Cb[1:M + 1, :N], ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, "strided")
+    assert np.all(Cb[0] == sentinel) and np.all(Cb[M + 1] == sentinel)
+    assert np.all(Cb[:, N:] == sentinel)
+
+
+def test_w4a16_minimal_and_empty():
+    _say("w4a16 minimal")
+    p = gen.w4a16_problem(1, 128, 64, seed=9)
+    blob = upload_w4a16(p)
+    C = qg.w4a16(_t(p["A"]), blob, 128, 64).cpu().numpy()
+    _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), 128, "K=128,N=64")
+    empty = qg.w4a16(torch.zeros((0, 128), dtype=torch.float16, device=DEV), blob, 128, 64)
+    assert empty.shape == (0, 64)
+
+
+# ----------------------------------------------------------------------------- W4A8
+def _w4a8_run(p, M=None, acc=True):
+    K, N = p["K"], p["N"]
+    A = p["A"] if M is None else p["A"][:M]
+    a_s = p["a_scale"] if M is None else p["a_scale"][:M]
+    blob = upload_w4a8(p)
+    acc_out = torch.empty((A.shape[0], N), dtype=torch.int32, device=DEV) if acc else None
+    C = qg.w4a8(_t(A), _t(a_s), blob, K, N, acc_out=acc_out)
+    return C.cpu().numpy(), (acc_out.cpu().numpy() if acc else None)
+
+
+@pytest.mark.parametrize("M", [16, 64, 128])
+def test_w4a8_config_layer(M):
+    K, N = 4096, 11008
+    _say("w4a8", M, K, N, qg.plan(qg.FMT_W4A8, M, K, N))
+    p = gen.w4a8_problem(M, K, N, seed=0)
+    C, acc = _w4a8_run(p)
+    acc_ref, C_ref = ref.gemm_w4a8(p["A"], p["codes"], p["group_scales"], p["a_scale"], p["chan_scales"])
+    assert np.array_equal(acc.astype(np.int64), acc_ref)
+    _ok(C, C_ref, K, ("w4a8", M))
+
+
+@pytest.mark.parametrize("M,force", [(1, None), (3, (1, 8)), (17, (2, 8)), (40, (4, 16)), (33, None)])
+def test_w4a8_ragged_and_splits(M, force):
+    K, N = 2048, 320
+    _say("w4a8 ragged", M, force)
+    p = gen.w4a8_problem(M, K, N, seed=M)
+    if force:
+        qg.set_plan_override(*force)
+    C, acc = _w4a8_run(p)
+    acc_ref, C_ref = ref.gemm_w4a8(p["A"], p["codes"], p["group_scales"], p["a_scale"], p["chan_scales"])
+    assert np.array_equal(acc.astype(np.int64), acc_ref)
+    _ok(C, C_ref, K, ("w4a8 ragged", M))
+
+
+def test_w4a8_one_hot_and_extremes():
+    _say("w4a8 one-hot + extremes")
+    K, N = 1024, 128
+    p = gen.w4a8_problem(8, K, N, seed=6)
+    rng = np.random.default_rng(1)
+    ks = rng.choice(K, size=8, replace=False)
+    A = np.zeros((8, K), dtype=np.int8)
+    A[np.arange(8), ks] = 1
+    p1 = dict(p, A=A)
+    _, acc = _w4a8_run(p1)
+    Wi = ref.w4a8_weights_int(p["codes"], p["group_scales"])
+    assert np.array_equal(acc.astype(np.int64), Wi[ks])
+    # extreme values: A = -128, q = -8, s_g = 127 or -128 everywhere
+    K2 = 16384
+    ext = {"K": K2, "N": 64, "A": np.full((2, K2), -128, dtype=np.int8),
+           "a_scale": np.full(2, 1e-4, dtype=np.float16),
+           "codes": gen.pack_nibbles_u32(np.full((K2, 64), 8, dtype=np.uint8)),
+           "group_scales": np.full((K2 // 128, 64), 127, dtype=np.int8),
+           "chan_scales": np.full(64, 1e-4, dtype=np.float16)}
+    ext["group_scales"][:, 1::2] = -128
+    _, acc2 = _w4a8_run(ext)
+    acc_ref = ref.w4a8_acc(ext["A"], ext["codes"], ext["group_scales"])
+    assert np.array_equal(acc2.astype(np.int64), acc_ref)
+
+
+# ----------------------------------------------------------------------------- mixed 2/4
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_w2w4_config_layer(M):
+    K, N = 4096, 4096
+    _say("w2w4", M, K, N, qg.plan(qg.FMT_W2W4, M, K, N))
+    p = gen.w2w4_problem(M, K, N, seed=0)
+    C = qg.w2w4_mixed(_t(p["A"]), upload_w2w4(p), K, N).cpu().numpy()
+    _ok(C, ref.gemm_w2w4(p["A"], p["codes"], p["bitmap"], p["scales"]), K, ("w2w4", M))
+
+
+@pytest.mark.parametrize("M,frac,force", [(3, 0.0, None), (17, 1.0, None), (20, 0.3, (1, 8)),
+                                          (9, 0.5, (4, 16)), (33, 0.1, (2, 8))])
+def test_w2w4_ragged_and_extremes(M, frac, force):
+    K, N = 2048, 320
+    _say("w2w4 ragged", M, frac, force)
+    p = gen.w2w4_problem(M, K, N, seed=M, frac4=frac)
+    if force:
+        qg.set_plan_override(*force)
+    C = qg.w2w4_mixed(_t(p["A"]), upload_w2w4(p), K, N).cpu().numpy()
+    _ok(C, ref.gemm_w2w4(p["A"], p["codes"], p["bitmap"], p["scales"]), K, ("w2w4", M, frac))
+
+
+def test_w2w4_one_hot_and_all_four_bit_equals_w4a16():
+    _say("w2w4 one-hot / all-4-bit")
+    K, N, M = 1024, 512, 16
+    p = gen.w2w4_problem(M, K, N, seed=8, frac4=0.25)
+    rng = np.random.default_rng(2)
+    A, ks = _one_hot(M, K, rng)
+    C = qg.w2w4_mixed(_t(A), upload_w2w4(p), K, N).cpu().numpy()
+    W = ref.dequant_w2w4(p["codes"], p["bitmap"], p["scales"])
+    assert np.array_equal(C.view(np.uint16), W[ks].astype(np.float16).view(np.uint16))
+    # every group 4-bit: same words, same plan -> bit-identical to the W4A16 kernel
+    full = gen.w2w4_problem(M, K, N, seed=8, mask=np.ones((K // 128, N), dtype=bool))
+    codes32 = gen.pack_nibbles_u32(full["codes"])
+    blob16 = qg.repack_w4a16(_t(codes32.view(np.int32)), _t(full["scales"]))
+    Cm = qg.w2w4_mixed(_t(full["A"]), upload_w2w4(full), K, N)
+    C16 = qg.w4a16(_t(full["A"]), blob16, K, N)
+    torch.cuda.synchronize()
+    assert torch.equal(Cm, C16)
