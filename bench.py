@@ -192,7 +192,7 @@ def main():
                       "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "mfma_frac": round(tf / FP16_PEAK_TFLOPS, 4),
                       "roofline_frac": round(roof_us / us, 4),
-                      "plan": {k: cs["plan"][k] for k in ("mb", "nb", "splits", "gps", "mt", "waves")}})
+                      "plan": {k: cs["plan"][k] for k in ("mb", "nb", "wpt", "splits", "mt", "waves")}})
 
     dom = max(per_m, key=lambda r: r["us"])
     dM = dom["M"]

@@ -19,7 +19,8 @@ namespace {
 
 thread_local std::string g_last_error;
 std::atomic<int> g_force_nb{0};
-std::atomic<int> g_force_gps{0};
+std::atomic<int> g_force_wpt{0};
+std::atomic<int> g_force_splits{0};
 
 constexpr int64_t kMaxM = 65535;
 constexpr int64_t kMaxKN = int64_t(1) << 20;
@@ -122,34 +123,42 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
   const int G = (int)(K / kGroup);
   pl.kernel = 1;
   pl.mb = M <= 16 ? 1 : 2;
-  pl.mt = (int)((M + 16 * pl.mb - 1) / (16 * pl.mb));
-  if (pl.mt < 1) pl.mt = 1;
+  pl.mt = (int)std::max<int64_t>(1, (M + 16 * pl.mb - 1) / (16 * pl.mb));
   const int force_nb = g_force_nb.load();
-  const int force_gps = g_force_gps.load();
+  const int force_wpt = g_force_wpt.load();
+  const int force_splits = g_force_splits.load();
   const int cands[3] = {4, 2, 1};
   for (int ci = 0; ci < 3; ++ci) {
     const int nb = force_nb ? force_nb : cands[ci];
-    const int64_t nt = N / (16 * nb);
-    const int64_t base = nt * pl.mt;
-    int gps;
-    if (force_gps) {
-      gps = force_gps;
-    } else {
-      const int64_t want = std::max<int64_t>(1, kTargetWaves / base);
-      gps = (int)((G + want - 1) / want);
-      gps = std::max(8, (gps + 7) / 8 * 8);
+    const int64_t tiles = (int64_t)pl.mt * (N / (16 * nb));
+    int splits = 1;
+    int wpt = force_wpt ? force_wpt
+                        : (int)std::min<int64_t>(kMaxWavesPerTile, (kTargetWaves + tiles - 1) / tiles);
+    wpt = std::min(wpt, kMaxWavesPerTile);
+    wpt = std::max(1, std::min(wpt, G));
+    while (wpt > 1 && wpt * pl.mb * nb > 64) --wpt;       // LDS reduction buffer <= 64 KiB
+    if (force_splits) {
+      splits = force_splits;
+    } else if (tiles * wpt < kCUs) {
+      // too few waves even with a full workgroup per tile: split K across workgroups
+      splits = (int)std::min<int64_t>((2 * kCUs + tiles * wpt - 1) / (tiles * wpt), G / wpt);
     }
-    if (gps >= G) gps = G;
-    const int splits = (G + gps - 1) / gps;
+    splits = std::max(1, std::min(splits, G));
+    if (tiles > kMaxCounters) splits = 1;
+    int gps = (G + splits - 1) / splits;
+    splits = (G + gps - 1) / gps;
+    wpt = std::min(wpt, gps);
     pl.nb = nb;
-    pl.nt = (int)nt;
-    pl.gps = gps;
+    pl.nt = (int)(N / (16 * nb));
+    pl.wpt = wpt;
     pl.splits = splits;
-    pl.waves = base * splits;
+    pl.gps = gps;
+    pl.workgroups = tiles * splits;
+    pl.waves = pl.workgroups * wpt;
     if (force_nb || pl.waves >= kTargetWaves / 2) break;
   }
   if (pl.splits > 1) {
-    pl.counter_bytes = align256((size_t)pl.mt * pl.nt * 4);
+    pl.counter_bytes = kCounterBytes;
     pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * M * N * 4);
   }
   (void)fmt;
@@ -207,24 +216,27 @@ int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* byte
   return QGEMM_OK;
 }
 
-int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out8) {
+int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10) {
   if (!valid_fmt(fmt)) return QGEMM_ERR_FORMAT;
-  if (!out8) return QGEMM_ERR_NULL;
+  if (!out10) return QGEMM_ERR_NULL;
   int st = check_kn(fmt, K, N);
   if (st) return st;
   if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
   const qg::Plan pl = qg::make_plan(fmt, M, K, N);
-  const int64_t v[8] = {pl.kernel, pl.mb, pl.nb, pl.splits, pl.gps, pl.mt, pl.nt, pl.waves};
-  std::memcpy(out8, v, sizeof(v));
+  const int64_t v[10] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps,
+                         pl.mt, pl.nt, pl.workgroups, pl.waves};
+  std::memcpy(out10, v, sizeof(v));
   return QGEMM_OK;
 }
 
-int qgemm_set_plan_override(int nb_per_wave, int groups_per_split) {
-  if (!(nb_per_wave == 0 || nb_per_wave == 1 || nb_per_wave == 2 || nb_per_wave == 4))
+int qgemm_set_plan_override(int nb_per_tile, int waves_per_tile, int k_splits) {
+  if (!(nb_per_tile == 0 || nb_per_tile == 1 || nb_per_tile == 2 || nb_per_tile == 4))
     return QGEMM_ERR_RANGE;
-  if (groups_per_split < 0 || groups_per_split % 8 != 0) return QGEMM_ERR_RANGE;
-  g_force_nb.store(nb_per_wave);
-  g_force_gps.store(groups_per_split);
+  if (waves_per_tile < 0 || waves_per_tile > qg::kMaxWavesPerTile) return QGEMM_ERR_RANGE;
+  if (k_splits < 0 || k_splits > 4096) return QGEMM_ERR_RANGE;
+  g_force_nb.store(nb_per_tile);
+  g_force_wpt.store(waves_per_tile);
+  g_force_splits.store(k_splits);
   return QGEMM_OK;
 }
 

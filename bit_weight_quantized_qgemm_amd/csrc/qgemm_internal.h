@@ -12,6 +12,12 @@ constexpr int kWave = 64;            // lanes per wavefront (CDNA)
 constexpr int kWavesPerBlock = 4;    // one wave per SIMD of a CU
 constexpr int kCUs = 256;            // MI355X compute units (8 XCDs x 32)
 constexpr int kTargetWaves = kCUs * 8;
+constexpr int kMaxWavesPerTile = 8;   // 512-thread workgroups keep 256 VGPRs per wave
+// Split-K arrival counters live in a fixed region at the start of every
+// workspace, so that calls with different plans sharing one workspace never see
+// another plan's partial sums in place of zero counters.
+constexpr size_t kCounterBytes = 65536;
+constexpr int64_t kMaxCounters = kCounterBytes / 4;
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -28,16 +34,20 @@ struct BlobLayout {
 
 BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4);
 
-// Work decomposition of one GEMM call.
+// Work decomposition of one GEMM call: workgroups own output tiles of
+// 16*mb rows x 16*nb columns; the wpt waves of a workgroup split the tile's K
+// range; `splits` > 1 additionally splits K across workgroups (rare).
 struct Plan {
-  int kernel = 0;        // 1 = skinny streaming kernel
-  int mb = 1;            // 16-row blocks per wave
-  int nb = 4;            // 16-column blocks per wave
-  int splits = 1;        // k-splits
-  int gps = 0;           // groups per split (multiple of 8, except when splits == 1)
+  int kernel = 1;        // 1 = streaming skinny kernel
+  int mb = 1;            // 16-row blocks per tile
+  int nb = 4;            // 16-column blocks per tile
+  int wpt = 1;           // waves per tile (workgroup size / 64)
+  int splits = 1;        // k-splits across workgroups
+  int gps = 0;           // groups per k-split
   int mt = 1;            // m-tiles
   int nt = 1;            // n-tiles
-  int64_t waves = 0;     // waves launched
+  int64_t workgroups = 0;
+  int64_t waves = 0;
   size_t counter_bytes = 0;
   size_t ws_bytes = 0;   // total workspace (0 when splits == 1)
 };
@@ -61,6 +71,9 @@ struct GemmArgs {
   int splits, gps, mt, nt;
 };
 
+size_t lds_bytes_w4a16(const Plan& pl, int G);
+size_t lds_bytes_w4a8(const Plan& pl, int G);
+size_t lds_bytes_w2w4(const Plan& pl, int G);
 hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);

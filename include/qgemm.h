@@ -89,11 +89,14 @@ int qgemm_packed_bytes(int fmt, int64_t K, int64_t N, const uint32_t* bitmap_hos
                        size_t* bytes);
 
 /*
- * Workspace bytes one GEMM call of this shape needs (split-K partial sums and
- * per-tile arrival counters; 0 when the plan does not split K). The workspace
- * must be filled with zero bytes ONCE before its first use; every completed
- * call leaves its counter region zero again, so it can be reused without
- * clearing. A larger workspace is always accepted.
+ * Workspace bytes one GEMM call of this shape needs (0 when the plan does not
+ * split K). Layout: a fixed 64 KiB region of per-tile arrival counters, then the
+ * split-K partial sums. The workspace must be filled with zero bytes ONCE before
+ * its first use; every completed call leaves the counter region zero again, so
+ * one workspace can be reused by any sequence of calls (of any shapes and
+ * formats) on one stream without clearing. A larger workspace is always
+ * accepted. A call interrupted before completion leaves it undefined: zero it
+ * again.
  */
 int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* bytes);
 
@@ -156,20 +159,24 @@ int qgemm_w2w4_mixed(const void* A, int64_t lda, const void* packed, void* C, in
                      void* stream);
 
 /*
- * Work decomposition actually used for a call of this shape (for tests and
- * tuning). Fills out[0..7] = {kernel id, row blocks of 16 per wave (MB),
- * column blocks of 16 per wave (NB), k-splits, groups per split, m-tiles,
- * n-tiles, waves launched}. Host-only; no HIP call.
+ * Work decomposition used for a call of this shape (for tests and tuning).
+ * Fills out10[0..9] = {kernel id, 16-row blocks per tile, 16-column blocks per
+ * tile, waves per tile (workgroup size / 64), k-splits across workgroups,
+ * groups per k-split, m-tiles, n-tiles, workgroups, waves}. Host-only; no HIP
+ * call.
  */
-int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out8);
+int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 
 /*
- * Override the automatic plan for calls on the calling process: column blocks
- * per wave (1, 2 or 4) and groups per k-split (a positive multiple of 8), or
- * 0 to restore automatic choice. For tests of the split-K reduction and for
- * tuning sweeps; affects qgemm_workspace_bytes and qgemm_plan too.
+ * Override the automatic plan for later calls of this process: 16-column blocks
+ * per tile (0, 1, 2 or 4), waves per tile (0..8) and k-splits across
+ * workgroups (0..4096); 0 keeps the automatic choice for that field. Values the
+ * shape cannot use are clamped (no more waves than groups, LDS limits). For
+ * tests of the split-K reductions and for tuning sweeps; affects
+ * qgemm_workspace_bytes and qgemm_plan too. Not thread-safe against concurrent
+ * GEMM calls.
  */
-int qgemm_set_plan_override(int nb_per_wave, int groups_per_split);
+int qgemm_set_plan_override(int nb_per_tile, int waves_per_tile, int k_splits);
 
 #ifdef __cplusplus
 }

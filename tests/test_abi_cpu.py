@@ -125,44 +125,65 @@ def test_repack_validation_without_gpu(L):
     assert L.qgemm_repack(1, K, N, codes, sc, None, None, _fake(0x10000000 + 4096), nb, None) == ERR_ALIAS
 
 
-@pytest.mark.parametrize("K,N", CONFIG_SHAPES)
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 17, 32, 64, 100, 128])
-def test_plan_covers_every_unit_once(K, N, M):
+def _check_plan(p, M, K, N):
     G = K // 128
-    p = qg.plan(qg.FMT_W4A16, M, K, N)
     assert p["nb"] in (1, 2, 4) and p["mb"] in (1, 2)
     assert p["nt"] * p["nb"] * 16 == N
     assert p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
-    assert p["waves"] == p["nt"] * p["mt"] * p["splits"]
-    if p["splits"] > 1:
-        assert p["gps"] % 8 == 0
-    # group ranges of the splits tile [0, G) exactly
+    assert 1 <= p["wpt"] <= 8 and (p["wpt"] == 1 or p["wpt"] * p["mb"] * p["nb"] <= 64)
+    assert p["wpt"] <= p["gps"]
+    assert p["workgroups"] == p["nt"] * p["mt"] * p["splits"]
+    assert p["waves"] == p["workgroups"] * p["wpt"]
+    # every group of K is streamed by exactly one wave of each tile
     cover = np.zeros(G, dtype=int)
     for s in range(p["splits"]):
-        g0 = s * p["gps"]
-        g1 = min(G, g0 + p["gps"])
-        assert g1 > g0
-        cover[g0:g1] += 1
+        G0, G1 = s * p["gps"], min(G, (s + 1) * p["gps"])
+        assert G1 > G0
+        gpw = -(-(G1 - G0) // p["wpt"])
+        for w in range(p["wpt"]):
+            g0 = G0 + w * gpw
+            g1 = min(G1, g0 + gpw)
+            if g1 > g0:
+                cover[g0:g1] += 1
     assert np.all(cover == 1)
     ws = qg.workspace_bytes(qg.FMT_W4A16, M, K, N)
     if p["splits"] == 1:
         assert ws == 0
     else:
-        assert ws >= p["splits"] * M * N * 4 + p["mt"] * p["nt"] * 4
+        assert ws >= p["splits"] * M * N * 4 + 65536
+        assert p["mt"] * p["nt"] <= 16384
+
+
+@pytest.mark.parametrize("K,N", CONFIG_SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 17, 32, 64, 100, 128])
+def test_plan_covers_every_unit_once(K, N, M):
+    _check_plan(qg.plan(qg.FMT_W4A16, M, K, N), M, K, N)
+
+
+@pytest.mark.parametrize("force", [(1, 1, 1), (4, 8, 1), (2, 3, 1), (4, 1, 4), (1, 2, 3),
+                                   (4, 8, 2), (2, 5, 7), (1, 8, 64)])
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 1024), (20, 1280, 192), (1, 28672, 8192)])
+def test_forced_plans_cover_every_unit_once(force, M, K, N):
+    try:
+        qg.set_plan_override(*force)
+        _check_plan(qg.plan(qg.FMT_W4A16, M, K, N), M, K, N)
+    finally:
+        qg.set_plan_override(0, 0, 0)
 
 
 def test_plan_override(L):
     try:
-        assert L.qgemm_set_plan_override(3, 0) == ERR_RANGE
-        assert L.qgemm_set_plan_override(1, 12) == ERR_RANGE
-        qg.set_plan_override(2, 8)
+        assert L.qgemm_set_plan_override(3, 0, 0) == ERR_RANGE
+        assert L.qgemm_set_plan_override(1, 9, 0) == ERR_RANGE
+        assert L.qgemm_set_plan_override(1, 0, -1) == ERR_RANGE
+        qg.set_plan_override(2, 4, 4)
         p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
-        assert p["nb"] == 2 and p["gps"] == 8 and p["splits"] == 4
-        qg.set_plan_override(1, 64)     # more than G groups -> one split
+        assert (p["nb"], p["wpt"], p["splits"], p["gps"]) == (2, 4, 4, 8)
+        qg.set_plan_override(1, 8, 64)   # more splits than groups: one group per split
         p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
-        assert p["splits"] == 1 and p["gps"] == 32
+        assert p["splits"] == 32 and p["gps"] == 1 and p["wpt"] == 1
     finally:
-        qg.set_plan_override(0, 0)
+        qg.set_plan_override(0, 0, 0)
     assert qg.plan(qg.FMT_W4A16, 16, 4096, 4096)["nb"] in (1, 2, 4)
 
 

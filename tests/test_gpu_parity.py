@@ -55,9 +55,9 @@ def _ok(C_gpu, C_ref, K, what):
 
 @pytest.fixture(autouse=True)
 def _reset_plan():
-    qg.set_plan_override(0, 0)
+    qg.set_plan_override(0, 0, 0)
     yield
-    qg.set_plan_override(0, 0)
+    qg.set_plan_override(0, 0, 0)
 
 
 # ----------------------------------------------------------------------------- repack bytes
@@ -94,8 +94,8 @@ def _one_hot(M, K, rng):
     return A, ks
 
 
-@pytest.mark.parametrize("M,K,N,force", [(16, 1024, 1024, None), (5, 4096, 256, (1, 8)),
-                                         (32, 1152, 320, (2, 8)), (20, 8192, 128, (4, 16))])
+@pytest.mark.parametrize("M,K,N,force", [(16, 1024, 1024, None), (5, 4096, 256, (1, 3, 2)),
+                                         (32, 1152, 320, (2, 8, 1)), (20, 8192, 128, (4, 2, 5))])
 def test_w4a16_one_hot_bit_exact(M, K, N, force):
     _say("w4a16 one-hot", M, K, N, force)
     rng = np.random.default_rng(M * 7 + K)
@@ -180,20 +180,21 @@ def test_w4a16_ragged_m(M):
     _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, M)
 
 
-@pytest.mark.parametrize("nb,gps", [(1, 8), (2, 8), (4, 8), (1, 16), (4, 24), (2, 0), (4, 0)])
+@pytest.mark.parametrize("force", [(1, 1, 1), (4, 8, 1), (2, 3, 1), (4, 1, 4), (1, 2, 3),
+                                   (4, 8, 2), (2, 5, 7), (1, 8, 32), (0, 0, 0)])
 @pytest.mark.parametrize("M", [16, 20])
-def test_w4a16_forced_splits(nb, gps, M):
+def test_w4a16_forced_splits(force, M):
     K, N = 4096, 1024
-    _say("w4a16 forced", nb, gps, M)
+    _say("w4a16 forced", force, M, qg.plan(qg.FMT_W4A16, M, K, N))
     p = gen.w4a16_problem(M, K, N, seed=11)
     blob = upload_w4a16(p)
-    qg.set_plan_override(nb, gps)
+    qg.set_plan_override(*force)
     A = _t(p["A"])
     C1 = qg.w4a16(A, blob, K, N)
     C2 = qg.w4a16(A, blob, K, N)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
-    _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, (nb, gps, M))
+    _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, (force, M))
 
 
 def test_w4a16_strided_and_guard_bands():
@@ -252,7 +253,8 @@ def test_w4a8_config_layer(M):
     _ok(C, C_ref, K, ("w4a8", M))
 
 
-@pytest.mark.parametrize("M,force", [(1, None), (3, (1, 8)), (17, (2, 8)), (40, (4, 16)), (33, None)])
+@pytest.mark.parametrize("M,force", [(1, None), (3, (1, 3, 2)), (17, (2, 8, 1)), (40, (4, 2, 4)),
+                                     (33, None), (9, (1, 1, 16))])
 def test_w4a8_ragged_and_splits(M, force):
     K, N = 2048, 320
     _say("w4a8 ragged", M, force)
@@ -300,8 +302,9 @@ def test_w2w4_config_layer(M):
     _ok(C, ref.gemm_w2w4(p["A"], p["codes"], p["bitmap"], p["scales"]), K, ("w2w4", M))
 
 
-@pytest.mark.parametrize("M,frac,force", [(3, 0.0, None), (17, 1.0, None), (20, 0.3, (1, 8)),
-                                          (9, 0.5, (4, 16)), (33, 0.1, (2, 8))])
+@pytest.mark.parametrize("M,frac,force", [(3, 0.0, None), (17, 1.0, None), (20, 0.3, (1, 3, 2)),
+                                          (9, 0.5, (4, 2, 4)), (33, 0.1, (2, 8, 1)),
+                                          (5, 0.2, (1, 1, 16))])
 def test_w2w4_ragged_and_extremes(M, frac, force):
     K, N = 2048, 320
     _say("w2w4 ragged", M, frac, force)
@@ -329,3 +332,17 @@ def test_w2w4_one_hot_and_all_four_bit_equals_w4a16():
     C16 = qg.w4a16(_t(full["A"]), blob16, K, N)
     torch.cuda.synchronize()
     assert torch.equal(Cm, C16)
+
+
+def test_workspace_shared_across_plans():
+    # one workspace serves a sequence of calls whose plans differ in tiles and
+    # splits: each call must find the counter region zero again
+    _say("workspace shared across plans")
+    ws = qg.Workspace()
+    seq = [(5, 4096, 256, (1, 3, 4)), (20, 8192, 128, (4, 2, 8)), (1, 4096, 4096, None),
+           (16, 2048, 1024, (1, 1, 16)), (3, 4096, 4096, (2, 4, 2)), (7, 1024, 64, None)]
+    for M, K, N, force in seq:
+        qg.set_plan_override(*(force or (0, 0, 0)))
+        p = gen.w4a16_problem(M, K, N, seed=M + N)
+        C = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N, workspace=ws).cpu().numpy()
+        _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, ("shared ws", M, K, N, force))
