@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L.qgemm_w4a8.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.qgemm_w2w4_mixed.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.qgemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
-        L.qgemm_set_plan_override.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.qgemm_set_plan_override.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override"):
             getattr(L, name).restype = ctypes.c_int
@@ -114,8 +114,10 @@ def plan(fmt: int, M: int, K: int, N: int) -> dict:
     return dict(zip(keys, list(arr)))
 
 
-def set_plan_override(nb_per_tile: int = 0, waves_per_tile: int = 0, k_splits: int = 0):
-    _check(lib().qgemm_set_plan_override(nb_per_tile, waves_per_tile, k_splits),
+def set_plan_override(nb_per_tile: int = 0, waves_per_tile: int = 0, k_splits: int = 0,
+                      kernel: int = 0):
+    """Force parts of the work decomposition (0 = automatic); see include/qgemm.h."""
+    _check(lib().qgemm_set_plan_override(kernel, nb_per_tile, waves_per_tile, k_splits),
            "qgemm_set_plan_override")
 
 

@@ -21,6 +21,7 @@ thread_local std::string g_last_error;
 std::atomic<int> g_force_nb{0};
 std::atomic<int> g_force_wpt{0};
 std::atomic<int> g_force_splits{0};
+std::atomic<int> g_force_kernel{0};
 
 constexpr int64_t kMaxM = 65535;
 constexpr int64_t kMaxKN = int64_t(1) << 20;
@@ -118,7 +119,46 @@ BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4) {
   return L;
 }
 
+// Large-M W4A16 plan: 4-wave workgroups own 16*mb x 256 tiles; K is split across
+// workgroups only as far as it shortens the number of rounds of resident tiles.
+Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
+  Plan pl;
+  const int G = (int)(K / kGroup);
+  pl.kernel = 2;
+  pl.mb = M <= 64 ? 4 : 8;
+  pl.nb = 4;
+  pl.wpt = 4;
+  pl.mt = (int)((M + 16 * pl.mb - 1) / (16 * pl.mb));
+  pl.nt = (int)(N / kWideCols);
+  const int64_t tiles = (int64_t)pl.mt * pl.nt;
+  const int64_t slots = (int64_t)kCUs * (pl.mb == 4 ? 2 : 1);   // resident workgroups
+  const int force_splits = g_force_splits.load();
+  int best = 1;
+  double best_cost = 1e30;
+  for (int s = 1; s <= std::max(1, std::min(16, G / 2)); ++s) {
+    const double rounds = (double)((tiles * s + slots - 1) / slots);
+    const double cost = rounds / s + (s > 1 ? 0.02 * s : 0.0);
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
+  }
+  int splits = force_splits ? std::min(force_splits, G) : best;
+  if (tiles > kMaxCounters) splits = 1;
+  pl.gps = (G + splits - 1) / splits;
+  pl.splits = (G + pl.gps - 1) / pl.gps;
+  pl.workgroups = tiles * pl.splits;
+  pl.waves = pl.workgroups * pl.wpt;
+  if (pl.splits > 1) {
+    // partial tiles are kept whole (rows padded to the tile) in fragment order
+    pl.counter_bytes = kCounterBytes;
+    pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * pl.mt * 16 * pl.mb * N * 4);
+  }
+  return pl;
+}
+
 Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
+  const int force_kernel = g_force_kernel.load();
+  const bool wide_ok = fmt == QGEMM_FMT_W4A16 && N % kWideCols == 0;
+  if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM)))
+    return make_wide_plan(M, K, N);
   Plan pl;
   const int G = (int)(K / kGroup);
   pl.kernel = 1;
@@ -161,7 +201,6 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
     pl.counter_bytes = kCounterBytes;
     pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * M * N * 4);
   }
-  (void)fmt;
   return pl;
 }
 
@@ -229,11 +268,13 @@ int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10) {
   return QGEMM_OK;
 }
 
-int qgemm_set_plan_override(int nb_per_tile, int waves_per_tile, int k_splits) {
+int qgemm_set_plan_override(int kernel, int nb_per_tile, int waves_per_tile, int k_splits) {
+  if (kernel < 0 || kernel > 2) return QGEMM_ERR_RANGE;
   if (!(nb_per_tile == 0 || nb_per_tile == 1 || nb_per_tile == 2 || nb_per_tile == 4))
     return QGEMM_ERR_RANGE;
   if (waves_per_tile < 0 || waves_per_tile > qg::kMaxWavesPerTile) return QGEMM_ERR_RANGE;
   if (k_splits < 0 || k_splits > 4096) return QGEMM_ERR_RANGE;
+  g_force_kernel.store(kernel);
   g_force_nb.store(nb_per_tile);
   g_force_wpt.store(waves_per_tile);
   g_force_splits.store(k_splits);
@@ -384,7 +425,7 @@ int run_gemm(const GemmCall& g) {
   }
   hipStream_t s = static_cast<hipStream_t>(g.stream);
   hipError_t e;
-  if (g.fmt == QGEMM_FMT_W4A16) e = qg::launch_w4a16(pl, a, s);
+  if (g.fmt == QGEMM_FMT_W4A16) e = pl.kernel == 2 ? qg::launch_w4a16_wide(pl, a, s) : qg::launch_w4a16(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4A8) e = qg::launch_w4a8(pl, a, s);
   else e = qg::launch_w2w4(pl, a, s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

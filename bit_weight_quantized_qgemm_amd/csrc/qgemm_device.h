@@ -34,6 +34,15 @@ __device__ __forceinline__ u32x4 load16(rsrc_t r, uint32_t voff, uint32_t soff) 
 __device__ __forceinline__ u32x2 load8(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
+// Device-scope coherent 16-byte access (SC1 cache policy): visible to, and seen
+// from, every CU and XCD without whole-cache write-back or invalidation.
+constexpr int kCoherentAgent = 16;
+__device__ __forceinline__ f32x4 load16_coherent(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCoherentAgent));
+}
+__device__ __forceinline__ void store16_coherent(f32x4 v, rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, kCoherentAgent);
+}
 
 // v_and_or_b32 with the mask in an SGPR and the OR operand in a VGPR: one VALU
 // op (gfx9 VOP3 cannot carry two literal constants, so plain C++ would split it).

@@ -13,6 +13,8 @@ constexpr int kWavesPerBlock = 4;    // one wave per SIMD of a CU
 constexpr int kCUs = 256;            // MI355X compute units (8 XCDs x 32)
 constexpr int kTargetWaves = kCUs * 8;
 constexpr int kMaxWavesPerTile = 8;   // 512-thread workgroups keep 256 VGPRs per wave
+constexpr int kWideCols = 256;        // columns per tile of the wide kernel
+constexpr int kWideMinM = 33;         // batches from which the wide kernel is used
 // Split-K arrival counters live in a fixed region at the start of every
 // workspace, so that calls with different plans sharing one workspace never see
 // another plan's partial sums in place of zero counters.
@@ -38,8 +40,8 @@ BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4);
 // 16*mb rows x 16*nb columns; the wpt waves of a workgroup split the tile's K
 // range; `splits` > 1 additionally splits K across workgroups (rare).
 struct Plan {
-  int kernel = 1;        // 1 = streaming skinny kernel
-  int mb = 1;            // 16-row blocks per tile
+  int kernel = 1;        // 1 = streaming skinny kernel, 2 = wide (large-M) W4A16 kernel
+  int mb = 1;            // 16-row blocks per tile (per wave for kernel 2)
   int nb = 4;            // 16-column blocks per tile
   int wpt = 1;           // waves per tile (workgroup size / 64)
   int splits = 1;        // k-splits across workgroups
@@ -75,6 +77,7 @@ size_t lds_bytes_w4a16(const Plan& pl, int G);
 size_t lds_bytes_w4a8(const Plan& pl, int G);
 size_t lds_bytes_w2w4(const Plan& pl, int G);
 hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);
+hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);
 

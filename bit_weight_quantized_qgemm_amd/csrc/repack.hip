@@ -9,16 +9,19 @@
 //
 //  W4A16 codes : chunk (b, g) of 1024 B at (b*G + g)*1024; lane l owns 16 B at
 //                +16l = words t = 0..3; word t holds the 8 codes of
-//                k = 128g + 32h + 8t + e (e = 0..7) of column n = 16b + c, element
+//                k = 128g + 32t + 8h + e (e = 0..7) of column n = 16b + c, element
 //                e in nibble sigma(e) = e/2 (e even) or 4 + (e-1)/2 (e odd), so
 //                that one AND/OR per nibble pair yields two fp16 lanes in k order.
 //                That is exactly the v_mfma_f32_16x16x32_f16 B-operand of lane l
-//                for k-step t, with the group's k permuted identically in A.
+//                for k-step t (lanes 16h..16h+15 hold k 8h..8h+7 of the step), and
+//                the matching A fragments of one step are 64 contiguous bytes per
+//                row.
 //  scales      : fp16 [NB][G8][16][8]: lane c loads the scales of 8 groups at once.
-//  W4A8 codes  : same chunks; element e of word t in nibble tau(e) = 2e (e < 4) or
-//                2(e-4) + 1 (e >= 4) so that (w & 0x0F0F0F0F) and
-//                ((w >> 4) & 0x0F0F0F0F) are the int8 B-operand bytes in k order;
-//                the nibble holds q + 8 (0..15).
+//  W4A8 codes  : same chunks; word t = 2u + s holds k = 128g + 64u + 16h + 8s + e
+//                (v_mfma_i32_16x16x64_i8 step u: lanes 16h.. hold k 16h..16h+15),
+//                element e in nibble tau(e) = 2e (e < 4) or 2(e-4) + 1 (e >= 4) so
+//                that (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) are the int8
+//                B-operand bytes in k order; the nibble holds q + 8 (0..15).
 //  W4A8 scales : int8 group scales [NB][G8][16][8], then fp16 channel scales [N].
 //  W2W4 base   : chunk (b, g) of 512 B; lane l owns 8 B = words s = 0, 1; bits
 //                [4p, 4p+1] of word s = low 2 bits of the code at slot p of W4A16
@@ -65,8 +68,9 @@ __global__ void repack_codes_u4(const uint32_t* __restrict__ codes, uint32_t* __
   u32x4 w;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    // canonical word row r = k/8 with k = 128g + 32h + 8t
-    uint32_t src = codes[(size_t)(16 * g + 4 * h + t) * N + n];
+    // canonical word row r = k/8: W4A16 k = 128g + 32t + 8h; W4A8 k = 128g + 64u + 16h + 8s
+    const int r = kW4A8 ? 16 * g + 8 * (t >> 1) + 2 * h + (t & 1) : 16 * g + 4 * t + h;
+    uint32_t src = codes[(size_t)r * N + n];
     if (kW4A8) src ^= 0x88888888u;   // two's-complement q -> q + 8 in every nibble
     w[t] = permute_nibbles<kW4A8>(src);
   }
@@ -113,9 +117,9 @@ __global__ void repack_w2w4_kernel(const uint8_t* __restrict__ codes, const u32x
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int e = sigma_inv(p);
-      const int k0 = 128 * g + 32 * h + 16 * s + e;   // W4A16 word 2s
+      const int k0 = 128 * g + 64 * s + 8 * h + e;   // W4A16 word 2s
       const uint32_t q0 = codes[(size_t)k0 * N + n];
-      const uint32_t q1 = codes[(size_t)(k0 + 8) * N + n];   // word 2s + 1
+      const uint32_t q1 = codes[(size_t)(k0 + 32) * N + n];   // word 2s + 1
       lo[s] |= ((q0 & 3u) << (4 * p)) | ((q1 & 3u) << (4 * p + 2));
       hi[s] |= (((q0 >> 2) & 3u) << (4 * p)) | (((q1 >> 2) & 3u) << (4 * p + 2));
     }

@@ -77,7 +77,7 @@ struct PolicyW2W4 {
                      (uint32_t)(((size_t)(ti.rows - 1) * p.lda + (size_t)ng * kGroup) * 2));
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda * 2 + h * 64);
+        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda * 2 + h * 16);
       sblk = ti.n8 * kScaleChunk;
       sl = lds + c * 16;
       desc = reinterpret_cast<const u32x2*>(lds + desc_offset(ti, NB));
@@ -99,7 +99,7 @@ struct PolicyW2W4 {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 256u + t * 16u);
+        for (int t = 0; t < 4; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 256u + t * 64u);
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7) * 2;
 #pragma unroll
       for (int j = 0; j < NB; ++j) st.s[j] = *reinterpret_cast<const uint16_t*>(sl + j * sblk + off);

@@ -57,7 +57,7 @@ struct PolicyW4A16 {
                      (uint32_t)(((size_t)(ti.rows - 1) * p.lda + (size_t)ng * kGroup) * 2));
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda * 2 + h * 64);
+        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda * 2 + h * 16);
       sblk = ti.n8 * kScaleChunk;
       sl = lds + c * 16;
     }
@@ -67,7 +67,7 @@ struct PolicyW4A16 {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 256u + t * 16u);
+        for (int t = 0; t < 4; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 256u + t * 64u);
       const int g = gw0 + rel;
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7) * 2;
 #pragma unroll

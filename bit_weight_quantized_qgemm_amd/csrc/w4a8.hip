@@ -56,7 +56,7 @@ struct PolicyW4A8 {
                      (uint32_t)((size_t)(ti.rows - 1) * p.lda + (size_t)ng * kGroup));
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda + h * 32);
+        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda + h * 16);
       sblk = ti.n8 * kScaleChunk;
       sl = lds + c * 8;
     }
@@ -66,7 +66,7 @@ struct PolicyW4A8 {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 128u + t * 16u);
+        for (int t = 0; t < 2; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 128u + t * 64u);
       const int g = gw0 + rel;
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7);
 #pragma unroll

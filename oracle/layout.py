@@ -15,14 +15,15 @@ bytes and its size is rounded up to 256):
 W4A16 (format 1)
   codes   NB*G chunks of 1024 B, chunk (b, g) at (b*G + g)*1024. Lane l owns
           16 B at +16*l: words t = 0..3. Word t holds the codes of
-          k = 128*g + 32*h + 8*t + e (e = 0..7), column n = 16*b + c, with
+          k = 128*g + 32*t + 8*h + e (e = 0..7), column n = 16*b + c, with
           element e in nibble sigma(e): sigma(e) = e/2 for even e and
           4 + (e-1)/2 for odd e.
   scales  fp16 at index ((b*G8 + g8)*16 + c)*8 + j  = s[8*g8 + j][16*b + c]
           (0 where 8*g8 + j >= G).
 
 W4A8 (format 2)
-  codes   same chunk geometry; element e of word t in nibble tau(e):
+  codes   same chunk geometry, but word t = 2*u + s (u, s in 0..1) holds
+          k = 128*g + 64*u + 16*h + 8*s + e; element e in nibble tau(e):
           tau(e) = 2*e for e < 4 and 2*(e-4) + 1 for e >= 4; the nibble holds
           the biased code (q mod 16) XOR 8 = q + 8 in 0..15.
   gscales int8 at index ((b*G8 + g8)*16 + c)*8 + j = s_g[8*g8 + j][16*b + c].
@@ -31,8 +32,9 @@ W4A8 (format 2)
 W2W4 mixed (format 3)
   base    NB*G chunks of 512 B, chunk (b, g) at (b*G + g)*512. Lane l owns 8 B
           at +8*l: words s = 0, 1. For slot p = 0..7 let e = sigma^-1(p); bits
-          [4p, 4p+1] hold lo2 of the code at k = 128*g + 32*h + 8*(2s) + e and
-          bits [4p+2, 4p+3] hold lo2 of the code at k + 8 (word 2s+1).
+          [4p, 4p+1] hold lo2 of the W4A16 word-2s code at slot p
+          (k = 128*g + 32*(2s) + 8*h + e) and bits [4p+2, 4p+3] hold lo2 of the
+          W4A16 word-(2s+1) code at slot p (k + 32).
           lo2 = code & 3.
   desc    8 B per chunk (b, g) at (b*G + g)*8: u32 off, u32 mask. mask bit c is
           set when group (g, 16*b + c) is 4-bit; off is the count of 4-bit
@@ -74,11 +76,20 @@ def _tau(e: int) -> int:
 def _codes_by_lane(q: np.ndarray, K: int, N: int) -> np.ndarray:
     """Rearrange codes ``[K][N]`` into ``[NB][G][lane=16h+c][t][e]``.
 
-    k = 128*g + 32*h + 8*t + e, n = 16*b + c.
+    k = 128*g + 32*t + 8*h + e, n = 16*b + c.
     """
     G, NB = K // GROUP, N // 16
-    x = np.asarray(q).reshape(G, 4, 4, 8, NB, 16)      # g, h, t, e, b, c
-    x = x.transpose(4, 0, 1, 5, 2, 3)                  # b, g, h, c, t, e
+    x = np.asarray(q).reshape(G, 4, 4, 8, NB, 16)      # g, t, h, e, b, c
+    x = x.transpose(4, 0, 2, 5, 1, 3)                  # b, g, h, c, t, e
+    return x.reshape(NB, G, 64, 4, 8)
+
+
+def _codes_by_lane_w4a8(q: np.ndarray, K: int, N: int) -> np.ndarray:
+    """``[K][N]`` -> ``[NB][G][lane][t = 2u + s][e]`` with
+    k = 128*g + 64*u + 16*h + 8*s + e."""
+    G, NB = K // GROUP, N // 16
+    x = np.asarray(q).reshape(G, 2, 4, 2, 8, NB, 16)   # g, u, h, s, e, b, c
+    x = x.transpose(5, 0, 2, 6, 1, 3, 4)               # b, g, h, c, u, s, e
     return x.reshape(NB, G, 64, 4, 8)
 
 
@@ -150,7 +161,7 @@ def blob_w4a8(qw: np.ndarray, group_scales: np.ndarray, chan_scales: np.ndarray)
     _check_shape(K, N)
     G, NB = K // GROUP, N // 16
     biased = _unpack_nibbles(qw) ^ np.uint32(8)            # two's complement q -> q + 8
-    q = _codes_by_lane(biased, K, N)
+    q = _codes_by_lane_w4a8(biased, K, N)
     words = np.zeros(q.shape[:4], dtype=np.uint32)
     for e in range(8):
         words |= q[..., e].astype(np.uint32) << np.uint32(4 * _tau(e))
@@ -221,7 +232,7 @@ def decode_w4a16(blob: bytes, K: int, N: int):
     q = np.zeros((NB, G, 64, 4, 8), dtype=np.uint8)
     for e in range(8):
         q[..., e] = (words >> np.uint32(4 * _sigma(e))) & 0xF
-    codes = q.reshape(NB, G, 4, 16, 4, 8).transpose(1, 2, 4, 5, 0, 3).reshape(K, N)
+    codes = q.reshape(NB, G, 4, 16, 4, 8).transpose(1, 4, 2, 5, 0, 3).reshape(K, N)
     s0 = _align256(NB * G * 1024)
     sc = raw[s0:s0 + NB * G8 * 256].view(np.float16).reshape(NB, G8, 16, 8)
     scales = sc.transpose(1, 3, 0, 2).reshape(G8 * 8, N)[:G]

@@ -127,6 +127,17 @@ def test_repack_validation_without_gpu(L):
 
 def _check_plan(p, M, K, N):
     G = K // 128
+    if p["kernel"] == 2:
+        assert p["mb"] in (4, 8) and p["nb"] == 4 and p["wpt"] == 4
+        assert p["nt"] * 256 == N and p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
+        assert p["workgroups"] == p["nt"] * p["mt"] * p["splits"]
+        cover = np.zeros(G, dtype=int)
+        for s in range(p["splits"]):
+            G0, G1 = s * p["gps"], min(G, (s + 1) * p["gps"])
+            assert G1 > G0
+            cover[G0:G1] += 1
+        assert np.all(cover == 1)
+        return
     assert p["nb"] in (1, 2, 4) and p["mb"] in (1, 2)
     assert p["nt"] * p["nb"] * 16 == N
     assert p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
@@ -173,9 +184,10 @@ def test_forced_plans_cover_every_unit_once(force, M, K, N):
 
 def test_plan_override(L):
     try:
-        assert L.qgemm_set_plan_override(3, 0, 0) == ERR_RANGE
-        assert L.qgemm_set_plan_override(1, 9, 0) == ERR_RANGE
-        assert L.qgemm_set_plan_override(1, 0, -1) == ERR_RANGE
+        assert L.qgemm_set_plan_override(0, 3, 0, 0) == ERR_RANGE
+        assert L.qgemm_set_plan_override(0, 1, 9, 0) == ERR_RANGE
+        assert L.qgemm_set_plan_override(0, 1, 0, -1) == ERR_RANGE
+        assert L.qgemm_set_plan_override(3, 0, 0, 0) == ERR_RANGE
         qg.set_plan_override(2, 4, 4)
         p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
         assert (p["nb"], p["wpt"], p["splits"], p["gps"]) == (2, 4, 4, 8)
@@ -185,6 +197,18 @@ def test_plan_override(L):
     finally:
         qg.set_plan_override(0, 0, 0)
     assert qg.plan(qg.FMT_W4A16, 16, 4096, 4096)["nb"] in (1, 2, 4)
+    # large batches use the wide kernel when N is a multiple of 256
+    assert qg.plan(qg.FMT_W4A16, 128, 8192, 28672)["kernel"] == 2
+    assert qg.plan(qg.FMT_W4A16, 128, 8192, 28736)["kernel"] == 1
+    assert qg.plan(qg.FMT_W4A8, 128, 4096, 11008)["kernel"] == 1
+    try:
+        qg.set_plan_override(kernel=1)
+        assert qg.plan(qg.FMT_W4A16, 128, 8192, 28672)["kernel"] == 1
+        qg.set_plan_override(kernel=2, k_splits=3)
+        p = qg.plan(qg.FMT_W4A16, 8, 8192, 28672)
+        assert p["kernel"] == 2 and p["splits"] == 3
+    finally:
+        qg.set_plan_override()
 
 
 def test_binding_needs_built_library_and_no_cpu_path():

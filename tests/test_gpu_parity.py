@@ -55,9 +55,9 @@ def _ok(C_gpu, C_ref, K, what):
 
 @pytest.fixture(autouse=True)
 def _reset_plan():
-    qg.set_plan_override(0, 0, 0)
+    qg.set_plan_override()
     yield
-    qg.set_plan_override(0, 0, 0)
+    qg.set_plan_override()
 
 
 # ----------------------------------------------------------------------------- repack bytes
@@ -346,3 +346,45 @@ def test_workspace_shared_across_plans():
         p = gen.w4a16_problem(M, K, N, seed=M + N)
         C = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N, workspace=ws).cpu().numpy()
         _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, ("shared ws", M, K, N, force))
+
+
+# ----------------------------------------------------------------------------- wide W4A16 kernel
+@pytest.mark.parametrize("M,K,N,splits", [(48, 1024, 512, 0), (128, 2048, 256, 3), (130, 1280, 512, 0),
+                                          (64, 4096, 768, 5)])
+def test_w4a16_wide_one_hot_bit_exact(M, K, N, splits):
+    _say("w4a16 wide one-hot", M, K, N, splits)
+    rng = np.random.default_rng(M + K + N)
+    p = gen.w4a16_problem(1, K, N, seed=M * 3 + 1, activations=False)
+    A, ks = _one_hot(M, K, rng)
+    qg.set_plan_override(kernel=2, k_splits=splits)
+    assert qg.plan(qg.FMT_W4A16, M, K, N)["kernel"] == 2
+    C = qg.w4a16(_t(A), upload_w4a16(p), K, N).cpu().numpy()
+    q = ref.unpack_u4(p["codes"])
+    expect = ((q[ks] - 8).astype(np.float64) * p["scales"][ks // 128].astype(np.float64)).astype(np.float16)
+    assert np.array_equal(C.view(np.uint16), expect.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 17, 33, 47, 64, 65, 100, 127, 128, 129, 200])
+def test_w4a16_wide_ragged(M):
+    K, N = 1280, 512                      # G = 10, two 256-column tiles
+    _say("w4a16 wide ragged", M, K, N)
+    p = gen.w4a16_problem(M, K, N, seed=M + 5)
+    qg.set_plan_override(kernel=2)
+    C1 = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N)
+    C2 = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, ("wide", M))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+@pytest.mark.parametrize("M", [40, 128])
+def test_w4a16_wide_forced_splits(splits, M):
+    K, N = 4096, 512
+    _say("w4a16 wide splits", splits, M)
+    p = gen.w4a16_problem(M, K, N, seed=splits)
+    qg.set_plan_override(kernel=2, k_splits=splits)
+    pl = qg.plan(qg.FMT_W4A16, M, K, N)
+    assert pl["kernel"] == 2 and pl["splits"] == splits
+    C = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N).cpu().numpy()
+    _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, ("wide splits", splits, M))

@@ -40,12 +40,12 @@ def test_w4a16_hand_derived_words():
     blob = np.frombuffer(layout.blob_w4a16(gen.pack_nibbles_u32(q),
                                            np.ones((2, N), np.float16)), dtype="<u4")
     g = _golden()
-    # chunk (b=0, g=0), lane 0 (c=0, h=0), word t=0 covers k = 0..7
-    assert blob[0] == g["w4a16_k_mod16_b0g0_l0_t0"]
-    # word t=1 covers k = 8..15
-    assert blob[1] == g["w4a16_k_mod16_b0g0_l0_t1"]
-    # lane 16 (h=1) word 0 covers k = 32..39 -> codes 0..7 again
-    assert blob[16 * 4] == g["w4a16_k_mod16_b0g0_l0_t0"]
+    # chunk (b=0, g=0): lane 0 word 0 is k = 0..7, word 1 is k = 32..39
+    assert blob[0] == g["w4a16_codes0to7"]
+    assert blob[1] == g["w4a16_codes0to7"]
+    # lane 16 (h=1) word 0 is k = 8..15, word 1 is k = 40..47
+    assert blob[16 * 4] == g["w4a16_codes8to15"]
+    assert blob[16 * 4 + 1] == g["w4a16_codes8to15"]
     q2 = _pattern(K, N, lambda k, n: n % 16)
     blob2 = np.frombuffer(layout.blob_w4a16(gen.pack_nibbles_u32(q2),
                                             np.ones((2, N), np.float16)), dtype="<u4")
@@ -75,12 +75,13 @@ def test_w4a8_hand_derived_words():
     blob = np.frombuffer(layout.blob_w4a8(gen.pack_nibbles_u32(q),
                                           np.ones((1, N), np.int8),
                                           np.ones(N, np.float16)), dtype="<u4")
-    assert blob[0] == _golden()["w4a8_k_mod16_b0g0_l0_t0"]
+    assert blob[0] == _golden()["w4a8_lane0_word0"]
+    assert blob[1] == _golden()["w4a8_lane0_word1"]
 
 
 def test_w2w4_hand_derived_words_and_desc():
     K, N = 128, 64
-    q = _pattern(K, N, lambda k, n: (k % 4) + 4 * ((k // 8) % 4))
+    q = _pattern(K, N, lambda k, n: (k % 4) + 4 * ((k // 32) % 4))
     mask = np.zeros((1, N), dtype=bool)
     mask[0, [0, 2, 17]] = True
     bm = gen.bitmap_from_mask(mask)
@@ -96,6 +97,7 @@ def test_w2w4_hand_derived_words_and_desc():
     h0 = d0 + 256 + 1024                # desc region: 32 B -> 256; scales: NB*G8*256 = 1024
     hi = np.frombuffer(blob[h0:h0 + 96], dtype="<u4")
     assert hi[0] == g["w2w4_high_col0_h0_s0"]
+    assert hi[1] == g["w2w4_high_col0_h0_s1"]
     assert len(blob) == layout.packed_bytes(layout.FMT_W2W4, K, N, n4=3)
 
 
