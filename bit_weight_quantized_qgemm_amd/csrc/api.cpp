@@ -159,6 +159,8 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
   const bool wide_ok = fmt == QGEMM_FMT_W4A16 && N % kWideCols == 0;
   if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM)))
     return make_wide_plan(M, K, N);
+  // Streaming kernel: 4*KP-wave workgroups own 16*mb x 64*nb tiles; the 4
+  // column waves of each of the KP K-parts share activations through LDS.
   Plan pl;
   const int G = (int)(K / kGroup);
   pl.kernel = 1;
@@ -167,39 +169,34 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
   const int force_nb = g_force_nb.load();
   const int force_wpt = g_force_wpt.load();
   const int force_splits = g_force_splits.load();
-  const int cands[3] = {4, 2, 1};
-  for (int ci = 0; ci < 3; ++ci) {
-    const int nb = force_nb ? force_nb : cands[ci];
-    const int64_t tiles = (int64_t)pl.mt * (N / (16 * nb));
-    int splits = 1;
-    int wpt = force_wpt ? force_wpt
-                        : (int)std::min<int64_t>(kMaxWavesPerTile, (kTargetWaves + tiles - 1) / tiles);
-    wpt = std::min(wpt, kMaxWavesPerTile);
-    wpt = std::max(1, std::min(wpt, G));
-    while (wpt > 1 && wpt * pl.mb * nb > 64) --wpt;       // LDS reduction buffer <= 64 KiB
-    if (force_splits) {
-      splits = force_splits;
-    } else if (tiles * wpt < kCUs) {
-      // too few waves even with a full workgroup per tile: split K across workgroups
-      splits = (int)std::min<int64_t>((2 * kCUs + tiles * wpt - 1) / (tiles * wpt), G / wpt);
-    }
-    splits = std::max(1, std::min(splits, G));
-    if (tiles > kMaxCounters) splits = 1;
-    int gps = (G + splits - 1) / splits;
-    splits = (G + gps - 1) / gps;
-    wpt = std::min(wpt, gps);
-    pl.nb = nb;
-    pl.nt = (int)(N / (16 * nb));
-    pl.wpt = wpt;
-    pl.splits = splits;
-    pl.gps = gps;
-    pl.workgroups = tiles * splits;
-    pl.waves = pl.workgroups * wpt;
-    if (force_nb || pl.waves >= kTargetWaves / 2) break;
+  int nb = force_nb ? std::min(force_nb, 2) : 1;
+  if (N % (64 * nb) != 0) nb = 1;
+  int kp = force_wpt ? std::max(1, force_wpt / 4) : (G >= 16 ? 4 : G >= 8 ? 2 : 1);
+  if (kp == 3) kp = 2;
+  const int64_t tiles = (int64_t)pl.mt * (N / (64 * nb));
+  int splits = 1;
+  if (force_splits) {
+    splits = force_splits;
+  } else if (tiles < kCUs) {
+    // too few tiles for the chip: split K across workgroups as well
+    splits = (int)std::min<int64_t>((2 * kCUs + tiles - 1) / tiles, std::max(1, G / (2 * kp)));
   }
+  splits = std::max(1, std::min(splits, G));
+  if (tiles > kMaxCounters) splits = 1;
+  int gps = (G + splits - 1) / splits;
+  splits = (G + gps - 1) / gps;
+  while (kp > 1 && kp > gps) kp /= 2;       // every K-part gets at least one group
+  pl.nb = nb;
+  pl.nt = (int)(N / (64 * nb));
+  pl.wpt = 4 * kp;
+  pl.splits = splits;
+  pl.gps = gps;
+  pl.workgroups = tiles * splits;
+  pl.waves = pl.workgroups * pl.wpt;
   if (pl.splits > 1) {
+    // partial tiles are kept whole (rows padded to the tile) in fragment order
     pl.counter_bytes = kCounterBytes;
-    pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * M * N * 4);
+    pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * pl.mt * 16 * pl.mb * N * 4);
   }
   return pl;
 }
@@ -272,7 +269,8 @@ int qgemm_set_plan_override(int kernel, int nb_per_tile, int waves_per_tile, int
   if (kernel < 0 || kernel > 2) return QGEMM_ERR_RANGE;
   if (!(nb_per_tile == 0 || nb_per_tile == 1 || nb_per_tile == 2 || nb_per_tile == 4))
     return QGEMM_ERR_RANGE;
-  if (waves_per_tile < 0 || waves_per_tile > qg::kMaxWavesPerTile) return QGEMM_ERR_RANGE;
+  if (!(waves_per_tile == 0 || waves_per_tile == 4 || waves_per_tile == 8 || waves_per_tile == 16))
+    return QGEMM_ERR_RANGE;
   if (k_splits < 0 || k_splits > 4096) return QGEMM_ERR_RANGE;
   g_force_kernel.store(kernel);
   g_force_nb.store(nb_per_tile);

@@ -12,7 +12,7 @@ constexpr int kWave = 64;            // lanes per wavefront (CDNA)
 constexpr int kWavesPerBlock = 4;    // one wave per SIMD of a CU
 constexpr int kCUs = 256;            // MI355X compute units (8 XCDs x 32)
 constexpr int kTargetWaves = kCUs * 8;
-constexpr int kMaxWavesPerTile = 8;   // 512-thread workgroups keep 256 VGPRs per wave
+constexpr int kMaxWavesPerTile = 16;
 constexpr int kWideCols = 256;        // columns per tile of the wide kernel
 constexpr int kWideMinM = 33;         // batches from which the wide kernel is used
 // Split-K arrival counters live in a fixed region at the start of every
@@ -36,13 +36,14 @@ struct BlobLayout {
 
 BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4);
 
-// Work decomposition of one GEMM call: workgroups own output tiles of
-// 16*mb rows x 16*nb columns; the wpt waves of a workgroup split the tile's K
-// range; `splits` > 1 additionally splits K across workgroups (rare).
+// Work decomposition of one GEMM call. Kernel 1: workgroups of wpt = 4*KP
+// waves own tiles of 16*mb rows x 64*nb columns, KP K-parts of 4 column waves;
+// kernel 2: 4-wave workgroups own 16*mb x 256 tiles. `splits` > 1 additionally
+// splits K across workgroups.
 struct Plan {
   int kernel = 1;        // 1 = streaming skinny kernel, 2 = wide (large-M) W4A16 kernel
   int mb = 1;            // 16-row blocks per tile (per wave for kernel 2)
-  int nb = 4;            // 16-column blocks per tile
+  int nb = 1;            // 16-column blocks per wave
   int wpt = 1;           // waves per tile (workgroup size / 64)
   int splits = 1;        // k-splits across workgroups
   int gps = 0;           // groups per k-split

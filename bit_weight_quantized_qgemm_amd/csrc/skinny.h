@@ -1,24 +1,29 @@
-// Shared driver of the streaming quantized-weight GEMM kernels (gfx950).
+// Shared driver of the streaming quantized-weight GEMM kernels (gfx950), used for
+// small and medium batches (the memory-bound regime of the MARLIN abstract).
 //
 // Work decomposition (the "task scheduling" of the MARLIN abstract, re-derived
 // for CDNA4):
-//   * one workgroup = one output tile of 16*MB rows x 16*NB columns, over the
-//     K range of its k-split (almost always the whole K);
-//   * its W waves (1..8) split that K range into W contiguous group ranges and
-//     stream them concurrently: small-M layers have few tiles, so parallelism
-//     comes from K (split-K inside the workgroup);
-//   * each wave keeps D groups of weights and activations in flight in a
-//     register ring (the "asynchronous memory access and pipelining");
-//   * the W partial tiles are summed in LDS in wave order (deterministic), and
-//     the workgroup writes fp16 C. No global workspace, no atomics.
-//   * Only when a layer has too few tiles even for 8 waves each does the plan
-//     also split K across workgroups; those partial tiles go through a global
-//     workspace with device-coherent stores and one arrival counter per tile;
-//     the last workgroup to arrive adds them in split order.
+//   * a workgroup owns one output tile of 16*MB rows x 64*NBW columns over the K
+//     range of its k-split (usually all of K);
+//   * its 4*KP waves form KP K-parts of 4 column waves: column wave n streams
+//     16*NBW columns, K-part k the k-th contiguous share of the tile's groups;
+//   * the 4 column waves of a K-part share the activations through LDS: each
+//     group's A fragments (16 rows x 32 fp16 or x 64 int8 k per KB, already in
+//     MFMA operand order) arrive by direct buffer-to-LDS loads two groups ahead
+//     into a 3-slot ring, each column wave fetching a quarter, published by one
+//     barrier per group;
+//   * weights stream per wave into a 3-stage register ring, also two groups
+//     ahead, so every wave keeps two groups of loads in flight;
+//   * at the end the KP partial tiles are summed in LDS in K-part order
+//     (deterministic) and written as fp16;
+//   * only when a layer has too few tiles does the plan also split K across
+//     workgroups; those partials go through a global workspace in fragment order
+//     with device-coherent 16-byte stores and loads and one arrival counter per
+//     tile; the last workgroup to arrive adds them in split order.
 //
-// A format policy F supplies the per-group stage (what one wave loads for one
-// group), its load and its math. Group scales of the tile are staged in LDS once
-// per workgroup, so a wave's K range may start at any group.
+// A format policy F supplies the per-group weight stage (load and math), the A
+// fragment geometry and the output conversion. Group scales of the tile are
+// staged in LDS once per workgroup, after the first loads are already in flight.
 #pragma once
 
 #include "qgemm_device.h"
@@ -26,7 +31,25 @@
 
 namespace qg {
 
-// LDS layout: [scale region | (after the main loop) reduction region]
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// vmcnt(n) with the other counters left unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence: __syncthreads() is a release fence,
+// which would also wait for every direct-to-LDS prefetch in flight. Callers make
+// their own completions explicit with wait_vmcnt; the compiler fences keep LDS
+// accesses on their side of the barrier.
+__device__ __forceinline__ void raw_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 struct TileInfo {
   int b0;      // first 16-column block of the tile
   int row0;    // first row of the tile
@@ -34,60 +57,6 @@ struct TileInfo {
   int G0, G1;  // group range of the workgroup
   int c8;      // first 8-group scale chunk (G0 / 8)
   int n8;      // scale chunks staged per column block
-};
-
-// Reduce W waves' accumulators through LDS and hand each output element to
-// `emit(row, col, value)` exactly once. Accumulators are 4-vectors of float or
-// int32; lane (c, h) of a wave holds rows 4h..4h+3 of column c of each 16x16 block.
-template <int MB, int NB, typename V, typename Emit>
-__device__ __forceinline__ void reduce_tile(const V (&acc)[MB][NB], char* lds, int W, int lane,
-                                            int wave, const TileInfo& ti, Emit emit) {
-  using E = decltype(acc[0][0][0] + acc[0][0][0]);
-  E* red = reinterpret_cast<E*>(lds);
-  constexpr int kPer = MB * NB * 4;   // elements per lane per wave
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        red[((wave * kPer) + (mb * NB + j) * 4 + i) * 64 + lane] = acc[mb][j][i];
-  __syncthreads();
-  const int nthreads = W * 64;
-  for (int e = threadIdx.x; e < kPer * 64; e += nthreads) {
-    E v = red[e];
-    for (int w = 1; w < W; ++w) v += red[w * kPer * 64 + e];
-    const int ln = e & 63, idx = e >> 6;
-    const int i = idx & 3, blk = idx >> 2;
-    const int j = blk % NB, mb = blk / NB;
-    const int row = ti.row0 + mb * 16 + 4 * (ln >> 4) + i;
-    const int col = (ti.b0 + j) * 16 + (ln & 15);
-    if (row < ti.row0 + ti.rows) emit(row, col, v);
-  }
-}
-
-// Cross-workgroup k-split: publish this workgroup's reduced tile, count arrivals,
-// and let the last arriver finish the tile. Partial stores and loads are
-// device-scope atomics (cache-coherent across XCDs without whole-cache
-// maintenance); every thread waits for its own stores before the barrier that
-// precedes the counter increment.
-template <typename E>
-struct CrossSplit {
-  E* part;              // [splits][M][N]
-  uint32_t* counter;    // this tile's counter
-  int split, splits, M, N;
-
-  __device__ __forceinline__ void publish(int row, int col, E v) const {
-    __hip_atomic_store(part + ((size_t)split * M + row) * N + col, v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __device__ __forceinline__ E gather(int row, int col) const {
-    E s = 0;
-    for (int q = 0; q < splits; ++q)
-      s += __hip_atomic_load(part + ((size_t)q * M + row) * N + col, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    return s;
-  }
 };
 
 // Returns true in every thread of the workgroup that arrived last.
@@ -117,17 +86,39 @@ __device__ __forceinline__ void stage_scales(const void* scales, char* lds, int 
   }
 }
 
-template <class F, int MB, int NB, int D>
-__global__ void __launch_bounds__(512) skinny_gemm(GemmArgs p) {
-  using Acc = typename F::Acc;
-  using Stage = typename F::template Stage<MB, NB>;
-  using View = typename F::template View<MB, NB>;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int s_flag;
+// LDS layout of a launch: [scales | extra | A rings (KP x 3 slots)]; the
+// reduction buffer reuses the start of LDS after the main loop.
+struct SkinnyLds {
+  int scale_bytes, extra_off, ring_off, slot_bytes, total;
+};
 
-  const int W = blockDim.x >> 6;
+template <class F>
+__host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_max, int ng_max) {
+  SkinnyLds L;
+  const int NB = 4 * NBW;
+  L.scale_bytes = NB * n8_max * F::kScaleChunk;
+  L.extra_off = L.scale_bytes;
+  const int extra = F::extra_lds(NB, ng_max);
+  L.ring_off = (L.extra_off + extra + 255) / 256 * 256;
+  L.slot_bytes = MB * F::kFrag * 1024;
+  const int rings = L.ring_off + KP * 3 * L.slot_bytes;
+  const int red = KP * 4 * MB * NBW * 1024;   // one 1 KB fragment of floats per (wave, block)
+  L.total = rings > red ? rings : red;
+  return L;
+}
+
+template <class F, int MB, int NBW, int KP>
+__device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* flag) {
+  using Acc = typename F::Acc;
+  using Stage = typename F::template Stage<NBW>;
+  using View = typename F::template View<NBW>;
+  constexpr int NB = 4 * NBW;
+  constexpr int kFrags = MB * F::kFrag;          // A fragments per group per K-part
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kp = wave >> 2, nw = wave & 3;
+  const int c = lane & 15, h = lane >> 4;
   const int nt = blockIdx.x % p.nt;
   const int rest = blockIdx.x / p.nt;
   const int mt = rest % p.mt;
@@ -141,92 +132,193 @@ __global__ void __launch_bounds__(512) skinny_gemm(GemmArgs p) {
   ti.G1 = min(p.G, ti.G0 + p.gps);
   ti.c8 = ti.G0 >> 3;
   ti.n8 = ((ti.G1 - 1) >> 3) - ti.c8 + 1;
-
-  stage_scales(p.scales, lds, NB, p.G8, ti.b0, ti.c8, ti.n8, F::kScaleChunk);
-  F::stage_extra(p, lds, ti, NB);
-  __syncthreads();
-
-  // this wave's groups [gw0, gw0 + ng)
   const int ngw = ti.G1 - ti.G0;
-  const int gpw = (ngw + W - 1) / W;
-  const int gw0 = ti.G0 + wave * gpw;
-  const int ng = min(ti.G1, gw0 + gpw) - gw0;
+  const SkinnyLds L = skinny_lds<F>(MB, NBW, KP, (min(p.G, p.gps) + 7) / 8 + 1, min(p.G, p.gps));
 
-  Acc acc[MB][NB];
+  // this K-part's groups [gk0, gk0 + ngk); every K-part runs `iters` iterations
+  const int iters = (ngw + KP - 1) / KP;
+  const int gk0 = ti.G0 + kp * iters;
+  const int ngk = max(0, min(ti.G1 - gk0, iters));
+  const int nload = max(ngk, 1);                  // clamp target for reloads
+  const int gk0c = ngk > 0 ? gk0 : ti.G0;         // empty K-parts re-read the first group
+
+  // ---- activations: this K-part's fragments, a quarter per column wave
+  const size_t arow = (size_t)p.lda * F::kAElem;
+  const rsrc_t ra = make_rsrc(static_cast<const char*>(p.A) + (size_t)ti.row0 * arow + (size_t)gk0c * 128 * F::kAElem,
+                              (uint32_t)((size_t)(ti.rows - 1) * arow + (size_t)nload * 128 * F::kAElem));
+  constexpr int kAPerWave = (kFrags + 3) / 4;     // fragment loads per column wave per group
+  uint32_t avoff[kAPerWave];
+  int afrag[kAPerWave];
+#pragma unroll
+  for (int q = 0; q < kAPerWave; ++q) {
+    const int fr = min(nw + 4 * q, kFrags - 1);   // waves past the last fragment duplicate it
+    const int rb = fr / F::kFrag, f = fr % F::kFrag;
+    afrag[q] = fr;
+    avoff[q] = (uint32_t)((size_t)min(rb * 16 + c, ti.rows - 1) * arow + 64 * f + 16 * h);
+  }
+  char* ring = lds + L.ring_off + kp * 3 * L.slot_bytes;
+  auto issue_a = [&](int rel, int slot) {
+#pragma unroll
+    for (int q = 0; q < kAPerWave; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ring + slot * L.slot_bytes + afrag[q] * 1024), 16,
+                                               avoff[q], rel * (128u * F::kAElem), 0, 0);
+  };
+
+  const View v(p, lds, L, ti, ti.b0 + nw * NBW, gk0c, nload, lane);
+  Acc acc[MB][NBW];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
+    for (int j = 0; j < NBW; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
 
-  if (ng > 0) {
-    const View v(p, lds, ti, gw0, ng, lane);
-    typename F::Consts k;
-    // Register ring of 4 stages with static slots: loads for group g + D are
-    // issued before the math of group g. Groups past the end (ragged tail of the
-    // 4-group body) reload the last group and are scaled by zero, so the body
-    // stays one basic block.
-    Stage st[4];
+  // ---- prologue: the first two groups' loads go out before the scale staging
+  Stage st[3];
+  issue_a(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  v.load_vmem(st[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_a(min(1, nload - 1), 1);
+  __builtin_amdgcn_sched_barrier(0);
+  v.load_vmem(st[1], min(1, nload - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  stage_scales(p.scales, lds, NB, p.G8, ti.b0, ti.c8, ti.n8, F::kScaleChunk);
+  F::stage_extra(p, lds + L.extra_off, ti, NB);
+  __syncthreads();
+  v.load_lds(st[0], 0);
+  v.load_lds(st[1], min(1, nload - 1));
+
+  const typename F::Consts k;
+  // Per iteration each wave issues one batch: its A fragments of group i + 2,
+  // then the weights of group i + 2. At the wait of iteration i at least the
+  // weights of group i and the whole batch of group i + 1 were issued after
+  // the wave's last A(i) load, and the counter retires loads in order.
+  constexpr int kAfter = kAPerWave + 2 * Stage::kVmem;
+  for (int base = 0; base < iters; base += 3) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) v.load(st[d], min(d, ng - 1));
-    for (int base = 0; base < ng; base += 4) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v.load(st[(r + D) & 3], min(base + r + D, ng - 1));
+    for (int r = 0; r < 3; ++r) {
+      const int i = base + r;
+      if (i < iters) {   // uniform over the workgroup
+        wait_vmcnt<kAfter>();
+        raw_barrier();
+        issue_a(min(i + 2, nload - 1), (r + 2) % 3);
+        v.load_vmem(st[(r + 2) % 3], min(i + 2, nload - 1));
         __builtin_amdgcn_sched_barrier(0);
-        F::template compute<MB, NB>(st[r], acc, base + r < ng, k, lane);
+        v.load_lds(st[(r + 2) % 3], min(i + 2, nload - 1));
+        F::template compute<MB, NBW>(st[r], ring + r * L.slot_bytes, acc, i < ngk, k, lane);
       }
     }
   }
-  __syncthreads();   // scale/extra LDS regions are dead: reuse LDS for the reduction
+  __syncthreads();   // all LDS reads done: reuse LDS for the reduction
 
+  // ---- reduce the KP K-parts in K-part order; fragment (wave, mb, j) = 1 KB
+  using E = typename F::Elem;
+  E* red = reinterpret_cast<E*>(lds);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(((wave * MB + mb) * NBW + j) * 64 + lane) * 4 + i] = acc[mb][j][i];
+  __syncthreads();
+  constexpr int kTileElems = 4 * MB * NBW * 256;   // 4 column waves x fragments x 256
+  const int tid = threadIdx.x;
   if (p.splits == 1) {
-    auto emit = [&](int row, int col, typename F::Elem v) { F::store(p, row, col, v); };
-    reduce_tile<MB, NB>(acc, lds, W, lane, wave, ti, emit);
+    for (int e = tid; e < kTileElems; e += KP * 256) {
+      E s = red[e];
+      for (int q = 1; q < KP; ++q) s += red[q * kTileElems + e];
+      const int i = e & 3, ln = (e >> 2) & 63, fj = e >> 8;      // fj = (nw*MB + mb)*NBW + j
+      const int j = fj % NBW, mb = (fj / NBW) % MB, w = fj / (NBW * MB);
+      const int row = ti.row0 + mb * 16 + 4 * (ln >> 4) + i;
+      const int col = (ti.b0 + w * NBW + j) * 16 + (ln & 15);
+      if (row < ti.row0 + ti.rows) F::store(p, row, col, s);
+    }
     return;
   }
-  CrossSplit<typename F::Elem> cs{static_cast<typename F::Elem*>(p.partial),
-                                  p.counters + (size_t)mt * p.nt + nt, split, p.splits, p.M, p.N};
-  reduce_tile<MB, NB>(acc, lds, W, lane, wave, ti,
-                      [&](int row, int col, typename F::Elem v) { cs.publish(row, col, v); });
-  if (!workgroup_arrive_last(cs.counter, (uint32_t)p.splits, &s_flag)) return;
-  constexpr int kElems = MB * NB * 256;
-  for (int e = threadIdx.x; e < kElems; e += blockDim.x) {
-    const int ln = e & 63, idx = e >> 6;
-    const int i = idx & 3, blk = idx >> 2;
-    const int j = blk % NB, mb = blk / NB;
-    const int row = ti.row0 + mb * 16 + 4 * (ln >> 4) + i;
-    const int col = (ti.b0 + j) * 16 + (ln & 15);
-    if (row < ti.row0 + ti.rows) F::store(p, row, col, cs.gather(row, col));
+  // cross-workgroup split: publish the reduced tile in fragment order
+  const size_t tile_id = (size_t)mt * p.nt + nt;
+  const size_t ntiles = (size_t)p.mt * p.nt;
+  constexpr uint32_t kRegion = kTileElems * 4;
+  auto region = [&](int q) {
+    return make_rsrc(static_cast<char*>(p.partial) + ((size_t)q * ntiles + tile_id) * kRegion, kRegion);
+  };
+  {
+    const rsrc_t mine = region(split);
+    for (int e4 = tid; e4 < kTileElems / 4; e4 += KP * 256) {
+      f32x4 s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        E x = red[e4 * 4 + i];
+        for (int q = 1; q < KP; ++q) x += red[q * kTileElems + e4 * 4 + i];
+        s[i] = __builtin_bit_cast(float, x);
+      }
+      store16_coherent(s, mine, e4 * 16u);
+    }
+  }
+  if (!workgroup_arrive_last(p.counters + tile_id, (uint32_t)p.splits, flag)) return;
+  for (int e4 = tid; e4 < kTileElems / 4; e4 += KP * 256) {
+    E s[4] = {0, 0, 0, 0};
+    for (int q = 0; q < p.splits; ++q) {
+      const f32x4 x = load16_coherent(region(q), e4 * 16u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // copy the lane out first: this compiler's bit_cast of a vector-element
+        // lvalue reads element 0 whatever the index
+        const float xi = x[i];
+        s[i] += __builtin_bit_cast(E, xi);
+      }
+    }
+    const int ln = e4 & 63, fj = e4 >> 6;
+    const int j = fj % NBW, mb = (fj / NBW) % MB, w = fj / (NBW * MB);
+    const int col = (ti.b0 + w * NBW + j) * 16 + (ln & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ti.row0 + mb * 16 + 4 * (ln >> 4) + i;
+      if (row < ti.row0 + ti.rows) F::store(p, row, col, s[i]);
+    }
   }
 }
 
-// LDS bytes a launch needs: max(staged scales + extras, reduction buffer).
+// One kernel per workgroup size, so each gets its own register budget (a
+// template-dependent launch bound would not do here).
+#define QG_SKINNY_KERNEL(KPV, THREADS)                                          \
+  template <class F, int MB, int NBW>                                           \
+  __global__ void __launch_bounds__(THREADS) skinny_gemm_kp##KPV(GemmArgs p) { \
+    extern __shared__ __attribute__((aligned(16))) char lds[];                 \
+    __shared__ int flag;                                                        \
+    skinny_body<F, MB, NBW, KPV>(p, lds, &flag);                               \
+  }
+QG_SKINNY_KERNEL(1, 256)
+QG_SKINNY_KERNEL(2, 512)
+QG_SKINNY_KERNEL(4, 1024)
+#undef QG_SKINNY_KERNEL
+
+// LDS bytes of a launch (the largest split range bounds the staged chunks)
 template <class F>
 inline size_t skinny_lds_bytes(const Plan& pl, int G) {
-  const int n8 = (std::min(G, pl.gps) + 7) / 8 + 1;   // chunks touched by one split, worst case
-  const size_t stage = (size_t)pl.nb * n8 * F::kScaleChunk + F::extra_lds(pl);
-  const size_t red = (size_t)pl.wpt * pl.mb * pl.nb * 4 * 64 * 4;
-  return std::max(stage, red);
+  const int ng_max = std::min(G, pl.gps);
+  return (size_t)skinny_lds<F>(pl.mb, pl.nb, pl.wpt / 4, (ng_max + 7) / 8 + 1, ng_max).total;
 }
 
-template <class F, int MB, int NB>
-hipError_t launch_skinny(const Plan& pl, const GemmArgs& a, hipStream_t s) {
-  constexpr int D = F::kDepth;
-  const size_t lds = skinny_lds_bytes<F>(pl, a.G);
-  hipLaunchKernelGGL((skinny_gemm<F, MB, NB, D>), dim3((unsigned)pl.workgroups),
-                     dim3(kWave * pl.wpt), lds, s, a);
+template <class F, int MB, int NBW>
+hipError_t dispatch_kp(const Plan& pl, const GemmArgs& a, hipStream_t s) {
+  const size_t lds = skinny_lds_bytes<F>(pl, a.G);   // <= 160 KiB, the gfx950 per-workgroup LDS
+  const dim3 grid((unsigned)pl.workgroups);
+  switch (pl.wpt / 4) {
+    case 1: hipLaunchKernelGGL((skinny_gemm_kp1<F, MB, NBW>), grid, dim3(256), lds, s, a); break;
+    case 2: hipLaunchKernelGGL((skinny_gemm_kp2<F, MB, NBW>), grid, dim3(512), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((skinny_gemm_kp4<F, MB, NBW>), grid, dim3(1024), lds, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <class F>
 hipError_t dispatch_skinny(const Plan& pl, const GemmArgs& a, hipStream_t s) {
   switch (pl.mb * 10 + pl.nb) {
-    case 11: return launch_skinny<F, 1, 1>(pl, a, s);
-    case 12: return launch_skinny<F, 1, 2>(pl, a, s);
-    case 14: return launch_skinny<F, 1, 4>(pl, a, s);
-    case 21: return launch_skinny<F, 2, 1>(pl, a, s);
-    case 22: return launch_skinny<F, 2, 2>(pl, a, s);
-    case 24: return launch_skinny<F, 2, 4>(pl, a, s);
+    case 11: return dispatch_kp<F, 1, 1>(pl, a, s);
+    case 12: return dispatch_kp<F, 1, 2>(pl, a, s);
+    case 21: return dispatch_kp<F, 2, 1>(pl, a, s);
+    case 22: return dispatch_kp<F, 2, 2>(pl, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -7,7 +7,9 @@
 // order as W4A16); the upper two bits of 4-bit groups live in a separate high
 // plane of 32-byte pieces found through a per-chunk descriptor
 // (slot offset, 16-bit column mask) that the workgroup stages in LDS. A lane of
-// a 4-bit group loads its 8-byte quarter of the piece; the others load nothing.
+// a 4-bit group loads its 8-byte quarter of the piece; the others issue the same
+// load out of the resource's range and read zeros (a fixed number of memory
+// operations per group keeps the driver's counted waits exact).
 // Each lane then rebuilds 4-bit nibble words
 //   nib_2s   = (base_s & 0x33333333) | ((high_s << 2) & 0xCCCCCCCC)
 //   nib_2s+1 = ((base_s >> 2) & 0x33333333) | (high_s & 0xCCCCCCCC)
@@ -16,13 +18,14 @@
 #include "skinny.h"
 
 namespace qg {
-namespace {
+namespace fmt {
 
 struct PolicyW2W4 {
   using Acc = f32x4;
   using Elem = float;
   static constexpr int kScaleChunk = 256;
-  static constexpr int kDepth = 2;
+  static constexpr int kFrag = 4;
+  static constexpr int kAElem = 2;
 
   struct Consts {
     f16x2 lo4 = splat_h2(-1032.0f), hi4 = splat_h2(-72.0f);   // zero point 8
@@ -30,22 +33,19 @@ struct PolicyW2W4 {
     uint32_t magic = 0x64006400u;
   };
 
-  template <int MB, int NB>
+  template <int NBW>
   struct Stage {
-    u32x2 base[NB];
-    u32x2 high[NB];
-    uint32_t is4[NB];
-    u32x4 a[MB][4];
-    uint32_t s[NB];
+    static constexpr int kVmem = 2 * NBW;   // base plane + high plane loads
+    u32x2 base[NBW];
+    u32x2 high[NBW];
+    uint32_t is4[NBW];
+    uint32_t s[NBW];
   };
 
-  // descriptors of the workgroup's chunks, [NB][groups of the split], after the scales
-  static size_t extra_lds(const Plan& pl) { return (size_t)pl.nb * pl.gps * 8 + 16; }
-  static __device__ __forceinline__ size_t desc_offset(const TileInfo& ti, int NB) {
-    return (size_t)NB * ti.n8 * kScaleChunk;
-  }
-  __device__ static void stage_extra(const GemmArgs& p, char* lds, const TileInfo& ti, int NB) {
-    u32x2* dst = reinterpret_cast<u32x2*>(lds + desc_offset(ti, NB));
+  // descriptors of the workgroup's chunks, [NB][groups of the split]
+  __host__ __device__ static int extra_lds(int NB, int ng) { return NB * ng * 8; }
+  __device__ static void stage_extra(const GemmArgs& p, char* dst_, const TileInfo& ti, int NB) {
+    u32x2* dst = reinterpret_cast<u32x2*>(dst_);
     const u32x2* src = static_cast<const u32x2*>(p.aux);
     const int ng = ti.G1 - ti.G0;
     for (int t = threadIdx.x; t < NB * ng; t += blockDim.x) {
@@ -54,64 +54,58 @@ struct PolicyW2W4 {
     }
   }
 
-  template <int MB, int NB>
+  template <int NBW>
   struct View {
-    rsrc_t rb, rh, ra;
+    rsrc_t rb, rh;
     uint32_t bvoff, bblk;
-    uint32_t avoff[MB];
     const char* sl;
-    const u32x2* desc;   // [NB][ngw] in LDS
+    const u32x2* desc;   // this wave's first block in the [NB][ngw] LDS table
     uint32_t sblk, below, hoff;
     int gw0, c8, G0, ngw, c;
 
-    __device__ View(const GemmArgs& p, const char* lds, const TileInfo& ti, int gw0_, int ng, int lane)
+    __device__ View(const GemmArgs& p, const char* lds, const SkinnyLds& L, const TileInfo& ti, int bw,
+                    int gw0_, int nload, int lane)
         : gw0(gw0_), c8(ti.c8), G0(ti.G0), ngw(ti.G1 - ti.G0) {
       c = lane & 15;
-      const int h = lane >> 4;
       bblk = (uint32_t)p.G * 512u;
       bvoff = lane * 8u;
-      rb = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)ti.b0 * p.G + gw0) * 512,
-                     (NB - 1) * bblk + ng * 512u);
-      rh = make_rsrc(p.high, 0x7FFFFFF0u);   // offsets come from the blob's own descriptors
-      ra = make_rsrc(static_cast<const f16*>(p.A) + (size_t)ti.row0 * p.lda + (size_t)gw0 * kGroup,
-                     (uint32_t)(((size_t)(ti.rows - 1) * p.lda + (size_t)ng * kGroup) * 2));
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda * 2 + h * 16);
+      rb = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)bw * p.G + gw0) * 512,
+                     (NBW - 1) * bblk + nload * 512u);
+      // High-plane slots come from the blob's own descriptors; lanes of 2-bit
+      // groups address past the resource's size and read zeros.
+      rh = make_rsrc(p.high, 0x7FFFFFF0u);
       sblk = ti.n8 * kScaleChunk;
-      sl = lds + c * 16;
-      desc = reinterpret_cast<const u32x2*>(lds + desc_offset(ti, NB));
+      sl = lds + (bw - ti.b0) * sblk + c * 16;
+      desc = reinterpret_cast<const u32x2*>(lds + L.extra_off) + (bw - ti.b0) * ngw;
       below = (1u << c) - 1u;
-      hoff = h * 8u;
+      hoff = (lane >> 4) * 8u;
     }
-    __device__ __forceinline__ void load(Stage<MB, NB>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) st.base[j] = load8(rb, bvoff, j * bblk + rel * 512u);
+    }
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
       const int g = gw0 + rel;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        st.base[j] = load8(rb, bvoff, j * bblk + rel * 512u);
+      for (int j = 0; j < NBW; ++j) {
         const u32x2 d = desc[j * ngw + (g - G0)];
         const uint32_t is4 = (d[1] >> c) & 1u;
-        u32x2 hv = {0u, 0u};
-        if (is4) hv = load8(rh, (d[0] + __builtin_popcount(d[1] & below)) * 32u + hoff, 0);
-        st.high[j] = hv;
+        const uint32_t off = is4 ? (d[0] + __builtin_popcount(d[1] & below)) * 32u + hoff : 0x7FFFFFF8u;
+        st.high[j] = load8(rh, off, 0);
         st.is4[j] = is4;
       }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 256u + t * 64u);
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7) * 2;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) st.s[j] = *reinterpret_cast<const uint16_t*>(sl + j * sblk + off);
+      for (int j = 0; j < NBW; ++j) st.s[j] = *reinterpret_cast<const uint16_t*>(sl + j * sblk + off);
     }
   };
 
-  template <int MB, int NB>
-  __device__ __forceinline__ static void compute(const Stage<MB, NB>& cur, Acc (&acc)[MB][NB],
-                                                 bool valid, const Consts& k, int) {
-    f16x8 bf[NB][4];
+  template <int MB, int NBW>
+  __device__ __forceinline__ static void compute(const Stage<NBW>& cur, const char* aslot, Acc (&acc)[MB][NBW],
+                                                 bool valid, const Consts& k, int lane) {
+    f16x8 bf[NBW][4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int j = 0; j < NBW; ++j) {
       const f16x2 lo_off = cur.is4[j] ? k.lo4 : k.lo2;
       const f16x2 hi_off = cur.is4[j] ? k.hi4 : k.hi2;
 #pragma unroll
@@ -123,15 +117,20 @@ struct PolicyW2W4 {
         bf[j][2 * s + 1] = dequant_u4x8(n1, lo_off, hi_off, k.magic);
       }
     }
+    f16x8 a[MB][4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[mb][t] = *reinterpret_cast<const f16x8*>(aslot + (mb * 4 + t) * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
       const float sc = valid ? half_of(cur.s[j], 0) : 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(cur.a[mb][t]), bf[j][t], part, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bf[j][t], part, 0, 0, 0);
         acc[mb][j] += sc * part;
       }
     }
@@ -142,7 +141,9 @@ struct PolicyW2W4 {
   }
 };
 
-}  // namespace
+}  // namespace fmt
+
+using namespace fmt;
 
 size_t lds_bytes_w2w4(const Plan& pl, int G) { return skinny_lds_bytes<PolicyW2W4>(pl, G); }
 

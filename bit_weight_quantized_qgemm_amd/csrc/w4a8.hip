@@ -16,77 +16,75 @@
 #include "skinny.h"
 
 namespace qg {
-namespace {
+namespace fmt {
 
 struct PolicyW4A8 {
   using Acc = i32x4;
   using Elem = int32_t;
   static constexpr int kScaleChunk = 128;   // 16 columns x 8 groups x int8
-  static constexpr int kDepth = 2;
+  static constexpr int kFrag = 2;           // A fragments (16 rows x 64 k) per group
+  static constexpr int kAElem = 1;
 
   struct Consts {};
 
-  template <int MB, int NB>
+  template <int NBW>
   struct Stage {
-    u32x4 code[NB];
-    u32x4 a[MB][2];
-    int32_t s[NB];
+    static constexpr int kVmem = NBW;
+    u32x4 code[NBW];
+    int32_t s[NBW];
   };
 
-  static size_t extra_lds(const Plan&) { return 0; }
+  __host__ __device__ static int extra_lds(int, int) { return 0; }
   __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
 
-  template <int MB, int NB>
+  template <int NBW>
   struct View {
-    rsrc_t rc, ra;
+    rsrc_t rc;
     uint32_t cvoff, cblk;
-    uint32_t avoff[MB];
     const char* sl;
     uint32_t sblk;
     int gw0, c8;
 
-    __device__ View(const GemmArgs& p, const char* lds, const TileInfo& ti, int gw0_, int ng, int lane)
+    __device__ View(const GemmArgs& p, const char* lds, const SkinnyLds&, const TileInfo& ti, int bw,
+                    int gw0_, int nload, int lane)
         : gw0(gw0_), c8(ti.c8) {
-      const int c = lane & 15, h = lane >> 4;
       cblk = (uint32_t)p.G * 1024u;
       cvoff = lane * 16u;
-      rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)ti.b0 * p.G + gw0) * 1024,
-                     (NB - 1) * cblk + ng * 1024u);
-      ra = make_rsrc(static_cast<const int8_t*>(p.A) + (size_t)ti.row0 * p.lda + (size_t)gw0 * kGroup,
-                     (uint32_t)((size_t)(ti.rows - 1) * p.lda + (size_t)ng * kGroup));
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        avoff[mb] = (uint32_t)((size_t)min(mb * 16 + c, ti.rows - 1) * p.lda + h * 16);
+      rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)bw * p.G + gw0) * 1024,
+                     (NBW - 1) * cblk + nload * 1024u);
       sblk = ti.n8 * kScaleChunk;
-      sl = lds + c * 8;
+      sl = lds + (bw - ti.b0) * sblk + (lane & 15) * 8;
     }
-    __device__ __forceinline__ void load(Stage<MB, NB>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) st.code[j] = load16(rc, cvoff, j * cblk + rel * 1024u);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) st.a[mb][t] = load16(ra, avoff[mb], rel * 128u + t * 64u);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * cblk + rel * 1024u);
+    }
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
       const int g = gw0 + rel;
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) st.s[j] = *reinterpret_cast<const int8_t*>(sl + j * sblk + off);
+      for (int j = 0; j < NBW; ++j) st.s[j] = *reinterpret_cast<const int8_t*>(sl + j * sblk + off);
     }
   };
 
-  template <int MB, int NB>
-  __device__ __forceinline__ static void compute(const Stage<MB, NB>& cur, Acc (&acc)[MB][NB],
-                                                 bool valid, const Consts&, int) {
+  template <int MB, int NBW>
+  __device__ __forceinline__ static void compute(const Stage<NBW>& cur, const char* aslot, Acc (&acc)[MB][NBW],
+                                                 bool valid, const Consts&, int lane) {
     const i32x4 ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
     const i32x4 zero = {0, 0, 0, 0};
+    i32x4 a[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) a[mb][u] = *reinterpret_cast<const i32x4*>(aslot + (mb * 2 + u) * 1024 + lane * 16);
     i32x4 rsum[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      rsum[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i4(cur.a[mb][0]), ones, zero, 0, 0, 0);
-      rsum[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i4(cur.a[mb][1]), ones, rsum[mb], 0, 0, 0);
+      rsum[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][0], ones, zero, 0, 0, 0);
+      rsum[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][1], ones, rsum[mb], 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
+    for (int j = 0; j < NBW; ++j) {
       const u32x4 w = cur.code[j];
       const i32x4 b0 = {(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
                         (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu)};
@@ -95,8 +93,8 @@ struct PolicyW4A8 {
       const int sg = valid ? cur.s[j] : 0;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        i32x4 part = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i4(cur.a[mb][0]), b0, zero, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i4(cur.a[mb][1]), b1, part, 0, 0, 0);
+        i32x4 part = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][0], b0, zero, 0, 0, 0);
+        part = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][1], b1, part, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int corr = part[r] - 8 * rsum[mb][r];   // sum_{k in g} A * q, |.| < 2^18
@@ -114,7 +112,9 @@ struct PolicyW4A8 {
   }
 };
 
-}  // namespace
+}  // namespace fmt
+
+using namespace fmt;
 
 size_t lds_bytes_w4a8(const Plan& pl, int G) { return skinny_lds_bytes<PolicyW4A8>(pl, G); }
 

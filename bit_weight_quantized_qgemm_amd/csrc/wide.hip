@@ -29,15 +29,6 @@ constexpr int kWideNBW = 4;                            // 16-column blocks per w
 static_assert(kWideCols == 4 * 4 * 16, "tile width = waves x blocks x 16");
 constexpr int kASlots = 3;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// vmcnt(n) with the other counters left unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 template <int MBW>
 struct WideStage {
   u32x4 code[kWideNBW];
@@ -135,14 +126,9 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
 #pragma unroll
     for (int r = 0; r < kASlots; ++r) {
       const int i = base + r;
-      // A raw s_barrier, not __syncthreads(): the latter is a release fence,
-      // which would also wait for the prefetches in flight (they write LDS).
-      // The counted wait is the only completion this barrier must publish; the
-      // compiler fences keep LDS accesses on their side of it.
+      // raw_barrier(): publishes only the counted completion above (see skinny.h)
       wait_vmcnt<kAPerWave + 4 * kWideNBW>();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      raw_barrier();
       issue_a(min(i + 2, ng - 1), (r + 2) % kASlots);
       issue_b(st[(r + 2) % kASlots], min(i + 2, ng - 1));
       __builtin_amdgcn_sched_barrier(0);
@@ -257,8 +243,14 @@ namespace {
 hipError_t launch_wide_k(const void* fn, void (*kernel)(GemmArgs), int mbw, const Plan& pl,
                          const GemmArgs& a, hipStream_t s) {
   const size_t lds = (size_t)kASlots * mbw * 4 * 1024;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+  // the LDS size is fixed per kernel: opt in to it (above 64 KiB) once
+  static bool big_lds[2] = {false, false};
+  bool& done = big_lds[mbw == 8];
+  if (!done) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    done = true;
+  }
   hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * kWideWaves), lds, s, a);
   return hipGetLastError();
 }

@@ -161,25 +161,24 @@ int qgemm_w2w4_mixed(const void* A, int64_t lda, const void* packed, void* C, in
 /*
  * Work decomposition used for a call of this shape (for tests and tuning).
  * Fills out10[0..9] = {kernel id (1 streaming, 2 wide), 16-row blocks per tile
- * (per wave for kernel 2), 16-column blocks per tile (per wave for kernel 2),
- * waves per tile (workgroup size / 64), k-splits across workgroups,
- * groups per k-split, m-tiles, n-tiles, workgroups, waves}. Host-only; no HIP
- * call.
+ * (per wave for kernel 2), 16-column blocks per wave, waves per workgroup,
+ * k-splits across workgroups, groups per k-split, m-tiles, n-tiles,
+ * workgroups, waves}. Host-only; no HIP call.
  */
 int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 
 /*
  * Override the automatic plan for later calls of this process: kernel (1 =
  * streaming kernel for every format, 2 = wide W4A16 kernel for N a multiple of
- * 256; other cases keep kernel 1), 16-column blocks per tile of kernel 1
- * (1, 2 or 4), waves per tile of kernel 1 (1..8) and k-splits across
- * workgroups (1..4096); 0 keeps the automatic choice for that field. Values the
- * shape cannot use are clamped (no more waves than groups, LDS limits). For
- * tests of the split-K reductions and for tuning sweeps; affects
+ * 256; other cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or
+ * 2; 4 is taken as 2), waves per workgroup of kernel 1 (4, 8 or 16) and
+ * k-splits across workgroups (1..4096); 0 keeps the automatic choice for that
+ * field. Values a shape cannot use are clamped (no more K-parts than groups).
+ * For tests of the split-K reductions and for tuning sweeps; affects
  * qgemm_workspace_bytes and qgemm_plan too. Not thread-safe against concurrent
  * GEMM calls.
  */
-int qgemm_set_plan_override(int kernel, int nb_per_tile, int waves_per_tile, int k_splits);
+int qgemm_set_plan_override(int kernel, int nb_per_wave, int waves_per_workgroup, int k_splits);
 
 #ifdef __cplusplus
 }

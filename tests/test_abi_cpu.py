@@ -138,22 +138,22 @@ def _check_plan(p, M, K, N):
             cover[G0:G1] += 1
         assert np.all(cover == 1)
         return
-    assert p["nb"] in (1, 2, 4) and p["mb"] in (1, 2)
-    assert p["nt"] * p["nb"] * 16 == N
+    assert p["kernel"] == 1 and p["nb"] in (1, 2) and p["mb"] in (1, 2)
+    assert p["nt"] * p["nb"] * 64 == N
     assert p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
-    assert 1 <= p["wpt"] <= 8 and (p["wpt"] == 1 or p["wpt"] * p["mb"] * p["nb"] <= 64)
-    assert p["wpt"] <= p["gps"]
+    assert p["wpt"] in (4, 8, 16) and p["wpt"] // 4 <= p["gps"]
     assert p["workgroups"] == p["nt"] * p["mt"] * p["splits"]
     assert p["waves"] == p["workgroups"] * p["wpt"]
-    # every group of K is streamed by exactly one wave of each tile
+    # every group of K is streamed by exactly one K-part of each tile
+    kp = p["wpt"] // 4
     cover = np.zeros(G, dtype=int)
     for s in range(p["splits"]):
         G0, G1 = s * p["gps"], min(G, (s + 1) * p["gps"])
         assert G1 > G0
-        gpw = -(-(G1 - G0) // p["wpt"])
-        for w in range(p["wpt"]):
-            g0 = G0 + w * gpw
-            g1 = min(G1, g0 + gpw)
+        iters = -(-(G1 - G0) // kp)
+        for k in range(kp):
+            g0 = G0 + k * iters
+            g1 = min(G1, g0 + iters)
             if g1 > g0:
                 cover[g0:g1] += 1
     assert np.all(cover == 1)
@@ -161,7 +161,7 @@ def _check_plan(p, M, K, N):
     if p["splits"] == 1:
         assert ws == 0
     else:
-        assert ws >= p["splits"] * M * N * 4 + 65536
+        assert ws >= p["splits"] * p["mt"] * p["mb"] * 16 * N * 4 + 65536
         assert p["mt"] * p["nt"] <= 16384
 
 
@@ -171,8 +171,8 @@ def test_plan_covers_every_unit_once(K, N, M):
     _check_plan(qg.plan(qg.FMT_W4A16, M, K, N), M, K, N)
 
 
-@pytest.mark.parametrize("force", [(1, 1, 1), (4, 8, 1), (2, 3, 1), (4, 1, 4), (1, 2, 3),
-                                   (4, 8, 2), (2, 5, 7), (1, 8, 64)])
+@pytest.mark.parametrize("force", [(1, 4, 1), (2, 8, 1), (2, 16, 1), (1, 16, 4), (1, 4, 3),
+                                   (2, 8, 2), (2, 4, 7), (1, 8, 64)])
 @pytest.mark.parametrize("M,K,N", [(16, 4096, 1024), (20, 1280, 192), (1, 28672, 8192)])
 def test_forced_plans_cover_every_unit_once(force, M, K, N):
     try:
@@ -188,15 +188,15 @@ def test_plan_override(L):
         assert L.qgemm_set_plan_override(0, 1, 9, 0) == ERR_RANGE
         assert L.qgemm_set_plan_override(0, 1, 0, -1) == ERR_RANGE
         assert L.qgemm_set_plan_override(3, 0, 0, 0) == ERR_RANGE
-        qg.set_plan_override(2, 4, 4)
+        qg.set_plan_override(2, 8, 4)
         p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
-        assert (p["nb"], p["wpt"], p["splits"], p["gps"]) == (2, 4, 4, 8)
-        qg.set_plan_override(1, 8, 64)   # more splits than groups: one group per split
+        assert (p["nb"], p["wpt"], p["splits"], p["gps"]) == (2, 8, 4, 8)
+        qg.set_plan_override(1, 16, 64)   # more splits than groups: one group per split
         p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
-        assert p["splits"] == 32 and p["gps"] == 1 and p["wpt"] == 1
+        assert p["splits"] == 32 and p["gps"] == 1 and p["wpt"] == 4
     finally:
-        qg.set_plan_override(0, 0, 0)
-    assert qg.plan(qg.FMT_W4A16, 16, 4096, 4096)["nb"] in (1, 2, 4)
+        qg.set_plan_override()
+    assert qg.plan(qg.FMT_W4A16, 16, 4096, 4096)["nb"] in (1, 2)
     # large batches use the wide kernel when N is a multiple of 256
     assert qg.plan(qg.FMT_W4A16, 128, 8192, 28672)["kernel"] == 2
     assert qg.plan(qg.FMT_W4A16, 128, 8192, 28736)["kernel"] == 1

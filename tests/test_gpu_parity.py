@@ -94,8 +94,8 @@ def _one_hot(M, K, rng):
     return A, ks
 
 
-@pytest.mark.parametrize("M,K,N,force", [(16, 1024, 1024, None), (5, 4096, 256, (1, 3, 2)),
-                                         (32, 1152, 320, (2, 8, 1)), (20, 8192, 128, (4, 2, 5))])
+@pytest.mark.parametrize("M,K,N,force", [(16, 1024, 1024, None), (5, 4096, 256, (1, 8, 2)),
+                                         (32, 1152, 384, (2, 16, 1)), (20, 8192, 128, (2, 4, 5))])
 def test_w4a16_one_hot_bit_exact(M, K, N, force):
     _say("w4a16 one-hot", M, K, N, force)
     rng = np.random.default_rng(M * 7 + K)
@@ -180,8 +180,8 @@ def test_w4a16_ragged_m(M):
     _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, M)
 
 
-@pytest.mark.parametrize("force", [(1, 1, 1), (4, 8, 1), (2, 3, 1), (4, 1, 4), (1, 2, 3),
-                                   (4, 8, 2), (2, 5, 7), (1, 8, 32), (0, 0, 0)])
+@pytest.mark.parametrize("force", [(1, 4, 1), (2, 8, 1), (2, 16, 1), (1, 16, 4), (1, 4, 3),
+                                   (2, 8, 2), (2, 4, 7), (1, 8, 32), (0, 0, 0)])
 @pytest.mark.parametrize("M", [16, 20])
 def test_w4a16_forced_splits(force, M):
     K, N = 4096, 1024
@@ -253,8 +253,8 @@ def test_w4a8_config_layer(M):
     _ok(C, C_ref, K, ("w4a8", M))
 
 
-@pytest.mark.parametrize("M,force", [(1, None), (3, (1, 3, 2)), (17, (2, 8, 1)), (40, (4, 2, 4)),
-                                     (33, None), (9, (1, 1, 16))])
+@pytest.mark.parametrize("M,force", [(1, None), (3, (1, 8, 2)), (17, (2, 16, 1)), (40, (2, 4, 4)),
+                                     (33, None), (9, (1, 4, 16))])
 def test_w4a8_ragged_and_splits(M, force):
     K, N = 2048, 320
     _say("w4a8 ragged", M, force)
@@ -302,9 +302,9 @@ def test_w2w4_config_layer(M):
     _ok(C, ref.gemm_w2w4(p["A"], p["codes"], p["bitmap"], p["scales"]), K, ("w2w4", M))
 
 
-@pytest.mark.parametrize("M,frac,force", [(3, 0.0, None), (17, 1.0, None), (20, 0.3, (1, 3, 2)),
-                                          (9, 0.5, (4, 2, 4)), (33, 0.1, (2, 8, 1)),
-                                          (5, 0.2, (1, 1, 16))])
+@pytest.mark.parametrize("M,frac,force", [(3, 0.0, None), (17, 1.0, None), (20, 0.3, (1, 8, 2)),
+                                          (9, 0.5, (2, 4, 4)), (33, 0.1, (2, 16, 1)),
+                                          (5, 0.2, (1, 4, 16))])
 def test_w2w4_ragged_and_extremes(M, frac, force):
     K, N = 2048, 320
     _say("w2w4 ragged", M, frac, force)
@@ -339,8 +339,9 @@ def test_workspace_shared_across_plans():
     # splits: each call must find the counter region zero again
     _say("workspace shared across plans")
     ws = qg.Workspace()
-    seq = [(5, 4096, 256, (1, 3, 4)), (20, 8192, 128, (4, 2, 8)), (1, 4096, 4096, None),
-           (16, 2048, 1024, (1, 1, 16)), (3, 4096, 4096, (2, 4, 2)), (7, 1024, 64, None)]
+    seq = [(5, 4096, 256, (1, 8, 4)), (20, 8192, 128, (2, 4, 8)), (1, 4096, 4096, None),
+           (16, 2048, 1024, (1, 4, 16)), (3, 4096, 4096, (2, 16, 2)), (7, 1024, 64, None),
+           (40, 2048, 512, (0, 0, 3, 2)), (9, 1024, 256, (0, 0, 2, 1))]
     for M, K, N, force in seq:
         qg.set_plan_override(*(force or (0, 0, 0)))
         p = gen.w4a16_problem(M, K, N, seed=M + N)
