@@ -14,10 +14,14 @@ The weight blob rotates over several copies (more bytes than the 256 MB
 Infinity Cache) so every launch streams its weights from HBM.
 
 Prints one JSON line. ``value`` is the aggregate TFLOP/s of the timed steps;
-``per_m`` gives each launch's own time, TFLOP/s and roofline fractions
-(kernel-only durations from HIP events around bursts of back-to-back launches);
-``roofline`` describes the launch that takes the largest share of the step;
-``cpu_baseline`` times the NumPy oracle on a bounded sample of the same work.
+``per_m`` gives each launch's mean duration over a burst of back-to-back
+launches (HIP events around the burst), its TFLOP/s and roofline fractions;
+``roofline`` describes the kernel with the largest share of the timed steps
+(algorithmic work of its launches / their time between the events that bracket
+each kernel's group of launches inside the timed steps), with
+``traffic`` = HBM bytes per launch from the committed counter summary when it
+was taken on the current kernel sources; ``cpu_baseline`` times the NumPy oracle
+on a bounded sample of the same work.
 """
 
 from __future__ import annotations
@@ -52,6 +56,45 @@ def alg_flops(M, K, N):
     return 2 * M * K * N
 
 
+def kernel_label(pl: dict) -> str:
+    """Name of the HIP kernel a plan launches (as rocprofv3 lists it, shortened)."""
+    if pl["kernel"] == 2:
+        return f"w4a16_wide_m{16 * pl['mb']}"
+    return f"skinny_gemm_kp{pl['wpt'] // 4}<PolicyW4A16,{pl['mb']},{pl['nb']}>"
+
+
+def source_sha() -> str:
+    """Hash of the kernel and planner sources: HBM byte counters taken for an
+    older version of them are not reported."""
+    import hashlib
+    d = os.path.join(ROOT, "bit_weight_quantized_qgemm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a16_sweep_70b_layer_hbm_traffic.txt")
+
+
+def measured_traffic(label: str):
+    """HBM bytes per launch of `label` from the committed counter summary, or
+    None when it is absent or was taken on other kernel sources."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    sha = next((l.split("=", 1)[1].strip() for l in lines if l.startswith("source_sha=")), None)
+    if sha != source_sha():
+        return None
+    for l in lines:
+        if l.startswith("kernel=") and l.split()[0] == "kernel=" + label:
+            kv = dict(x.split("=", 1) for x in l.split() if "=" in x)
+            return float(kv["traffic_bytes_per_launch"])
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +105,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--shapes", default="all", choices=["all", "up", "down"])
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (the known-size "
+                         "reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -153,30 +199,54 @@ def main():
         for cs in cases:
             launch(cs, i)
 
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed steps. Launches of one kernel run back to back (the step's
+    # order groups them), and one event closes each group, so the dominant
+    # kernel's duration comes from the timed steps themselves at a cost of a
+    # few events per step.
+    groups = {}
+    for j, cs in enumerate(cases):
+        groups.setdefault(kernel_label(cs["plan"]), []).append(j)
+    glist = list(groups.items())
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    bounds = [[ev() for _ in glist] for _ in range(args.steps)]
+    e0 = ev()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        step(i)
-    e1.record(stream)
+        for gi, (_, idx) in enumerate(glist):
+            for j in idx:
+                launch(cases[j], i)
+            bounds[i][gi].record(stream)
+    e1 = bounds[-1][-1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     step_ms = e0.elapsed_time(e1) / args.steps
     step_flops = sum(alg_flops(c["M"], c["K"], c["N"]) for c in cases)
     value = step_flops / (step_ms * 1e-3) / 1e12
+    kernel_us = {}
+    for i in range(args.steps):
+        for gi, (label, idx) in enumerate(glist):
+            start = bounds[i][gi - 1] if gi else (bounds[i - 1][-1] if i else e0)
+            kernel_us[label] = kernel_us.get(label, 0.0) + start.elapsed_time(bounds[i][gi]) * 1e3
 
-    # ---- per-launch kernel durations (bursts of back-to-back launches)
+    # ---- per-launch table: bursts of back-to-back launches of each case
     per_m = []
     for cs in cases:
         for i in range(3):
             launch(cs, i)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = ev(), ev()
         a.record(stream)
         for i in range(args.burst):
             launch(cs, i)
@@ -191,21 +261,37 @@ def main():
         per_m.append({"shape": f"{K}x{N}", "M": M, "us": round(us, 2), "tflops": round(tf, 2),
                       "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "mfma_frac": round(tf / FP16_PEAK_TFLOPS, 4),
-                      "roofline_frac": round(roof_us / us, 4),
+                      "roofline_frac": round(roof_us / us, 4), "kernel": kernel_label(cs["plan"]),
                       "plan": {k: cs["plan"][k] for k in ("mb", "nb", "wpt", "splits", "mt", "waves")}})
 
-    dom = max(per_m, key=lambda r: r["us"])
-    dM = dom["M"]
-    dK, dN = (int(x) for x in dom["shape"].split("x"))
-    mfma_bound = alg_flops(dM, dK, dN) / (FP16_PEAK_TFLOPS * 1e12) > alg_bytes(dM, dK, dN) / (HBM_PEAK_GBS * 1e9)
+    # ---- roofline of the dominant kernel: the one with the largest share of
+    # the timed steps; algorithmic work of its launches / their event time
+    by_kernel = {}
+    for cs in cases:
+        label = kernel_label(cs["plan"])
+        k = by_kernel.setdefault(label, {"us": kernel_us[label], "n": 0, "bytes": 0, "flops": 0})
+        M, K, N = cs["M"], cs["K"], cs["N"]
+        k["n"] += args.steps
+        k["bytes"] += alg_bytes(M, K, N) * args.steps
+        k["flops"] += alg_flops(M, K, N) * args.steps
+    dom_label, dom = max(by_kernel.items(), key=lambda kv: kv[1]["us"])
+    mfma_bound = dom["flops"] / (FP16_PEAK_TFLOPS * 1e12) > dom["bytes"] / (HBM_PEAK_GBS * 1e9)
+    traffic = measured_traffic(dom_label)
     if mfma_bound:
-        roof = {"bound": "mfma", "achieved": dom["tflops"], "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom["tflops"] / FP16_PEAK_TFLOPS, 4), "traffic": None}
+        ach = dom["flops"] / (dom["us"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP16_PEAK_TFLOPS, 4)}
     else:
-        roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["kernel"] = f"w4a16 M={dM} {dom['shape']}"
-    roof["us_per_launch"] = dom["us"]
+        ach = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None if traffic is None else round(traffic)
+    roof.update({"kernel": dom_label, "launches": dom["n"], "us_per_launch": round(dom["us"] / dom["n"], 2),
+                 "alg_bytes_per_launch": round(dom["bytes"] / dom["n"]),
+                 "alg_flops_per_launch": round(dom["flops"] / dom["n"]),
+                 "share_of_step": round(dom["us"] / (step_ms * 1e3 * args.steps), 3),
+                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                 "source_sha": source_sha()})
 
     out = {
         "metric": METRIC,
