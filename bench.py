@@ -64,14 +64,18 @@ def kernel_label(pl: dict) -> str:
 
 
 def source_sha() -> str:
-    """Hash of the kernel and planner sources: HBM byte counters taken for an
-    older version of them are not reported."""
+    """Hash of the kernel and planner sources with comments and blank lines
+    removed: HBM byte counters taken on other code are not reported."""
     import hashlib
+    import re
     d = os.path.join(ROOT, "bit_weight_quantized_qgemm_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(d, f)) as fh:
+            txt = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        txt = re.sub(r"//[^\n]*", "", txt)
+        code = "\n".join(l.rstrip() for l in txt.splitlines() if l.strip())
+        h.update(f.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
 
 

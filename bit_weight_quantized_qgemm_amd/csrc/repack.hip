@@ -1,7 +1,7 @@
-// Offline weight repacking into the order the GEMM kernels stream (the "matrix
-// preprocessing that optimizes data layout" of the arbitrary-precision Tensor Core
-// page; the 2-bit page's "memory alignment consideration" for mixed 2/4-bit
-// groups).
+// Offline weight repacking into the order the GEMM kernels stream (the
+// arbitrary-precision Tensor Core page's abstract preprocesses the matrices into
+// a layout suited to the later computation; the 2-bit page's abstract stores the
+// mixed 2/4-bit groups with aligned memory access in mind).
 //
 // Blob layout (G = K/128 groups, NB = N/16 column blocks, G8 = ceil(G/8); lane l
 // of a 64-wide wave has column c = l % 16 and k-quarter h = l / 16; regions start

@@ -1,8 +1,8 @@
 // Shared driver of the streaming quantized-weight GEMM kernels (gfx950), used for
 // small and medium batches (the memory-bound regime of the MARLIN abstract).
 //
-// Work decomposition (the "task scheduling" of the MARLIN abstract, re-derived
-// for CDNA4):
+// Work decomposition (the MARLIN abstract's scheduling of the work across the
+// GPU, re-derived for CDNA4):
 //   * a workgroup owns one output tile of 16*MB rows x 64*NBW columns over the K
 //     range of its k-split (usually all of K);
 //   * its 4*KP waves form KP K-parts of 4 column waves: column wave n streams

@@ -1,6 +1,6 @@
 // W4A16 GEMM for larger batches (M > 32) on gfx950: the compute-bound end of the
-// MARLIN abstract's regime ("batchsizes up to 64-128 with gradually decreasing,
-// but still significant, acceleration").
+// batch range of the MARLIN abstract, where its speedup shrinks with batch size
+// but persists up to 64-128.
 //
 // Each workgroup owns a tile of 16*MBW rows (64 or 128) x 256 columns; its four
 // waves each own 64 columns and every row of the tile, so every weight is

@@ -3,7 +3,7 @@
  *
  * The library computes C[M,N] = A[M,K] * dequant(Wq)[K,N] for small-to-medium
  * batches (M = 1..128 is the design range; larger M is accepted), the
- * "mixed-precision auto-regressive linear" layer of the MARLIN paper (abstract:
+ * mixed-precision auto-regressive linear layer of the MARLIN paper (abstract:
  * weights compressed to about 4 bits per element, batched decode with 1..128
  * parallel clients, memory-bound up to batch 16..32). Three weight formats:
  *
@@ -101,9 +101,9 @@ int qgemm_packed_bytes(int fmt, int64_t K, int64_t N, const uint32_t* bitmap_hos
 int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* bytes);
 
 /*
- * Offline weight preprocessing (the "matrix preprocessing that optimizes data
- * layout for subsequent computations" of the arbitrary-precision Tensor Core
- * page's abstract): rewrites canonical codes and scales into the blob the GEMM
+ * Offline weight preprocessing (the arbitrary-precision Tensor Core page's
+ * abstract reorganises the matrices ahead of time into a layout suited to the
+ * later computation): rewrites canonical codes and scales into the blob the GEMM
  * kernels stream, laid out in gfx950 MFMA operand order (one 1 KB, fully
  * coalesced wave load per 16 columns x 128 k for the 4-bit formats).
  *

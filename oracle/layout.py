@@ -1,9 +1,9 @@
 """Independent implementation of the repacked weight blob layout (CPU, NumPy).
 
 The GPU repack reorders codes and scales into the order in which the GEMM
-kernels consume them (the "matrix preprocessing that optimizes data layout for
-subsequent computations" of the arbitrary-precision Tensor Core page, and the
-"memory alignment consideration" of the 2-bit page). This module builds the same
+kernels consume them (the arbitrary-precision Tensor Core page's abstract
+preprocesses matrices into a layout suited to the later computation; the 2-bit
+page's abstract stores mixed groups with aligned memory access in mind). This module builds the same
 bytes from the canonical arrays with NumPy index arithmetic, written from the
 layout specification alone, so the GPU blob can be compared byte for byte.
 
