@@ -26,6 +26,7 @@ std::atomic<int> g_force_kernel{0};
 constexpr int64_t kMaxM = 65535;
 constexpr int64_t kMaxKN = int64_t(1) << 20;
 constexpr int64_t kMaxKW4A8 = 16384;
+constexpr int64_t kMaxWeights = int64_t(1) << 32;   // K*N: at most 2 GiB of 4-bit codes
 
 int hip_fail(hipError_t e, const char* what) {
   g_last_error = std::string(what) + ": " + hipGetErrorString(e);
@@ -46,6 +47,7 @@ int check_kn(int fmt, int64_t K, int64_t N) {
   if (K <= 0 || K % qg::kGroup != 0 || K > kMaxKN) return QGEMM_ERR_SHAPE;
   if (N <= 0 || N % 64 != 0 || N > kMaxKN) return QGEMM_ERR_SHAPE;
   if (fmt == QGEMM_FMT_W4A8 && K > kMaxKW4A8) return QGEMM_ERR_SHAPE;
+  if (K * N > kMaxWeights) return QGEMM_ERR_SHAPE;   // 32-bit buffer offsets into the blob
   return QGEMM_OK;
 }
 
@@ -161,6 +163,17 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
     return make_wide_plan(M, K, N);
   // Streaming kernel: 4*KP-wave workgroups own 16*mb x 64*nb tiles; the 4
   // column waves of each of the KP K-parts share activations through LDS.
+  //
+  // With group-major weight chunks, every K position that is streamed at the
+  // same time (one per K-part and k-split) is a contiguous front sweeping
+  // through the blob. Measured on MI355X, the fewer such fronts the better,
+  // provided that (a) at least ~3/4 of the CUs get a workgroup, (b) enough
+  // weight loads are in flight (each wave keeps two groups of nb chunks in
+  // flight; about 8 MB in total covers HBM latency at full bandwidth), and (c)
+  // every workgroup is resident at once. Among plans meeting these, the search
+  // prefers nb = 2 when M > 4 (half the activation traffic per weight) and
+  // nb = 1 otherwise, then the lowest fronts + k-splits (a k-split also costs
+  // partial-sum traffic and a second reduction), then fewer k-splits.
   Plan pl;
   const int G = (int)(K / kGroup);
   pl.kernel = 1;
@@ -169,25 +182,85 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
   const int force_nb = g_force_nb.load();
   const int force_wpt = g_force_wpt.load();
   const int force_splits = g_force_splits.load();
-  int nb = force_nb ? std::min(force_nb, 2) : 1;
-  if (N % (64 * nb) != 0) nb = 1;
-  int kp = force_wpt ? std::max(1, force_wpt / 4) : (G >= 16 ? 4 : G >= 8 ? 2 : 1);
-  if (kp == 3) kp = 2;
-  const int64_t tiles = (int64_t)pl.mt * (N / (64 * nb));
-  int splits = 1;
-  if (force_splits) {
-    splits = force_splits;
-  } else if (tiles < kCUs) {
-    // too few tiles for the chip: split K across workgroups as well
-    splits = (int)std::min<int64_t>((2 * kCUs + tiles - 1) / tiles, std::max(1, G / (2 * kp)));
+  const double chunk = fmt == QGEMM_FMT_W2W4 ? 560.0 : 1024.0;   // streamed bytes per 16 x 128 chunk
+  const double blob = (double)G * (double)(N / 16) * chunk;
+  const double inflight_target = std::min(8.0 * 1048576.0, blob / 2);
+  const int pref_nb = M > 4 ? 2 : 1;
+  struct Score {
+    int violations, nb_pen, cost, splits;
+    int64_t neg_waves;
+    bool operator<(const Score& o) const {
+      if (violations != o.violations) return violations < o.violations;
+      if (nb_pen != o.nb_pen) return nb_pen < o.nb_pen;
+      if (cost != o.cost) return cost < o.cost;
+      if (splits != o.splits) return splits < o.splits;
+      return neg_waves < o.neg_waves;
+    }
+  };
+  bool have = false;
+  Score best{};
+  int best_nb = 1, best_kp = 1, best_s = 1;
+  for (int nb = 1; nb <= 2; ++nb) {
+    if (force_nb && nb != std::min(force_nb, 2)) continue;
+    if (N % (64 * nb) != 0) continue;
+    const int64_t tiles = (int64_t)pl.mt * (N / (64 * nb));
+    for (int kp = 1; kp <= 4; kp *= 2) {
+      if (force_wpt && kp != std::max(1, force_wpt / 4)) continue;
+      if (kp > G) continue;
+      // the mixed format's 2 x 2 tile with four K-parts would spill registers
+      if (fmt == QGEMM_FMT_W2W4 && pl.mb == 2 && nb == 2 && kp == 4 && !force_wpt) continue;
+      const int smax = tiles > kMaxCounters ? 1 : std::min(G, 64);
+      for (int s0 = 1; s0 <= smax; ++s0) {
+        if (force_splits && s0 != std::min(force_splits, G)) continue;
+        const int gps = (G + s0 - 1) / s0;
+        const int s = (G + gps - 1) / gps;
+        if (s != s0) continue;                       // the same plan as a smaller s0
+        if (kp > gps) continue;                      // every K-part gets a group
+        Plan c = pl;
+        c.nb = nb;
+        c.wpt = 4 * kp;
+        c.gps = gps;
+        const size_t lds = fmt == QGEMM_FMT_W4A16 ? lds_bytes_w4a16(c, G)
+                           : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G) : lds_bytes_w2w4(c, G);
+        if (lds > 160 * 1024) continue;
+        const int64_t wgs = tiles * s;
+        const int64_t waves = wgs * 4 * kp;
+        // resident workgroups per CU: LDS, and registers (two-block tiles take
+        // about 96-128 VGPRs, one-block tiles at most 76)
+        const int per_simd = nb == 2 ? 4 : 8;
+        const int64_t cap = std::max<int64_t>(
+            1, std::min<int64_t>((160 * 1024) / std::max<size_t>(lds, 1), (4 * per_simd) / (4 * kp)));
+        Score sc;
+        sc.violations = (wgs * 4 < 3 * kCUs) + (waves * nb * 2.0 * chunk < inflight_target) +
+                        (wgs > cap * kCUs);
+        sc.cost = s * kp + s;   // fronts + k-splits
+        sc.splits = s;
+        sc.nb_pen = nb == pref_nb ? 0 : 1;
+        sc.neg_waves = -waves;
+        if (!have || sc < best) {
+          have = true;
+          best = sc;
+          best_nb = nb;
+          best_kp = kp;
+          best_s = s;
+        }
+      }
+    }
   }
-  splits = std::max(1, std::min(splits, G));
-  if (tiles > kMaxCounters) splits = 1;
-  int gps = (G + splits - 1) / splits;
+  if (!have) {   // a forced shape outside the search space: fall back to its literal values
+    best_nb = (force_nb && N % (64 * std::min(force_nb, 2)) == 0) ? std::min(force_nb, 2) : 1;
+    best_s = std::max(1, std::min(force_splits ? force_splits : 1, G));
+    best_kp = force_wpt ? std::max(1, std::min(4, force_wpt / 4)) : 1;
+    if (best_kp == 3) best_kp = 2;
+  }
+  const int64_t tiles = (int64_t)pl.mt * (N / (64 * best_nb));
+  int splits = tiles > kMaxCounters ? 1 : best_s;
+  const int gps = (G + splits - 1) / splits;
   splits = (G + gps - 1) / gps;
+  int kp = best_kp;
   while (kp > 1 && kp > gps) kp /= 2;       // every K-part gets at least one group
-  pl.nb = nb;
-  pl.nt = (int)(N / (64 * nb));
+  pl.nb = best_nb;
+  pl.nt = (int)(N / (64 * best_nb));
   pl.wpt = 4 * kp;
   pl.splits = splits;
   pl.gps = gps;
@@ -320,12 +393,12 @@ int qgemm_repack(int fmt, int64_t K, int64_t N, const void* codes, const void* g
     std::vector<uint32_t> desc((size_t)L.NB * L.G * 2);
     const int64_t W = (N + 31) / 32;
     uint32_t off = 0;
-    for (int64_t b = 0; b < L.NB; ++b)
-      for (int64_t g = 0; g < G; ++g) {
+    for (int64_t g = 0; g < G; ++g)          // chunk order g*NB + b, as the base plane
+      for (int64_t b = 0; b < L.NB; ++b) {
         const uint32_t word = bitmap_host[g * W + (16 * b) / 32];
         const uint32_t m16 = (word >> ((16 * b) % 32)) & 0xFFFFu;
-        desc[(size_t)(b * G + g) * 2] = off;
-        desc[(size_t)(b * G + g) * 2 + 1] = m16;
+        desc[(size_t)(g * L.NB + b) * 2] = off;
+        desc[(size_t)(g * L.NB + b) * 2 + 1] = m16;
         off += (uint32_t)__builtin_popcount(m16);
       }
     e = hipMemcpyAsync(static_cast<char*>(packed) + L.aux, desc.data(), desc.size() * 4,

@@ -7,7 +7,10 @@
 // of a 64-wide wave has column c = l % 16 and k-quarter h = l / 16; regions start
 // on 256-byte boundaries):
 //
-//  W4A16 codes : chunk (b, g) of 1024 B at (b*G + g)*1024; lane l owns 16 B at
+//  W4A16 codes : chunk (b, g) of 1024 B at (g*NB + b)*1024 (group-major, so the
+//                chunks of one group are adjacent for every column block and the
+//                waves of a launch, advancing through K together, read
+//                neighbouring kilobytes at the same time); lane l owns 16 B at
 //                +16l = words t = 0..3; word t holds the 8 codes of
 //                k = 128g + 32t + 8h + e (e = 0..7) of column n = 16b + c, element
 //                e in nibble sigma(e) = e/2 (e even) or 4 + (e-1)/2 (e odd), so
@@ -23,11 +26,12 @@
 //                that (w & 0x0F0F0F0F) and ((w >> 4) & 0x0F0F0F0F) are the int8
 //                B-operand bytes in k order; the nibble holds q + 8 (0..15).
 //  W4A8 scales : int8 group scales [NB][G8][16][8], then fp16 channel scales [N].
-//  W2W4 base   : chunk (b, g) of 512 B; lane l owns 8 B = words s = 0, 1; bits
+//  W2W4 base   : chunk (b, g) of 512 B at (g*NB + b)*512; lane l owns 8 B = words s = 0, 1; bits
 //                [4p, 4p+1] of word s = low 2 bits of the code at slot p of W4A16
 //                word 2s, bits [4p+2, 4p+3] = same for word 2s+1.
-//  W2W4 desc   : per chunk (b, g): u32 off, u32 mask16 (bit c = column 16b + c is
-//                a 4-bit group; off = 4-bit groups in all earlier chunks).
+//  W2W4 desc   : per chunk (b, g), at index g*NB + b: u32 off, u32 mask16 (bit c =
+//                column 16b + c is a 4-bit group; off = 4-bit groups in all
+//                earlier chunks of that order).
 //  W2W4 high   : per 4-bit group, 32 B at 32*(off + rank(c)), quarter h at +8h,
 //                the upper 2 code bits in the base-plane arrangement.
 #include "qgemm_device.h"
@@ -62,7 +66,8 @@ __global__ void repack_codes_u4(const uint32_t* __restrict__ codes, uint32_t* __
   if (tid >= total) return;
   const int lane = (int)(tid & 63);
   const int64_t chunk = tid >> 6;
-  const int b = (int)(chunk / G), g = (int)(chunk % G);
+  const int NB = N / 16;
+  const int g = (int)(chunk / NB), b = (int)(chunk % NB);
   const int c = lane & 15, h = lane >> 4;
   const int n = 16 * b + c;
   u32x4 w;
@@ -108,9 +113,9 @@ __global__ void repack_w2w4_kernel(const uint8_t* __restrict__ codes, const u32x
   if (tid >= total) return;
   const int lane = (int)(tid & 63);
   const int64_t chunk = tid >> 6;
-  const int g = (int)(chunk % G);
+  const int g = (int)(chunk / (N / 16));
   const int c = lane & 15, h = lane >> 4;
-  const int n = 16 * (int)(chunk / G) + c;
+  const int n = 16 * (int)(chunk % (N / 16)) + c;
   u32x2 lo = {0u, 0u}, hi = {0u, 0u};
 #pragma unroll
   for (int s = 0; s < 2; ++s) {

@@ -50,14 +50,14 @@ struct PolicyW2W4 {
     const int ng = ti.G1 - ti.G0;
     for (int t = threadIdx.x; t < NB * ng; t += blockDim.x) {
       const int j = t / ng, i = t % ng;
-      dst[t] = src[(size_t)(ti.b0 + j) * p.G + ti.G0 + i];
+      dst[t] = src[(size_t)(ti.G0 + i) * (p.N / 16) + ti.b0 + j];
     }
   }
 
   template <int NBW>
   struct View {
     rsrc_t rb, rh;
-    uint32_t bvoff, bblk;
+    uint32_t bvoff, gstep;
     const char* sl;
     const u32x2* desc;   // this wave's first block in the [NB][ngw] LDS table
     uint32_t sblk, below, hoff;
@@ -67,10 +67,11 @@ struct PolicyW2W4 {
                     int gw0_, int nload, int lane)
         : gw0(gw0_), c8(ti.c8), G0(ti.G0), ngw(ti.G1 - ti.G0) {
       c = lane & 15;
-      bblk = (uint32_t)p.G * 512u;
+      const uint32_t nbt = (uint32_t)(p.N / 16);
+      gstep = nbt * 512u;
       bvoff = lane * 8u;
-      rb = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)bw * p.G + gw0) * 512,
-                     (NBW - 1) * bblk + nload * 512u);
+      rb = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)gw0 * nbt + bw) * 512,
+                     (uint32_t)(nload - 1) * gstep + NBW * 512u);
       // High-plane slots come from the blob's own descriptors; lanes of 2-bit
       // groups address past the resource's size and read zeros.
       rh = make_rsrc(p.high, 0x7FFFFFF0u);
@@ -82,7 +83,7 @@ struct PolicyW2W4 {
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.base[j] = load8(rb, bvoff, j * bblk + rel * 512u);
+      for (int j = 0; j < NBW; ++j) st.base[j] = load8(rb, bvoff, j * 512u + rel * gstep);
     }
     __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
       const int g = gw0 + rel;

@@ -40,7 +40,7 @@ struct PolicyW4A8 {
   template <int NBW>
   struct View {
     rsrc_t rc;
-    uint32_t cvoff, cblk;
+    uint32_t cvoff, gstep;   // gstep: bytes from a group's chunk to the next group's
     const char* sl;
     uint32_t sblk;
     int gw0, c8;
@@ -48,16 +48,17 @@ struct PolicyW4A8 {
     __device__ View(const GemmArgs& p, const char* lds, const SkinnyLds&, const TileInfo& ti, int bw,
                     int gw0_, int nload, int lane)
         : gw0(gw0_), c8(ti.c8) {
-      cblk = (uint32_t)p.G * 1024u;
+      const uint32_t nbt = (uint32_t)(p.N / 16);
+      gstep = nbt * 1024u;
       cvoff = lane * 16u;
-      rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)bw * p.G + gw0) * 1024,
-                     (NBW - 1) * cblk + nload * 1024u);
+      rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)gw0 * nbt + bw) * 1024,
+                     (uint32_t)(nload - 1) * gstep + NBW * 1024u);
       sblk = ti.n8 * kScaleChunk;
       sl = lds + (bw - ti.b0) * sblk + (lane & 15) * 8;
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * cblk + rel * 1024u);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * 1024u + rel * gstep);
     }
     __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
       const int g = gw0 + rel;

@@ -79,15 +79,15 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   };
 
   // weights and scales of this wave's four column blocks
-  const uint32_t cblk = (uint32_t)p.G * 1024u;
-  const rsrc_t rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)bw * p.G + G0) * 1024,
-                              (kWideNBW - 1) * cblk + ng * 1024u);
+  const uint32_t gstep = (uint32_t)(p.N / 16) * 1024u;   // group-major chunks
+  const rsrc_t rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)G0 * (p.N / 16) + bw) * 1024,
+                              (uint32_t)(ng - 1) * gstep + kWideNBW * 1024u);
   const uint32_t sblk = (uint32_t)p.G8 * 256u;
   const rsrc_t rs = make_rsrc(static_cast<const char*>(p.scales) + (size_t)bw * p.G8 * 256,
                               kWideNBW * sblk);
   auto issue_b = [&](WideStage<MBW>& st, int rel) {
 #pragma unroll
-    for (int j = 0; j < kWideNBW; ++j) st.code[j] = load16(rc, lane * 16u, j * cblk + rel * 1024u);
+    for (int j = 0; j < kWideNBW; ++j) st.code[j] = load16(rc, lane * 16u, j * 1024u + rel * gstep);
     const int g = G0 + rel;
     const uint32_t soff = (uint32_t)(g >> 3) * 256u + (uint32_t)(g & 7) * 2u;
 #pragma unroll

@@ -33,8 +33,9 @@
  *   - Return value: QGEMM_OK (0) or a negative qgemm_status. Arguments are fully
  *     validated before any HIP call; a call that fails validation enqueues
  *     nothing and writes nothing. No C++ exception crosses this boundary.
- *   - Shapes: K > 0 a multiple of 128, N > 0 a multiple of 64, 0 <= M <= 65535
- *     (M == 0 returns QGEMM_OK without launching anything).
+ *   - Shapes: K > 0 a multiple of 128, N > 0 a multiple of 64, K and N at most
+ *     2^20, K*N at most 2^32 (2 GiB of 4-bit codes), 0 <= M <= 65535 (M == 0
+ *     returns QGEMM_OK without launching anything).
  *   - Pointers: 16-byte aligned; lda, ldc multiples of 8 (fp16) or 16 (int8).
  *   - Concurrent calls that share one workspace race; give each stream its own.
  */

@@ -13,7 +13,10 @@ c = l % 16 and quarter h = l // 16; every region starts at a multiple of 256
 bytes and its size is rounded up to 256):
 
 W4A16 (format 1)
-  codes   NB*G chunks of 1024 B, chunk (b, g) at (b*G + g)*1024. Lane l owns
+  codes   G*NB chunks of 1024 B, chunk (b, g) at (g*NB + b)*1024 (group-major:
+          the chunks of one group of 128 k are adjacent for all column blocks,
+          so the waves of a launch, which advance through K together, read
+          neighbouring kilobytes at the same time). Lane l owns
           16 B at +16*l: words t = 0..3. Word t holds the codes of
           k = 128*g + 32*t + 8*h + e (e = 0..7), column n = 16*b + c, with
           element e in nibble sigma(e): sigma(e) = e/2 for even e and
@@ -30,15 +33,15 @@ W4A8 (format 2)
   cscales fp16[N] = s_c[n].
 
 W2W4 mixed (format 3)
-  base    NB*G chunks of 512 B, chunk (b, g) at (b*G + g)*512. Lane l owns 8 B
+  base    G*NB chunks of 512 B, chunk (b, g) at (g*NB + b)*512. Lane l owns 8 B
           at +8*l: words s = 0, 1. For slot p = 0..7 let e = sigma^-1(p); bits
           [4p, 4p+1] hold lo2 of the W4A16 word-2s code at slot p
           (k = 128*g + 32*(2s) + 8*h + e) and bits [4p+2, 4p+3] hold lo2 of the
           W4A16 word-(2s+1) code at slot p (k + 32).
           lo2 = code & 3.
-  desc    8 B per chunk (b, g) at (b*G + g)*8: u32 off, u32 mask. mask bit c is
+  desc    8 B per chunk (b, g) at (g*NB + b)*8: u32 off, u32 mask. mask bit c is
           set when group (g, 16*b + c) is 4-bit; off is the count of 4-bit
-          groups in all chunks before (b, g) in (b*G + g) order.
+          groups in all chunks before (b, g) in (g*NB + b) order.
   scales  as W4A16.
   high    for every 4-bit group (g, n = 16*b + c): 32 B at
           32*(off(b, g) + rank(c)), rank(c) = set mask bits below c; quarter h
@@ -74,23 +77,23 @@ def _tau(e: int) -> int:
 
 
 def _codes_by_lane(q: np.ndarray, K: int, N: int) -> np.ndarray:
-    """Rearrange codes ``[K][N]`` into ``[NB][G][lane=16h+c][t][e]``.
+    """Rearrange codes ``[K][N]`` into ``[G][NB][lane=16h+c][t][e]``.
 
     k = 128*g + 32*t + 8*h + e, n = 16*b + c.
     """
     G, NB = K // GROUP, N // 16
     x = np.asarray(q).reshape(G, 4, 4, 8, NB, 16)      # g, t, h, e, b, c
-    x = x.transpose(4, 0, 2, 5, 1, 3)                  # b, g, h, c, t, e
-    return x.reshape(NB, G, 64, 4, 8)
+    x = x.transpose(0, 4, 2, 5, 1, 3)                  # g, b, h, c, t, e
+    return x.reshape(G, NB, 64, 4, 8)
 
 
 def _codes_by_lane_w4a8(q: np.ndarray, K: int, N: int) -> np.ndarray:
-    """``[K][N]`` -> ``[NB][G][lane][t = 2u + s][e]`` with
+    """``[K][N]`` -> ``[G][NB][lane][t = 2u + s][e]`` with
     k = 128*g + 64*u + 16*h + 8*s + e."""
     G, NB = K // GROUP, N // 16
     x = np.asarray(q).reshape(G, 2, 4, 2, 8, NB, 16)   # g, u, h, s, e, b, c
-    x = x.transpose(5, 0, 2, 6, 1, 3, 4)               # b, g, h, c, u, s, e
-    return x.reshape(NB, G, 64, 4, 8)
+    x = x.transpose(0, 5, 2, 6, 1, 3, 4)               # g, b, h, c, u, s, e
+    return x.reshape(G, NB, 64, 4, 8)
 
 
 def _scale_region(values: np.ndarray, G: int, N: int, dtype) -> bytes:
@@ -142,7 +145,7 @@ def blob_w4a16(qw: np.ndarray, scales: np.ndarray) -> bytes:
     K, N = qw.shape[0] * 8, qw.shape[1]
     _check_shape(K, N)
     G, NB = K // GROUP, N // 16
-    q = _codes_by_lane(_unpack_nibbles(qw), K, N)         # [NB][G][64][4][8]
+    q = _codes_by_lane(_unpack_nibbles(qw), K, N)         # [G][NB][64][4][8]
     words = np.zeros(q.shape[:4], dtype=np.uint32)
     for e in range(8):
         words |= q[..., e].astype(np.uint32) << np.uint32(4 * _sigma(e))
@@ -182,7 +185,7 @@ def _bitmap_mask(bitmap: np.ndarray, G: int, N: int) -> np.ndarray:
 
 
 def _two_bit_words(plane: np.ndarray) -> np.ndarray:
-    """``[NB][G][64][4][8]`` 2-bit values -> ``[NB][G][64][2]`` u32 words."""
+    """``[G][NB][64][4][8]`` 2-bit values -> ``[G][NB][64][2]`` u32 words."""
     out = np.zeros(plane.shape[:3] + (2,), dtype=np.uint32)
     for s in range(2):
         for p in range(8):
@@ -199,19 +202,19 @@ def blob_w2w4(codes_u8: np.ndarray, bitmap: np.ndarray, scales: np.ndarray) -> b
     G, NB = K // GROUP, N // 16
     G8 = (G + 7) // 8
     mask = _bitmap_mask(bitmap, G, N)                      # [G][N]
-    q = _codes_by_lane(codes_u8, K, N)                     # [NB][G][64][4][8]
-    base = _two_bit_words(q & np.uint8(3))                 # [NB][G][64][2]
+    q = _codes_by_lane(codes_u8, K, N)                     # [G][NB][64][4][8]
+    base = _two_bit_words(q & np.uint8(3))                 # [G][NB][64][2]
     high = _two_bit_words((q >> np.uint8(2)) & np.uint8(3))
-    # descriptors in chunk order b*G + g
-    m_bg = mask.reshape(G, NB, 16).transpose(1, 0, 2)      # [NB][G][16]
-    cnt = m_bg.sum(axis=2).ravel()
+    # descriptors in chunk order g*NB + b
+    m_gb = mask.reshape(G, NB, 16)                          # [G][NB][16]
+    cnt = m_gb.sum(axis=2).ravel()
     off = np.concatenate([[0], np.cumsum(cnt)[:-1]]).astype(np.uint32)
-    bits = (m_bg.astype(np.uint32) << np.arange(16, dtype=np.uint32)).sum(axis=2).ravel()
+    bits = (m_gb.astype(np.uint32) << np.arange(16, dtype=np.uint32)).sum(axis=2).ravel()
     desc = np.stack([off, bits.astype(np.uint32)], axis=1).astype("<u4")
     n4 = int(cnt.sum())
-    # high plane: quarter pieces of 4-bit groups in (b, g, c) order
-    hi_words = high.reshape(NB, G, 4, 16, 2).transpose(0, 1, 3, 2, 4)   # b, g, c, h, s
-    sel = hi_words[m_bg]                                    # [n4][4][2] in (b, g, c) order
+    # high plane: quarter pieces of 4-bit groups in (g, b, c) order
+    hi_words = high.reshape(G, NB, 4, 16, 2).transpose(0, 1, 3, 2, 4)   # g, b, c, h, s
+    sel = hi_words[m_gb]                                    # [n4][4][2] in (g, b, c) order
     hbytes = sel.astype("<u4").tobytes()
     out = (_pad_to(base.astype("<u4").tobytes(), _align256(NB * G * 512))
            + _pad_to(desc.tobytes(), _align256(NB * G * 8))
@@ -228,11 +231,11 @@ def decode_w4a16(blob: bytes, K: int, N: int):
     G, NB = K // GROUP, N // 16
     G8 = (G + 7) // 8
     raw = np.frombuffer(blob, dtype=np.uint8)
-    words = raw[:NB * G * 1024].view("<u4").reshape(NB, G, 64, 4)
-    q = np.zeros((NB, G, 64, 4, 8), dtype=np.uint8)
+    words = raw[:NB * G * 1024].view("<u4").reshape(G, NB, 64, 4)
+    q = np.zeros((G, NB, 64, 4, 8), dtype=np.uint8)
     for e in range(8):
         q[..., e] = (words >> np.uint32(4 * _sigma(e))) & 0xF
-    codes = q.reshape(NB, G, 4, 16, 4, 8).transpose(1, 4, 2, 5, 0, 3).reshape(K, N)
+    codes = q.reshape(G, NB, 4, 16, 4, 8).transpose(0, 4, 2, 5, 1, 3).reshape(K, N)
     s0 = _align256(NB * G * 1024)
     sc = raw[s0:s0 + NB * G8 * 256].view(np.float16).reshape(NB, G8, 16, 8)
     scales = sc.transpose(1, 3, 0, 2).reshape(G8 * 8, N)[:G]

@@ -71,6 +71,9 @@ def test_shape_and_format_validation(L):
     assert L.qgemm_packed_bytes(1, 1024, 64, None, None) == ERR_NULL
     assert L.qgemm_packed_bytes(2, 16384, 64, None, ctypes.byref(out)) == OK
     assert L.qgemm_packed_bytes(2, 16512, 64, None, ctypes.byref(out)) == ERR_SHAPE
+    # K*N above 2^32 (blob offsets are 32-bit); exactly 2^32 is accepted
+    assert L.qgemm_packed_bytes(1, 1 << 20, 1 << 13, None, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_packed_bytes(1, 1 << 19, 1 << 13, None, ctypes.byref(out)) == OK
     assert L.qgemm_packed_bytes(3, 1024, 64, None, ctypes.byref(out)) == ERR_NULL
     assert L.qgemm_workspace_bytes(1, -1, 1024, 64, ctypes.byref(out)) == ERR_SHAPE
     assert L.qgemm_workspace_bytes(1, 65536, 1024, 64, ctypes.byref(out)) == ERR_SHAPE

@@ -51,8 +51,22 @@ def test_w4a16_hand_derived_words():
                                             np.ones((2, N), np.float16)), dtype="<u4")
     # lane 5 (c=5) holds column 5 everywhere: all nibbles 5
     assert blob2[5 * 4] == g["w4a16_n_mod16_lane5"]
-    # chunk (b=1, g=0) starts at word (1*G + 0)*256; lane 0 is column 16 -> code 0
-    assert blob2[2 * 256] == 0
+    # chunk (b=1, g=0) starts at word (0*NB + 1)*256 (group-major); lane 0 is column 16
+    assert blob2[1 * 256] == 0
+
+
+def test_w4a16_chunks_are_group_major():
+    # codes constant per (group, column block): v = (5*g + b) % 16; every word of chunk
+    # (b, g) is then v repeated in all 8 nibbles, and the chunk sits at (g*NB + b)*1 KB
+    K, N = 384, 128
+    G, NB = K // 128, N // 16
+    q = _pattern(K, N, lambda k, n: (5 * (k // 128) + n // 16) % 16)
+    words = np.frombuffer(layout.blob_w4a16(gen.pack_nibbles_u32(q), np.ones((G, N), np.float16)),
+                          dtype="<u4")
+    for g in range(G):
+        for b in range(NB):
+            chunk = words[(g * NB + b) * 256:(g * NB + b + 1) * 256]
+            assert np.all(chunk == 0x11111111 * ((5 * g + b) % 16)), (g, b)
 
 
 def test_w4a16_scale_region_hand():
@@ -143,12 +157,12 @@ def test_w2w4_all_four_bit_base_plus_high_reconstruct_w4a16_words():
     blob = layout.blob_w2w4(q, gen.bitmap_from_mask(mask), p["scales"])
     w16 = np.frombuffer(layout.blob_w4a16(p["codes"], p["scales"]), dtype="<u4")
     NB, G = N // 16, K // 128
-    base = np.frombuffer(blob[:NB * G * 512], dtype="<u4").reshape(NB, G, 64, 2)
+    base = np.frombuffer(blob[:NB * G * 512], dtype="<u4").reshape(G, NB, 64, 2)
     d0 = NB * G * 512
     h0 = d0 + 256 + 1024                # desc: 64 B -> 256; scales: NB*G8*256 = 1024
-    high_w = np.frombuffer(blob[h0:h0 + 32 * NB * G * 16], dtype="<u4").reshape(NB, G, 16, 4, 2)
-    high = high_w.transpose(0, 1, 3, 2, 4).reshape(NB, G, 64, 2)   # (b, g, h, c, s) -> lane
-    w16 = w16[:NB * G * 256].reshape(NB, G, 64, 4)
+    high_w = np.frombuffer(blob[h0:h0 + 32 * NB * G * 16], dtype="<u4").reshape(G, NB, 16, 4, 2)
+    high = high_w.transpose(0, 1, 3, 2, 4).reshape(G, NB, 64, 2)   # (g, b, h, c, s) -> lane
+    w16 = w16[:NB * G * 256].reshape(G, NB, 64, 4)
     for s in range(2):
         lo0 = base[..., s] & 0x33333333
         lo1 = (base[..., s] >> 2) & 0x33333333
