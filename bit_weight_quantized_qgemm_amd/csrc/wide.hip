@@ -2,49 +2,72 @@
 // batch range of the MARLIN abstract, where its speedup shrinks with batch size
 // but persists up to 64-128.
 //
-// Each workgroup owns a tile of 16*MBW rows (64 or 128) x 256 columns; its four
-// waves each own 64 columns and every row of the tile, so every weight is
-// dequantized once per tile and reused by MBW v_mfma_f32_16x16x32_f16 row blocks.
-// Activations are shared by the four waves through LDS:
-//   * per group of 128 k, the tile's activations arrive in MFMA A-fragment order
-//     (1 KB per 16 rows x 32 k) by direct buffer-to-LDS loads, issued two groups
-//     ahead into a 3-slot LDS ring, each wave fetching a quarter of the fragments;
-//   * one barrier per group publishes a slot, after the wave's own loads of that
-//     slot are counted complete (s_waitcnt on the in-order vector memory counter);
-//   * the slot written next is the one all waves finished reading before the
-//     barrier, so no second barrier is needed.
-// Weights stream per wave into a register ring (two groups ahead) together with
-// the lane's fp16 group scale; dequantization is exact to fp16 (q - 8), then one
-// packed multiply by the scale rounds once (the scale cannot be applied after the
-// MFMA here without doubling the accumulators). Accumulation is fp32.
+// Each workgroup owns a tile of 16*MBW rows (64 or 128) x 256 columns; its eight
+// waves (two per SIMD, so one wave's dequantization and LDS reads overlap the
+// other's matrix operations) form a grid of NWC column waves x 8/NWC row waves,
+// each owning 256/NWC columns and 16*MBW*NWC/8 rows. Each weight is dequantized
+// by the 8/NWC row waves of its columns and reused by all of their rows. The products
+// run on v_mfma_f32_32x32x16_f16, which on gfx950 sustains nearly twice the
+// throughput of the 16x16x32 form for the same operand bytes:
+//   * operands of one 32x32x16 step: lane l holds row (A) or column (B) l % 32
+//     and k = 8*(l/32) .. +7 of the 16-k step; the result's element i of lane l
+//     is row 8*(i/4) + 4*(l/32) + i%4, column l % 32;
+//   * the blob keeps its 16-column chunk order (shared with the streaming
+//     kernel): the B operand of 32-column block jb for k-step u is word u/2 of
+//     blob lane 16*(2*(u%2) + l/32) + l%16 of 16-column block 2*jb + (l%32)/16,
+//     so every lane fetches two 16-byte pieces per 32-column block and group
+//     (its "even" and "odd" k-steps) at lane-dependent offsets - each byte of
+//     the chunk pair is still loaded exactly once per wave;
+//   * per group of 128 k the tile's activations arrive in 32x32x16 A-operand
+//     order (1 KB per 32 rows x 16 k) by direct buffer-to-LDS loads, issued
+//     kDepth groups ahead into an LDS ring, each wave fetching an eighth; one
+//     barrier per group publishes a slot after the wave's own loads of it are
+//     counted complete (s_waitcnt on the in-order vector memory counter), and the
+//     slot written next is the one all waves finished reading before that
+//     barrier.
+// Weights stream per wave into a register ring (kDepth groups ahead) together
+// with the lane's fp16 group scales; dequantization is exact to fp16 (q - 8),
+// then one packed multiply by the scale rounds once (the scale cannot be applied
+// after the MFMA here without doubling the accumulators). Accumulation is fp32.
 // When a layer has too few tiles for the chip, K is also split across workgroups
 // and finished with the coherent-store / arrival-counter fix-up.
 #include "skinny.h"
 
+#include <atomic>
+
 namespace qg {
 namespace {
 
-constexpr int kWideWaves = 4;
-constexpr int kWideNBW = 4;                            // 16-column blocks per wave
-static_assert(kWideCols == 4 * 4 * 16, "tile width = waves x blocks x 16");
-constexpr int kASlots = 3;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int MBW>
+constexpr int kWideWaves = 8;
+constexpr int kDepth = 3;                              // groups of loads in flight ahead
+constexpr int kASlots = kDepth + 1;                    // LDS slots and register stages
+
+template <int JB>
 struct WideStage {
-  u32x4 code[kWideNBW];
-  uint32_t s[kWideNBW];
+  u32x4 even[JB];   // words t = k-steps 2t of each 32-column block
+  u32x4 odd[JB];    // words t = k-steps 2t + 1
+  uint32_t s[JB];   // fp16 group scale of the lane's column (low half)
 };
 
 }  // namespace
 
-template <int MBW>
+template <int MBW, int NWC>
 __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* flag) {
-  constexpr int kSlotBytes = MBW * 4 * 1024;        // MBW row blocks x 4 k-steps x 1 KB
-  constexpr int kAPerWave = MBW;                    // fragment loads per wave per group
+  constexpr int NWR = kWideWaves / NWC;             // row waves
+  constexpr int kWideJB = kWideCols / 32 / NWC;     // 32-column blocks per wave
+  constexpr int R32T = MBW / 2;                     // 32-row blocks of the tile
+  constexpr int R32 = R32T / NWR;                   // 32-row blocks per wave
+  static_assert(R32 >= 1 && kWideJB >= 1, "wave grid");
+  constexpr int kSlotBytes = R32T * 8 * 1024;       // 32-row blocks x 8 k-steps x 1 KB
+  constexpr int kAPerWave = R32T * 8 / kWideWaves;  // fragment loads per wave per group
+  using Stage = WideStage<kWideJB>;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, h = lane >> 4;
+  const int wc = wave % NWC, wr = wave / NWC;
+  const int c32 = lane & 31, hh = lane >> 5;
   const int nt = blockIdx.x % p.nt;
   const int rest = blockIdx.x / p.nt;
   const int mt = rest % p.mt;
@@ -53,189 +76,226 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   const int ng = min(p.G, G0 + p.gps) - G0;
   const int row0 = mt * MBW * 16;
   const int rows = min(MBW * 16, p.M - row0);
-  const int bw = nt * (kWideCols / 16) + wave * kWideNBW;   // first block of this wave
+  const int bw = nt * (kWideCols / 16) + wc * 2 * kWideJB;     // first 16-column block of the wave
+  const int rw0 = wr * R32 * 32;                                // first tile row of the wave
 
   // activations: rows of the tile from k = 128*G0; rows beyond M re-read a valid row
   const rsrc_t ra = make_rsrc(static_cast<const f16*>(p.A) + (size_t)row0 * p.lda + (size_t)G0 * kGroup,
                               (uint32_t)(((size_t)(rows - 1) * p.lda + (size_t)ng * kGroup) * 2));
-  // this wave fetches row blocks rb = wave*MBW/4 .. +MBW/4, all four k-steps
-  constexpr int kRbPerWave = MBW / 4;
-  uint32_t avoff[kRbPerWave];
+  // fragment f = rb32 * 8 + u (32 rows x 16 k); this wave fetches f = wave*kAPerWave ..
+  uint32_t avoff[kAPerWave];
+  int afrag[kAPerWave];
 #pragma unroll
-  for (int q = 0; q < kRbPerWave; ++q) {
-    const int rb = wave * kRbPerWave + q;
-    avoff[q] = (uint32_t)((size_t)min(rb * 16 + c, rows - 1) * p.lda * 2 + h * 16);
+  for (int q = 0; q < kAPerWave; ++q) {
+    const int f = wave * kAPerWave + q;
+    const int rb32 = f >> 3, u = f & 7;
+    afrag[q] = f;
+    avoff[q] = (uint32_t)((size_t)min(rb32 * 32 + c32, rows - 1) * p.lda * 2 + u * 32 + hh * 16);
   }
   auto issue_a = [&](int rel, int slot) {
 #pragma unroll
-    for (int q = 0; q < kRbPerWave; ++q) {
-      const int rb = wave * kRbPerWave + q;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        char* dst = lds + slot * kSlotBytes + (rb * 4 + t) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)dst, 16, avoff[q], rel * 256u + t * 64u, 0, 0);
-      }
-    }
+    for (int q = 0; q < kAPerWave; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + slot * kSlotBytes + afrag[q] * 1024), 16,
+                                               avoff[q], rel * 256u, 0, 0);
   };
 
-  // weights and scales of this wave's four column blocks
-  const uint32_t gstep = (uint32_t)(p.N / 16) * 1024u;   // group-major chunks
+  // weights and scales of this wave's 32-column blocks (group-major chunks)
+  const uint32_t gstep = (uint32_t)(p.N / 16) * 1024u;
   const rsrc_t rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)G0 * (p.N / 16) + bw) * 1024,
-                              (uint32_t)(ng - 1) * gstep + kWideNBW * 1024u);
+                              (uint32_t)(ng - 1) * gstep + 2 * kWideJB * 1024u);
+  uint32_t cvoff[kWideJB];
+#pragma unroll
+  for (int jb = 0; jb < kWideJB; ++jb)
+    cvoff[jb] = (uint32_t)((2 * jb + (c32 >> 4)) * 1024 + (16 * hh + (c32 & 15)) * 16);
   const uint32_t sblk = (uint32_t)p.G8 * 256u;
   const rsrc_t rs = make_rsrc(static_cast<const char*>(p.scales) + (size_t)bw * p.G8 * 256,
-                              kWideNBW * sblk);
-  auto issue_b = [&](WideStage<MBW>& st, int rel) {
+                              2 * kWideJB * sblk);
+  uint32_t svoff[kWideJB];
 #pragma unroll
-    for (int j = 0; j < kWideNBW; ++j) st.code[j] = load16(rc, lane * 16u, j * 1024u + rel * gstep);
+  for (int jb = 0; jb < kWideJB; ++jb) svoff[jb] = (uint32_t)((2 * jb + (c32 >> 4)) * sblk + (c32 & 15) * 16);
+  auto issue_b = [&](Stage& st, int rel) {
+#pragma unroll
+    for (int jb = 0; jb < kWideJB; ++jb) {
+      st.even[jb] = load16(rc, cvoff[jb], rel * gstep);
+      st.odd[jb] = load16(rc, cvoff[jb] + 512u, rel * gstep);
+    }
     const int g = G0 + rel;
     const uint32_t soff = (uint32_t)(g >> 3) * 256u + (uint32_t)(g & 7) * 2u;
 #pragma unroll
-    for (int j = 0; j < kWideNBW; ++j)
-      st.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, c * 16u, j * sblk + soff, 0);
+    for (int jb = 0; jb < kWideJB; ++jb) st.s[jb] = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff[jb], soff, 0);
   };
+  constexpr int kBPerGroup = 3 * kWideJB;           // vector memory operations of issue_b
 
-  f32x4 acc[MBW][kWideNBW];
+  f32x16 acc[R32][kWideJB];
 #pragma unroll
-  for (int rb = 0; rb < MBW; ++rb)
+  for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-    for (int j = 0; j < kWideNBW; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < kWideJB; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][jb][i] = 0.f;
 
   const f16x2 lo_off = splat_h2(-1032.0f), hi_off = splat_h2(-72.0f);
   const uint32_t magic = 0x64006400u;
 
-  // Prologue: activations and weights of groups 0 and 1. Each later iteration
-  // issues one batch (activations, then weights and scales, of group i + 2), so
-  // at the wait of iteration i exactly the weights of group i and the batch of
-  // group i + 1 (MBW + 4*NBW operations) were issued after the last fragment
-  // load of group i; the vector memory counter retires loads in order. Weights
-  // live in a 3-stage register ring (two groups ahead); slots and stages are
-  // static inside the 3-iteration body, and the iterations past the end only
-  // re-issue in-bounds loads and skip the math.
-  WideStage<MBW> st[kASlots];
-  issue_a(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue_b(st[0], 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue_a(min(1, ng - 1), 1);
-  __builtin_amdgcn_sched_barrier(0);
-  issue_b(st[1], min(1, ng - 1));
-  __builtin_amdgcn_sched_barrier(0);
+  // Prologue: activations and weights of groups 0 .. kDepth-1. Each later
+  // iteration issues one batch (activations, then weights and scales, of group
+  // i + kDepth), so at the wait of iteration i the weights of group i and the
+  // batches of groups i+1 .. i+kDepth-1 were issued after the last fragment load
+  // of group i; the vector memory counter retires loads in order. Slots and
+  // stages are static inside the unrolled body, and the iterations past the end
+  // only re-issue in-bounds loads and skip the math.
+  Stage st[kASlots];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    issue_a(min(d, ng - 1), d);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(st[d], min(d, ng - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  constexpr int kAfter = kBPerGroup + (kDepth - 1) * (kAPerWave + kBPerGroup);
+  static_assert(kAfter < 64, "vmcnt range");
+
+  // B operand of k-step u for both 32-column blocks, scaled
+  auto dequant_step = [&](const Stage& cur, int u, f16x8 (&bf)[kWideJB]) {
+#pragma unroll
+    for (int jb = 0; jb < kWideJB; ++jb) {
+      const uint32_t w = (u & 1) ? cur.odd[jb][u >> 1] : cur.even[jb][u >> 1];
+      const f16 sh = as_h2(cur.s[jb])[0];
+      const f16x8 sc8 = {sh, sh, sh, sh, sh, sh, sh, sh};
+      bf[jb] = dequant_u4x8(w, lo_off, hi_off, magic) * sc8;
+    }
+  };
+  auto read_a = [&](const char* slot, int u, f16x8 (&a)[R32]) {
+#pragma unroll
+    for (int rb = 0; rb < R32; ++rb)
+      a[rb] = *reinterpret_cast<const f16x8*>(slot + ((wr * R32 + rb) * 8 + u) * 1024 + lane * 16);
+  };
 
   for (int base = 0; base < ng; base += kASlots) {
 #pragma unroll
     for (int r = 0; r < kASlots; ++r) {
       const int i = base + r;
       // raw_barrier(): publishes only the counted completion above (see skinny.h)
-      wait_vmcnt<kAPerWave + 4 * kWideNBW>();
+      wait_vmcnt<kAfter>();
       raw_barrier();
-      issue_a(min(i + 2, ng - 1), (r + 2) % kASlots);
-      issue_b(st[(r + 2) % kASlots], min(i + 2, ng - 1));
+      issue_a(min(i + kDepth, ng - 1), (r + kDepth) % kASlots);
+      issue_b(st[(r + kDepth) % kASlots], min(i + kDepth, ng - 1));
       __builtin_amdgcn_sched_barrier(0);
       if (i < ng) {
-        const WideStage<MBW>& cur = st[r];
+        const Stage& cur = st[r];
         const char* slot = lds + r * kSlotBytes;
+        // software pipeline over the 8 k-steps: the fragments and dequantized
+        // weights of step u+1 are fetched while the MFMAs of step u run
+        f16x8 a[2][R32], bf[2][kWideJB];
+        read_a(slot, 0, a[0]);
+        dequant_step(cur, 0, bf[0]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          f16x8 bf[kWideNBW];
-#pragma unroll
-          for (int j = 0; j < kWideNBW; ++j) {
-            const f16 sh = as_h2(cur.s[j])[0];
-            const f16x8 sc8 = {sh, sh, sh, sh, sh, sh, sh, sh};
-            bf[j] = dequant_u4x8(cur.code[j][t], lo_off, hi_off, magic) * sc8;
+        for (int u = 0; u < 8; ++u) {
+          if (u < 7) {
+            read_a(slot, u + 1, a[(u + 1) & 1]);
+            dequant_step(cur, u + 1, bf[(u + 1) & 1]);
           }
 #pragma unroll
-          for (int rb = 0; rb < MBW; ++rb) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(slot + (rb * 4 + t) * 1024 + lane * 16);
+          for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-            for (int j = 0; j < kWideNBW; ++j)
-              acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[j], acc[rb][j], 0, 0, 0);
-          }
+            for (int jb = 0; jb < kWideJB; ++jb)
+              acc[rb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[u & 1][rb], bf[u & 1][jb], acc[rb][jb], 0, 0, 0);
         }
       }
     }
   }
 
-  // ---- epilogue
-  const int colw = bw * 16 + c;
-  if (p.splits == 1) {
+  // ---- epilogue: element i of lane l is row 8*(i/4) + 4*hh + i%4 of the 32-row
+  // block, column c32 of the 32-column block
+  auto store_tile = [&]() {
     f16* C = static_cast<f16*>(p.C);
 #pragma unroll
-    for (int rb = 0; rb < MBW; ++rb)
+    for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + 4 * h + i;
+      for (int i = 0; i < 16; ++i) {
+        const int r = rw0 + rb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
         if (r < rows) {
 #pragma unroll
-          for (int j = 0; j < kWideNBW; ++j)
-            C[(size_t)(row0 + r) * p.ldc + colw + j * 16] = (f16)acc[rb][j][i];
+          for (int jb = 0; jb < kWideJB; ++jb)
+            C[(size_t)(row0 + r) * p.ldc + (bw + 2 * jb) * 16 + c32] = (f16)acc[rb][jb][i];
         }
       }
+  };
+  if (p.splits == 1) {
+    store_tile();
     return;
   }
-  // Cross-workgroup split: partials in MFMA-fragment order, one 1 KB wave
-  // fragment per (wave, row block, column block), so every access is a
-  // coalesced 16-byte device-coherent buffer operation. Region of (split,
-  // tile): kWideWaves * MBW * NBW KB.
-  constexpr int kFrag = MBW * kWideNBW;
+  // Cross-workgroup split: partials in accumulator order, four 1 KB pieces per
+  // (wave, 32-row block, 32-column block), so every access is a coalesced
+  // 16-byte device-coherent buffer operation. Region of (split, tile):
+  // kWideWaves * R32 * kWideJB * 4 KB.
+  constexpr int kFrag = R32 * kWideJB * 4;
   constexpr uint32_t kRegion = kWideWaves * kFrag * 1024;
   const size_t tile_id = (size_t)mt * p.nt + nt;
   const size_t ntiles = (size_t)p.mt * p.nt;
   auto region = [&](int q) {
     return make_rsrc(static_cast<char*>(p.partial) + ((size_t)q * ntiles + tile_id) * kRegion, kRegion);
   };
-  auto voff = [&](int rb, int j) {
-    return (uint32_t)(((wave * kFrag + rb * kWideNBW + j) * 64 + lane) * 16);
+  auto voff = [&](int rb, int jb, int q4) {
+    return (uint32_t)((((wave * R32 + rb) * kWideJB + jb) * 4 + q4) * 1024 + lane * 16);
   };
   {
     const rsrc_t mine = region(split);
 #pragma unroll
-    for (int rb = 0; rb < MBW; ++rb)
+    for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-      for (int j = 0; j < kWideNBW; ++j) store16_coherent(acc[rb][j], mine, voff(rb, j));
+      for (int jb = 0; jb < kWideJB; ++jb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = {acc[rb][jb][4 * q4], acc[rb][jb][4 * q4 + 1], acc[rb][jb][4 * q4 + 2],
+                           acc[rb][jb][4 * q4 + 3]};
+          store16_coherent(v, mine, voff(rb, jb, q4));
+        }
   }
   if (!workgroup_arrive_last(p.counters + tile_id, (uint32_t)p.splits, flag)) return;
   // last arriver: sum the splits in split order (deterministic), then store fp16
 #pragma unroll
-  for (int rb = 0; rb < MBW; ++rb)
+  for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-    for (int j = 0; j < kWideNBW; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jb = 0; jb < kWideJB; ++jb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][jb][i] = 0.f;
   for (int q = 0; q < p.splits; ++q) {
     const rsrc_t rq = region(q);
-    f32x4 v[MBW][kWideNBW];
 #pragma unroll
-    for (int rb = 0; rb < MBW; ++rb)
+    for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-      for (int j = 0; j < kWideNBW; ++j) v[rb][j] = load16_coherent(rq, voff(rb, j));
+      for (int jb = 0; jb < kWideJB; ++jb)
 #pragma unroll
-    for (int rb = 0; rb < MBW; ++rb)
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = load16_coherent(rq, voff(rb, jb, q4));
 #pragma unroll
-      for (int j = 0; j < kWideNBW; ++j) acc[rb][j] += v[rb][j];
+          for (int e = 0; e < 4; ++e) {
+            const float ve = v[e];
+            acc[rb][jb][4 * q4 + e] += ve;
+          }
+        }
   }
-  f16* C = static_cast<f16*>(p.C);
-#pragma unroll
-  for (int rb = 0; rb < MBW; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rb * 16 + 4 * h + i;
-      if (r < rows) {
-#pragma unroll
-        for (int j = 0; j < kWideNBW; ++j)
-          C[(size_t)(row0 + r) * p.ldc + colw + j * 16] = (f16)acc[rb][j][i];
-      }
-    }
+  store_tile();
 }
 
-__global__ void __launch_bounds__(256) w4a16_wide_m64(GemmArgs p) {
+#ifndef QG_WIDE_NWC64
+#define QG_WIDE_NWC64 8
+#endif
+#ifndef QG_WIDE_NWC128
+#define QG_WIDE_NWC128 8
+#endif
+
+__global__ void __launch_bounds__(512) w4a16_wide_m64(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flag;
-  wide_body<4>(p, lds, &flag);
+  wide_body<4, QG_WIDE_NWC64>(p, lds, &flag);
 }
 
-__global__ void __launch_bounds__(256) w4a16_wide_m128(GemmArgs p) {
+__global__ void __launch_bounds__(512) w4a16_wide_m128(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flag;
-  wide_body<8>(p, lds, &flag);
+  wide_body<8, QG_WIDE_NWC128>(p, lds, &flag);
 }
 
 namespace {
@@ -244,12 +304,12 @@ hipError_t launch_wide_k(const void* fn, void (*kernel)(GemmArgs), int mbw, cons
                          const GemmArgs& a, hipStream_t s) {
   const size_t lds = (size_t)kASlots * mbw * 4 * 1024;
   // the LDS size is fixed per kernel: opt in to it (above 64 KiB) once
-  static bool big_lds[2] = {false, false};
-  bool& done = big_lds[mbw == 8];
-  if (!done) {
+  static std::atomic<bool> big_lds[2] = {false, false};
+  std::atomic<bool>& done = big_lds[mbw == 8];
+  if (!done.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    done = true;
+    done.store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * kWideWaves), lds, s, a);
   return hipGetLastError();
