@@ -109,6 +109,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--shapes", default="all", choices=["all", "up", "down"])
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other configured workloads (7B layers, W4A8, mixed 2/4-bit)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (the known-size "
                          "reference for HBM byte counters)")
@@ -148,6 +150,103 @@ def cpu_baseline(target_s: float) -> dict:
         "sample": f"fp64 dequantize+matmul of the M sweep {MS} on both shapes, first {n_cols} "
                   f"output columns ({flops / 1e9:.2f} GFLOP, {dt:.2f} s; includes input generation)",
     }
+
+
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
+
+SECONDARY = (
+    [("w4a16 config-0", 1, 1024, 1024, 16)]
+    + [("w4a16 7B layer", 1, K, N, M) for (K, N) in [(4096, 4096), (4096, 11008), (11008, 4096)]
+       for M in (1, 16, 32, 64, 128)]
+    + [("w4a8", 2, 4096, 11008, M) for M in (16, 64, 128)]
+    + [("mixed 2/4-bit", 3, 4096, 4096, M) for M in (1, 16, 64)]
+)
+
+
+def secondary_bytes_ops(fmt, K, N, M, n4=0):
+    """Algorithmic bytes and ops of one launch (codes, scales, A, C)."""
+    G = K // 128
+    if fmt == 1:
+        return alg_bytes(M, K, N), alg_flops(M, K, N)
+    if fmt == 2:
+        return K * N // 2 + G * N + 2 * N + M * K + 2 * M + 2 * M * N, alg_flops(M, K, N)
+    groups = G * N
+    return (32 * (groups - n4) + 64 * n4 + 2 * groups + groups // 8 + 2 * M * K + 2 * M * N,
+            alg_flops(M, K, N))
+
+
+def secondary(torch, qg, dev, rotate_mb):
+    """The other configured workloads, each timed as replays of a captured HIP
+    graph of back-to-back launches over rotating weight copies (kernel time
+    without host launch overhead; weights stream from HBM)."""
+    from synth import gen
+    stream = torch.cuda.current_stream()
+    rows = []
+    built = {}
+    for (name, fmt, K, N, M) in SECONDARY:
+        key = (fmt, K, N)
+        if key not in built:
+            if fmt == 1:
+                p = gen.w4a16_problem(128, K, N, seed=0)
+                blob = qg.repack_w4a16(torch.from_numpy(p["codes"].view(np.int32)).to(dev),
+                                       torch.from_numpy(p["scales"]).to(dev))
+                A = torch.from_numpy(p["A"]).to(dev)
+                extra = {}
+            elif fmt == 2:
+                p = gen.w4a8_problem(128, K, N, seed=0)
+                blob = qg.repack_w4a8(torch.from_numpy(p["codes"].view(np.int32)).to(dev),
+                                      torch.from_numpy(p["group_scales"]).to(dev),
+                                      torch.from_numpy(p["chan_scales"]).to(dev))
+                A = torch.from_numpy(p["A"]).to(dev)
+                extra = {"a_scale": torch.from_numpy(p["a_scale"]).to(dev)}
+            else:
+                p = gen.w2w4_problem(128, K, N, seed=0)
+                blob = qg.repack_w2w4(torch.from_numpy(p["codes"]).to(dev), torch.from_numpy(p["scales"]).to(dev),
+                                      p["bitmap"])
+                A = torch.from_numpy(p["A"]).to(dev)
+                extra = {"n4": int(p["mask"].sum())}
+            reps = max(2, math.ceil(rotate_mb * 2**20 / blob.numel()))
+            built = {key: (([blob] + [blob.clone() for _ in range(reps - 1)]), A, extra)}
+        blobs, A_all, extra = built[key]
+        A = A_all[:M].contiguous()
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        ws = qg.Workspace()
+        if fmt == 1:
+            run = lambda b: qg.w4a16(A, b, K, N, out=C, workspace=ws)
+        elif fmt == 2:
+            a_s = extra["a_scale"][:M].contiguous()
+            run = lambda b: qg.w4a8(A, a_s, b, K, N, out=C, workspace=ws)
+        else:
+            run = lambda b: qg.w2w4_mixed(A, b, K, N, out=C, workspace=ws)
+        for i in range(3):
+            run(blobs[i % len(blobs)])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        n = len(blobs)
+        with torch.cuda.graph(g):
+            for i in range(n):
+                run(blobs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (5 * n)
+        byt, ops = secondary_bytes_ops(fmt, K, N, M, extra.get("n4", 0))
+        peak = INT8_PEAK_TOPS if fmt == 2 else FP16_PEAK_TFLOPS
+        gbs = byt / (us * 1e-6) / 1e9
+        tops = ops / (us * 1e-6) / 1e12
+        roof_us = max(byt / (HBM_PEAK_GBS * 1e9), ops / (peak * 1e12)) * 1e6
+        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4"][fmt], "K": K, "N": N, "M": M,
+                     "us": round(us, 2), "tops": round(tops, 2), "gbs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline_frac": round(roof_us / us, 4),
+                     "bound": "hbm" if byt / (HBM_PEAK_GBS * 1e9) >= ops / (peak * 1e12) else "mfma",
+                     "launches_per_graph": n})
+        del g
+    return rows
 
 
 def main():
@@ -297,6 +396,8 @@ def main():
                  "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                  "source_sha": source_sha()})
 
+    sec = None if args.no_secondary else secondary(torch, qg, dev, 512)
+
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -318,6 +419,7 @@ def main():
         "roofline": roof,
         "per_m": per_m,
         "cpu_baseline": cpu,
+        "secondary": sec,
     }
     print(json.dumps(out), flush=True)
 
