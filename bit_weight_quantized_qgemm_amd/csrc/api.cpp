@@ -159,8 +159,14 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
 Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
   const int force_kernel = g_force_kernel.load();
   const bool wide_ok = fmt == QGEMM_FMT_W4A16 && N % kWideCols == 0;
-  if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM)))
-    return make_wide_plan(M, K, N);
+  if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM))) {
+    // The wide tile (256 columns, all rows of the batch) needs many k-splits on
+    // narrow layers, and their partial sums then cost more than re-streaming
+    // the weights once per 32-row tile of the streaming kernel (measured on
+    // MI355X: 7B-class layers at M = 64..128 and N = 8192 at M = 128).
+    const Plan wide = make_wide_plan(M, K, N);
+    if (force_kernel == 2 || wide.splits <= 4 || (K * N >= (int64_t(1) << 27) && M <= 64)) return wide;
+  }
   // Streaming kernel: 4*KP-wave workgroups own 16*mb x 64*nb tiles; the 4
   // column waves of each of the KP K-parts share activations through LDS.
   //
@@ -207,8 +213,10 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
     for (int kp = 1; kp <= 4; kp *= 2) {
       if (force_wpt && kp != std::max(1, force_wpt / 4)) continue;
       if (kp > G) continue;
-      // the mixed format's 2 x 2 tile with four K-parts would spill registers
-      if (fmt == QGEMM_FMT_W2W4 && pl.mb == 2 && nb == 2 && kp == 4 && !force_wpt) continue;
+      // 1024-thread workgroups leave 128 VGPRs per wave: these tiles would spill
+      if (kp == 4 && !force_wpt && nb == 2 &&
+          (fmt == QGEMM_FMT_W2W4 || (fmt == QGEMM_FMT_W4A8 && pl.mb == 2)))
+        continue;
       const int smax = tiles > kMaxCounters ? 1 : std::min(G, 64);
       for (int s0 = 1; s0 <= smax; ++s0) {
         if (force_splits && s0 != std::min(force_splits, G)) continue;

@@ -86,6 +86,19 @@ __device__ __forceinline__ void stage_scales(const void* scales, char* lds, int 
   }
 }
 
+// Geometry shared by the policies built on 16 x 16 MFMA tiles: A fragment fr
+// (16 rows x one k-step) of a 16-row block, and the position of accumulator
+// element i of lane ln in fragment (mb, j) of a wave's tile.
+struct Tile16 {
+  template <int kFrag>
+  __device__ static uint32_t a_voff16(int fr, int lane, int rows, size_t arow) {
+    const int rb = fr / kFrag, f = fr % kFrag;
+    return (uint32_t)((size_t)min(rb * 16 + (lane & 15), rows - 1) * arow + 64 * f + 16 * (lane >> 4));
+  }
+  __device__ static int row_of(int mb, int, int i, int ln) { return mb * 16 + 4 * (ln >> 4) + i; }
+  __device__ static int col_of(int, int j, int ln) { return j * 16 + (ln & 15); }
+};
+
 // LDS layout of a launch: [scales | extra | A rings (KP x 3 slots)]; the
 // reduction buffer reuses the start of LDS after the main loop.
 struct SkinnyLds {
@@ -96,7 +109,7 @@ template <class F>
 __host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_max, int ng_max) {
   SkinnyLds L;
   const int NB = 4 * NBW;
-  L.scale_bytes = NB * n8_max * F::kScaleChunk;
+  L.scale_bytes = F::kStageScales ? NB * n8_max * F::kScaleChunk : 0;
   L.extra_off = L.scale_bytes;
   const int extra = F::extra_lds(NB, ng_max);
   L.ring_off = (L.extra_off + extra + 255) / 256 * 256;
@@ -152,9 +165,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
 #pragma unroll
   for (int q = 0; q < kAPerWave; ++q) {
     const int fr = min(nw + 4 * q, kFrags - 1);   // waves past the last fragment duplicate it
-    const int rb = fr / F::kFrag, f = fr % F::kFrag;
     afrag[q] = fr;
-    avoff[q] = (uint32_t)((size_t)min(rb * 16 + c, ti.rows - 1) * arow + 64 * f + 16 * h);
+    avoff[q] = F::a_voff(fr, lane, ti.rows, arow);
   }
   char* ring = lds + L.ring_off + kp * 3 * L.slot_bytes;
   auto issue_a = [&](int rel, int slot) {
@@ -171,40 +183,52 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
 
-  // ---- prologue: the first two groups' loads go out before the scale staging
-  Stage st[3];
+  // ---- prologue. Weights run kWD groups ahead in a register ring of kWD + 1
+  // stages, activations two groups ahead in a 3-slot LDS ring. (A deeper weight
+  // ring was measured slower on MI355X: the extra registers cost occupancy.)
+  // The first loads go out before the scale staging.
+  constexpr int kWD = 2, kWS = kWD + 1, kAS = 3;
+  static_assert(kWS % kAS == 0, "the unrolled body must return both rings to slot 0");
+  auto wl = [&](int g) { return min(g, nload - 1); };
+  Stage st[kWS];
+#pragma unroll
+  for (int d = 0; d < kWD - 2; ++d) {
+    v.load_vmem(st[d], wl(d));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   issue_a(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  v.load_vmem(st[0], 0);
+  v.load_vmem(st[kWD - 2], wl(kWD - 2));
   __builtin_amdgcn_sched_barrier(0);
-  issue_a(min(1, nload - 1), 1);
+  issue_a(wl(1), 1);
   __builtin_amdgcn_sched_barrier(0);
-  v.load_vmem(st[1], min(1, nload - 1));
+  v.load_vmem(st[kWD - 1], wl(kWD - 1));
   __builtin_amdgcn_sched_barrier(0);
-  stage_scales(p.scales, lds, NB, p.G8, ti.b0, ti.c8, ti.n8, F::kScaleChunk);
+  if (F::kStageScales) stage_scales(p.scales, lds, NB, p.G8, ti.b0, ti.c8, ti.n8, F::kScaleChunk);
   F::stage_extra(p, lds + L.extra_off, ti, NB);
   __syncthreads();
-  v.load_lds(st[0], 0);
-  v.load_lds(st[1], min(1, nload - 1));
+#pragma unroll
+  for (int d = 0; d < kWD; ++d) v.load_lds(st[d], wl(d));
 
   const typename F::Consts k;
   // Per iteration each wave issues one batch: its A fragments of group i + 2,
-  // then the weights of group i + 2. At the wait of iteration i at least the
-  // weights of group i and the whole batch of group i + 1 were issued after
-  // the wave's last A(i) load, and the counter retires loads in order.
+  // then the weights of group i + kWD. At the wait of iteration i the weights
+  // of group i + kWD - 2 and the whole batch of iteration i - 1 were issued
+  // after the wave's last A(i) load (the weights of group i went out earlier
+  // still), and the counter retires loads in order.
   constexpr int kAfter = kAPerWave + 2 * Stage::kVmem;
-  for (int base = 0; base < iters; base += 3) {
+  for (int base = 0; base < iters; base += kWS) {
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
+    for (int r = 0; r < kWS; ++r) {
       const int i = base + r;
       if (i < iters) {   // uniform over the workgroup
         wait_vmcnt<kAfter>();
         raw_barrier();
-        issue_a(min(i + 2, nload - 1), (r + 2) % 3);
-        v.load_vmem(st[(r + 2) % 3], min(i + 2, nload - 1));
+        issue_a(wl(i + 2), (r + 2) % kAS);
+        v.load_vmem(st[(r + kWD) % kWS], wl(i + kWD));
         __builtin_amdgcn_sched_barrier(0);
-        v.load_lds(st[(r + 2) % 3], min(i + 2, nload - 1));
-        F::template compute<MB, NBW>(st[r], ring + r * L.slot_bytes, acc, i < ngk, k, lane);
+        v.load_lds(st[(r + kWD) % kWS], wl(i + kWD));
+        F::template compute<MB, NBW>(st[r], ring + (r % kAS) * L.slot_bytes, acc, i < ngk, k, lane);
       }
     }
   }
@@ -228,8 +252,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
       for (int q = 1; q < KP; ++q) s += red[q * kTileElems + e];
       const int i = e & 3, ln = (e >> 2) & 63, fj = e >> 8;      // fj = (nw*MB + mb)*NBW + j
       const int j = fj % NBW, mb = (fj / NBW) % MB, w = fj / (NBW * MB);
-      const int row = ti.row0 + mb * 16 + 4 * (ln >> 4) + i;
-      const int col = (ti.b0 + w * NBW + j) * 16 + (ln & 15);
+      const int row = ti.row0 + F::row_of(mb, j, i, ln);
+      const int col = (ti.b0 + w * NBW) * 16 + F::col_of(mb, j, ln);
       if (row < ti.row0 + ti.rows) F::store(p, row, col, s);
     }
     return;
@@ -269,10 +293,10 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
     }
     const int ln = e4 & 63, fj = e4 >> 6;
     const int j = fj % NBW, mb = (fj / NBW) % MB, w = fj / (NBW * MB);
-    const int col = (ti.b0 + w * NBW + j) * 16 + (ln & 15);
+    const int col = (ti.b0 + w * NBW) * 16 + F::col_of(mb, j, ln);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = ti.row0 + mb * 16 + 4 * (ln >> 4) + i;
+      const int row = ti.row0 + F::row_of(mb, j, i, ln);
       if (row < ti.row0 + ti.rows) F::store(p, row, col, s[i]);
     }
   }

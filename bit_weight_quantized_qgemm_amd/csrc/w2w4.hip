@@ -20,12 +20,16 @@
 namespace qg {
 namespace fmt {
 
-struct PolicyW2W4 {
+struct PolicyW2W4 : Tile16 {
   using Acc = f32x4;
   using Elem = float;
   static constexpr int kScaleChunk = 256;
   static constexpr int kFrag = 4;
   static constexpr int kAElem = 2;
+  static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
+  __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
+    return a_voff16<kFrag>(fr, lane, rows, arow);
+  }
 
   struct Consts {
     f16x2 lo4 = splat_h2(-1032.0f), hi4 = splat_h2(-72.0f);   // zero point 8

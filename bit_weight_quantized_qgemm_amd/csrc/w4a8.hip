@@ -18,12 +18,16 @@
 namespace qg {
 namespace fmt {
 
-struct PolicyW4A8 {
+struct PolicyW4A8 : Tile16 {
   using Acc = i32x4;
   using Elem = int32_t;
   static constexpr int kScaleChunk = 128;   // 16 columns x 8 groups x int8
   static constexpr int kFrag = 2;           // A fragments (16 rows x 64 k) per group
   static constexpr int kAElem = 1;
+  static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
+  __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
+    return a_voff16<kFrag>(fr, lane, rows, arow);
+  }
 
   struct Consts {};
 
