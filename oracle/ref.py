@@ -133,6 +133,33 @@ def gemm_w4a8(A_i8, qw, group_scales, a_scale, chan_scales, cols=None):
     return acc, w4a8_out(acc, a_scale, chan_scales, cols=cols)
 
 
+def quantize_a8(A: np.ndarray):
+    """Per-token (per-row) dynamic int8 quantization of fp16 activations, the
+    input side of the W4A8 GEMM (the Atom review's method section adapts the
+    activation quantization parameters to each activation matrix at inference
+    time; the OdysseyLLM abstract's W4A8 GEMM consumes int8 activations).
+
+    The pages give no formula; the reading taken here is symmetric absmax:
+
+        a_s[m]   = fp16(amax_m / 127),  amax_m = max_k |A[m, k]|   (fp32 division,
+                                                                  one RNE rounding)
+        q[m, k]  = clamp(rint(fp32(A[m, k]) / fp32(a_s[m])), -127, 127)
+                   (fp32 division, round half to even)
+
+    A row whose a_s is zero (all zeros, or so small that amax/127 rounds to fp16
+    zero) quantizes to zeros. Inputs must be finite. Returns (q int8[M][K],
+    a_s fp16[M]).
+    """
+    A32 = np.asarray(A, dtype=np.float16).astype(np.float32)
+    amax = np.abs(A32).max(axis=1) if A32.shape[1] else np.zeros(A32.shape[0], np.float32)
+    a_s = (amax / np.float32(127.0)).astype(np.float32).astype(np.float16)
+    s32 = a_s.astype(np.float32)
+    q = np.zeros(A32.shape, dtype=np.float32)
+    nz = s32 > 0
+    q[nz] = np.rint(A32[nz] / s32[nz, None])
+    return np.clip(q, -127, 127).astype(np.int8), a_s
+
+
 # --------------------------------------------------------------------------- mixed 2/4-bit
 def dequant_w2w4(codes_u8: np.ndarray, bitmap: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """fp64 ``W[k, n] = (q[k, n] - z[g, n]) * s[g, n]`` with ``g = k // 128`` and
