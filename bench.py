@@ -160,12 +160,19 @@ SECONDARY = (
        for M in (1, 16, 32, 64, 128)]
     + [("w4a8", 2, 4096, 11008, M) for M in (16, 64, 128)]
     + [("mixed 2/4-bit", 3, 4096, 4096, M) for M in (1, 16, 64)]
+    + [("per-token int8 quantization", 4, 4096, 0, M) for M in (16, 64, 128)]
+    + [("w4a8 from fp16 (quantize + GEMM)", 5, 4096, 11008, M) for M in (16, 64, 128)]
 )
 
 
 def secondary_bytes_ops(fmt, K, N, M, n4=0):
     """Algorithmic bytes and ops of one launch (codes, scales, A, C)."""
     G = K // 128
+    if fmt == 4:   # read fp16 A, write int8 codes and fp16 scales
+        return 3 * M * K + 2 * M, M * K
+    if fmt == 5:   # the quantization's bytes plus the W4A8 GEMM's
+        b, o = secondary_bytes_ops(2, K, N, M)
+        return b + 3 * M * K + 2 * M, o
     if fmt == 1:
         return alg_bytes(M, K, N), alg_flops(M, K, N)
     if fmt == 2:
@@ -186,36 +193,55 @@ def secondary(torch, qg, dev, rotate_mb):
     for (name, fmt, K, N, M) in SECONDARY:
         key = (fmt, K, N)
         if key not in built:
-            if fmt == 1:
+            if fmt == 4:
+                A = torch.from_numpy(gen.w4a16_problem(128, K, 128, seed=0, weights=False)["A"]).to(dev)
+                blob, extra = None, {}
+            elif fmt == 1:
                 p = gen.w4a16_problem(128, K, N, seed=0)
                 blob = qg.repack_w4a16(torch.from_numpy(p["codes"].view(np.int32)).to(dev),
                                        torch.from_numpy(p["scales"]).to(dev))
                 A = torch.from_numpy(p["A"]).to(dev)
                 extra = {}
-            elif fmt == 2:
+            elif fmt in (2, 5):
                 p = gen.w4a8_problem(128, K, N, seed=0)
                 blob = qg.repack_w4a8(torch.from_numpy(p["codes"].view(np.int32)).to(dev),
                                       torch.from_numpy(p["group_scales"]).to(dev),
                                       torch.from_numpy(p["chan_scales"]).to(dev))
                 A = torch.from_numpy(p["A"]).to(dev)
                 extra = {"a_scale": torch.from_numpy(p["a_scale"]).to(dev)}
+                if fmt == 5:
+                    A = torch.from_numpy(gen.w4a16_problem(128, K, 128, seed=0, weights=False)["A"]).to(dev)
             else:
                 p = gen.w2w4_problem(128, K, N, seed=0)
                 blob = qg.repack_w2w4(torch.from_numpy(p["codes"]).to(dev), torch.from_numpy(p["scales"]).to(dev),
                                       p["bitmap"])
                 A = torch.from_numpy(p["A"]).to(dev)
                 extra = {"n4": int(p["mask"].sum())}
-            reps = max(2, math.ceil(rotate_mb * 2**20 / blob.numel()))
-            built = {key: (([blob] + [blob.clone() for _ in range(reps - 1)]), A, extra)}
+            if blob is None:   # no weights: a graph of 64 launches
+                built = {key: ([None] * 64, A, extra)}
+            else:
+                reps = max(2, math.ceil(rotate_mb * 2**20 / blob.numel()))
+                built = {key: (([blob] + [blob.clone() for _ in range(reps - 1)]), A, extra)}
         blobs, A_all, extra = built[key]
         A = A_all[:M].contiguous()
-        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        C = torch.empty((M, max(N, 1)), dtype=torch.float16, device=dev)
         ws = qg.Workspace()
         if fmt == 1:
             run = lambda b: qg.w4a16(A, b, K, N, out=C, workspace=ws)
         elif fmt == 2:
             a_s = extra["a_scale"][:M].contiguous()
             run = lambda b: qg.w4a8(A, a_s, b, K, N, out=C, workspace=ws)
+        elif fmt == 4:
+            Qb = torch.empty((M, K), dtype=torch.int8, device=dev)
+            Sb = torch.empty((M,), dtype=torch.float16, device=dev)
+            run = lambda b: qg.quantize_a8(A, out=Qb, scale_out=Sb)
+        elif fmt == 5:
+            Qb = torch.empty((M, K), dtype=torch.int8, device=dev)
+            Sb = torch.empty((M,), dtype=torch.float16, device=dev)
+
+            def run(b):
+                qg.quantize_a8(A, out=Qb, scale_out=Sb)
+                qg.w4a8(Qb, Sb, b, K, N, out=C, workspace=ws)
         else:
             run = lambda b: qg.w2w4_mixed(A, b, K, N, out=C, workspace=ws)
         for i in range(3):
@@ -236,11 +262,12 @@ def secondary(torch, qg, dev, rotate_mb):
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (5 * n)
         byt, ops = secondary_bytes_ops(fmt, K, N, M, extra.get("n4", 0))
-        peak = INT8_PEAK_TOPS if fmt == 2 else FP16_PEAK_TFLOPS
+        peak = INT8_PEAK_TOPS if fmt in (2, 5) else FP16_PEAK_TFLOPS
         gbs = byt / (us * 1e-6) / 1e9
         tops = ops / (us * 1e-6) / 1e12
         roof_us = max(byt / (HBM_PEAK_GBS * 1e9), ops / (peak * 1e12)) * 1e6
-        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4"][fmt], "K": K, "N": N, "M": M,
+        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4", "quant_a8", "w4a8_fp16"][fmt],
+                     "K": K, "N": N, "M": M,
                      "us": round(us, 2), "tops": round(tops, 2), "gbs": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline_frac": round(roof_us / us, 4),
                      "bound": "hbm" if byt / (HBM_PEAK_GBS * 1e9) >= ops / (peak * 1e12) else "mfma",

@@ -15,7 +15,8 @@ import os
 __all__ = [
     "FMT_W4A16", "FMT_W4A8", "FMT_W2W4", "QgemmError", "lib", "lib_path", "packed_bytes",
     "workspace_bytes", "plan", "set_plan_override", "repack", "repack_w4a16", "repack_w4a8",
-    "repack_w2w4", "w4a16", "w4a8", "w2w4_mixed", "Workspace", "EXPORTED_SYMBOLS",
+    "repack_w2w4", "w4a16", "w4a8", "w2w4_mixed", "Workspace", "EXPORTED_SYMBOLS", "quantize_a8",
+    "w4a8_fp16",
 ]
 
 FMT_W4A16 = 1
@@ -29,7 +30,7 @@ _lib = None
 EXPORTED_SYMBOLS = (
     "qgemm_status_str", "qgemm_last_error", "qgemm_version", "qgemm_packed_bytes",
     "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16", "qgemm_w4a8", "qgemm_w2w4_mixed",
-    "qgemm_plan", "qgemm_set_plan_override",
+    "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8",
 )
 
 
@@ -64,8 +65,10 @@ def lib() -> ctypes.CDLL:
         L.qgemm_w2w4_mixed.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.qgemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
         L.qgemm_set_plan_override.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.qgemm_quantize_a8.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
-                     "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override"):
+                     "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
+                     "qgemm_quantize_a8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -239,3 +242,27 @@ def w2w4_mixed(A, blob, K: int, N: int, out=None, workspace: Workspace | None = 
     _check(lib().qgemm_w2w4_mixed(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K,
                                   N, _ptr(ws), wsb, _stream_ptr(A.device)), "qgemm_w2w4_mixed")
     return out
+
+
+def quantize_a8(A, out=None, scale_out=None):
+    """Per-token int8 quantization of fp16 activations A [M][K]; returns
+    (A_q int8 [M][K'] with K' = K rounded up to 16 for the row stride, viewed as
+    [M][K], a_scale fp16 [M])."""
+    torch = _torch()
+    _require_cuda(A)
+    M, K = A.shape
+    ldq = (K + 15) // 16 * 16
+    if out is None:
+        out = torch.empty((M, ldq), dtype=torch.int8, device=A.device)
+    if scale_out is None:
+        scale_out = torch.empty((M,), dtype=torch.float16, device=A.device)
+    _check(lib().qgemm_quantize_a8(_ptr(A), A.stride(0), M, K, _ptr(out), out.stride(0), _ptr(scale_out),
+                                   _stream_ptr(A.device)), "qgemm_quantize_a8")
+    return out[:, :K], scale_out
+
+
+def w4a8_fp16(A, blob, K: int, N: int, out=None, acc_out=None, workspace: Workspace | None = None):
+    """W4A8 GEMM from fp16 activations: per-token int8 quantization, then the
+    int8 x int4 GEMM (two launches on the current stream)."""
+    A_q, a_s = quantize_a8(A)
+    return w4a8(A_q, a_s, blob, K, N, out=out, acc_out=acc_out, workspace=workspace)

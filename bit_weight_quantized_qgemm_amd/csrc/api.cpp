@@ -535,4 +535,24 @@ int qgemm_w2w4_mixed(const void* A, int64_t lda, const void* packed, void* C, in
                    workspace_bytes, stream});
 }
 
+int qgemm_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* A_q, int64_t ldq,
+                      void* a_scale, void* stream) {
+  if (K <= 0 || K % 8 != 0 || K > kMaxKN) return QGEMM_ERR_SHAPE;
+  if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
+  if (M == 0) return QGEMM_OK;
+  if (!A || !A_q || !a_scale) return QGEMM_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(A_q, 16) || !aligned(a_scale, 2)) return QGEMM_ERR_ALIGN;
+  if (lda < K || lda % 8 != 0 || ldq < K || ldq % 16 != 0) return QGEMM_ERR_ALIGN;
+  const size_t a_bytes = (size_t)((M - 1) * lda + K) * 2;
+  const size_t q_bytes = (size_t)((M - 1) * ldq + K);
+  if (overlap(A_q, q_bytes, A, a_bytes) || overlap(a_scale, (size_t)M * 2, A, a_bytes) ||
+      overlap(a_scale, (size_t)M * 2, A_q, q_bytes))
+    return QGEMM_ERR_ALIAS;
+  const int st = check_device();
+  if (st) return st;
+  const hipError_t e = qg::launch_quantize_a8(A, lda, M, K, A_q, ldq, a_scale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return QGEMM_OK;
+}
+
 }  // extern "C"

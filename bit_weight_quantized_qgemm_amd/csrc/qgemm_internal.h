@@ -83,6 +83,8 @@ hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* Q, int64_t ldq,
+                              void* S, hipStream_t s);
 hipError_t launch_repack_w4a16(const BlobLayout& L, const void* codes, const void* scales,
                                void* packed, hipStream_t s);
 hipError_t launch_repack_w4a8(const BlobLayout& L, const void* codes, const void* gscales,

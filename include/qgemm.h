@@ -160,6 +160,25 @@ int qgemm_w2w4_mixed(const void* A, int64_t lda, const void* packed, void* C, in
                      void* stream);
 
 /*
+ * Per-token dynamic int8 quantization of fp16 activations, producing the A and
+ * a_scale operands of qgemm_w4a8 (the Atom review's method section adapts the
+ * activation quantization parameters to each activation matrix at inference
+ * time; the OdysseyLLM abstract's W4A8 GEMM takes int8 activations). Symmetric
+ * absmax per row m of A fp16[M][lda]:
+ *   a_scale[m] = fp16(amax_m / 127), amax_m = max_k |A[m,k]| (fp32 division,
+ *                round to nearest even),
+ *   A_q[m,k]   = clamp(rint(A[m,k] / a_scale[m]), -127, 127) (fp32, half to
+ *                even); a row with a_scale[m] == 0 becomes zeros.
+ * A_q int8[M][ldq] and a_scale fp16[M] are device outputs owned by the caller.
+ * Shapes: 0 < K <= 2^20 a multiple of 8, 0 <= M <= 65535 (M == 0: no launch).
+ * Alignment: A and A_q 16 bytes, a_scale 2 bytes, lda >= K a multiple of 8,
+ * ldq >= K a multiple of 16 (so A_q feeds qgemm_w4a8 directly). Outputs must
+ * not overlap A or each other (QGEMM_ERR_ALIAS). Elements of A must be finite.
+ */
+int qgemm_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* A_q, int64_t ldq,
+                      void* a_scale, void* stream);
+
+/*
  * Work decomposition used for a call of this shape (for tests and tuning).
  * Fills out10[0..9] = {kernel id (1 streaming, 2 wide), 16-row blocks per tile
  * (per wave for kernel 2), 16-column blocks per wave, waves per workgroup,

@@ -115,6 +115,29 @@ def test_gemm_validation_order_without_gpu(L):
         assert len(L.qgemm_last_error()) > 0
 
 
+def test_quantize_a8_validation_without_gpu(L):
+    A, Q, S = _fake(0x10000000), _fake(0x20000000), _fake(0x30000000)
+    M, K = 16, 4096
+    assert L.qgemm_quantize_a8(None, K, 0, K, None, K, None, None) == OK       # M == 0: no launch
+    assert L.qgemm_quantize_a8(A, K, M, 0, Q, K, S, None) == ERR_SHAPE
+    assert L.qgemm_quantize_a8(A, K, M, 12, Q, K, S, None) == ERR_SHAPE       # K % 8
+    assert L.qgemm_quantize_a8(A, K, -1, K, Q, K, S, None) == ERR_SHAPE
+    assert L.qgemm_quantize_a8(A, K, 65536, K, Q, K, S, None) == ERR_SHAPE
+    assert L.qgemm_quantize_a8(A, K, M, K, None, K, S, None) == ERR_NULL
+    assert L.qgemm_quantize_a8(A, K, M, K, Q, K, None, None) == ERR_NULL
+    assert L.qgemm_quantize_a8(_fake(0x10000008), K, M, K, Q, K, S, None) == ERR_ALIGN
+    assert L.qgemm_quantize_a8(A, K, M, K, _fake(0x20000008), K, S, None) == ERR_ALIGN
+    assert L.qgemm_quantize_a8(A, K, M, K, Q, K, _fake(0x30000001), None) == ERR_ALIGN
+    assert L.qgemm_quantize_a8(A, K - 8, M, K, Q, K, S, None) == ERR_ALIGN     # lda < K
+    assert L.qgemm_quantize_a8(A, K + 4, M, K, Q, K, S, None) == ERR_ALIGN     # lda % 8
+    assert L.qgemm_quantize_a8(A, K, M, K, Q, K + 8, S, None) == ERR_ALIGN     # ldq % 16
+    assert L.qgemm_quantize_a8(A, K, M, K, _fake(0x10000000 + 1024), K, S, None) == ERR_ALIAS
+    assert L.qgemm_quantize_a8(A, K, M, K, Q, K, _fake(0x20000000 + 64), None) == ERR_ALIAS
+    st = L.qgemm_quantize_a8(A, K, M, K, Q, K, S, None)
+    if st != OK:
+        assert st in (ERR_HIP, ERR_DEV)
+
+
 def test_repack_validation_without_gpu(L):
     K, N = 1024, 1024
     nb = qg.packed_bytes(qg.FMT_W4A16, K, N)
