@@ -107,7 +107,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--burst", type=int, default=40, help="launches per per-kernel timing burst")
     ap.add_argument("--rotate-mb", type=int, default=640, help="minimum bytes of distinct weight copies")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle sample time")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--shapes", default="all", choices=["all", "up", "down"])
     ap.add_argument("--no-secondary", action="store_true",
@@ -121,7 +121,8 @@ def parse():
 def cpu_baseline(target_s: float) -> dict:
     """The NumPy oracle as it stands, on a bounded sample of the step's work:
     the full M sweep on both shapes restricted to the first n_cols output
-    columns (n_cols grown until the sample takes about target_s seconds)."""
+    columns of each shape (n_cols grown until the sample takes about target_s
+    seconds; at the full width of a shape the sweep is repeated)."""
     from oracle import ref
     from synth import gen
 
@@ -130,26 +131,40 @@ def cpu_baseline(target_s: float) -> dict:
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    n_cols = 256
-    while True:
+
+    def sweep(n_cols):
         flops = 0
-        t0 = time.perf_counter()
         for (K, N) in SHAPES:
-            p = gen.w4a16_problem(128, K, n_cols, seed=0)
+            n = min(n_cols, N)
+            p = gen.w4a16_problem(128, K, n, seed=0)
             for M in MS:
                 ref.gemm_w4a16(p["A"][:M], p["codes"], p["scales"])
-                flops += alg_flops(M, K, n_cols)
+                flops += alg_flops(M, K, n)
+        return flops
+
+    n_cols = 512
+    while True:
+        t0 = time.perf_counter()
+        flops = sweep(n_cols)
         dt = time.perf_counter() - t0
-        if dt >= target_s / 3 or n_cols >= 8192:
+        if dt >= target_s / 2 or n_cols >= max(N for _, N in SHAPES):
             break
-        n_cols *= 2
+        n_cols = min(n_cols * 2, max(N for _, N in SHAPES))
+    reps = 1
+    while dt < target_s * 0.75 and reps < 8:    # full width reached: repeat the sweep
+        t0 = time.perf_counter()
+        flops_r = sweep(n_cols)
+        dt += time.perf_counter() - t0
+        flops += flops_r
+        reps += 1
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 dequantize+matmul of the M sweep {MS} on both shapes, first {n_cols} "
-                  f"output columns ({flops / 1e9:.2f} GFLOP, {dt:.2f} s; includes input generation)",
+        "sample": f"fp64 dequantize+matmul of the M sweep {MS} on both shapes, first {n_cols} output "
+                  f"columns of each ({reps} pass(es), {flops / 1e9:.2f} GFLOP, {dt:.2f} s; includes input "
+                  f"generation)",
     }
 
 
