@@ -121,27 +121,22 @@ BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4) {
   return L;
 }
 
-// Large-M W4A16 plan: 4-wave workgroups own 16*mb x 256 tiles; K is split across
-// workgroups only as far as it shortens the number of rounds of resident tiles.
+// Large-M W4A16 plan: 8-wave workgroups own 16*mb x 256 tiles. K is split across
+// workgroups until about one workgroup per CU is busy: measured on MI355X, a
+// second resident workgroup per CU does not pay for the extra partial-sum
+// traffic of the splits it needs.
 Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   Plan pl;
   const int G = (int)(K / kGroup);
   pl.kernel = 2;
   pl.mb = M <= 64 ? 4 : 8;
   pl.nb = 4;
-  pl.wpt = 4;
+  pl.wpt = 8;
   pl.mt = (int)((M + 16 * pl.mb - 1) / (16 * pl.mb));
   pl.nt = (int)(N / kWideCols);
   const int64_t tiles = (int64_t)pl.mt * pl.nt;
-  const int64_t slots = (int64_t)kCUs * (pl.mb == 4 ? 2 : 1);   // resident workgroups
   const int force_splits = g_force_splits.load();
-  int best = 1;
-  double best_cost = 1e30;
-  for (int s = 1; s <= std::max(1, std::min(16, G / 2)); ++s) {
-    const double rounds = (double)((tiles * s + slots - 1) / slots);
-    const double cost = rounds / s + (s > 1 ? 0.02 * s : 0.0);
-    if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
-  }
+  const int best = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, G / 2), kCUs / tiles));
   int splits = force_splits ? std::min(force_splits, G) : best;
   if (tiles > kMaxCounters) splits = 1;
   pl.gps = (G + splits - 1) / splits;
