@@ -129,7 +129,11 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   Plan pl;
   const int G = (int)(K / kGroup);
   pl.kernel = 2;
-  pl.mb = M <= 64 ? 4 : 8;
+  // 64-row tiles at every M: larger M takes more row tiles, which re-read the
+  // same weights from L2 (row tiles of one column tile sit on one XCD), rather
+  // than taller tiles that would need more k-splits (measured on MI355X:
+  // 128 x 8192 x 28672 in 78 us as 2 x 64 rows vs 93 us as one 128-row tile)
+  pl.mb = 4;
   pl.nb = 4;
   pl.wpt = 8;
   pl.mt = (int)((M + 16 * pl.mb - 1) / (16 * pl.mb));

@@ -2,7 +2,7 @@
 // batch range of the MARLIN abstract, where its speedup shrinks with batch size
 // but persists up to 64-128.
 //
-// Each workgroup owns a tile of 16*MBW rows (64 or 128) x 256 columns; its eight
+// Each workgroup owns a tile of 16*MBW = 64 rows x 256 columns; its eight
 // waves (two per SIMD, so one wave's dequantization and LDS reads overlap the
 // other's matrix operations) form a grid of NWC column waves x 8/NWC row waves,
 // each owning 256/NWC columns and 16*MBW*NWC/8 rows. Each weight is dequantized
@@ -254,6 +254,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   }
   if (!workgroup_arrive_last(p.counters + tile_id, (uint32_t)p.splits, flag)) return;
   // last arriver: sum the splits in split order (deterministic), then store fp16
+  // (measured faster than prefetching the next split or reusing the own partial
+  // from registers, which raise register pressure)
 #pragma unroll
   for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
@@ -279,24 +281,13 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   store_tile();
 }
 
-#ifndef QG_WIDE_NWC64
-#define QG_WIDE_NWC64 8
-#endif
-#ifndef QG_WIDE_NWC128
-#define QG_WIDE_NWC128 8
-#endif
-
 __global__ void __launch_bounds__(512) w4a16_wide_m64(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flag;
-  wide_body<4, QG_WIDE_NWC64>(p, lds, &flag);
+  wide_body<4, 8>(p, lds, &flag);   // eight column waves of 32 columns
 }
 
-__global__ void __launch_bounds__(512) w4a16_wide_m128(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int flag;
-  wide_body<8, QG_WIDE_NWC128>(p, lds, &flag);
-}
+
 
 namespace {
 
@@ -304,8 +295,7 @@ hipError_t launch_wide_k(const void* fn, void (*kernel)(GemmArgs), int mbw, cons
                          const GemmArgs& a, hipStream_t s) {
   const size_t lds = (size_t)kASlots * mbw * 4 * 1024;
   // the LDS size is fixed per kernel: opt in to it (above 64 KiB) once
-  static std::atomic<bool> big_lds[2] = {false, false};
-  std::atomic<bool>& done = big_lds[mbw == 8];
+  static std::atomic<bool> done{false};
   if (!done.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -320,7 +310,6 @@ hipError_t launch_wide_k(const void* fn, void (*kernel)(GemmArgs), int mbw, cons
 hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s) {
   switch (pl.mb) {
     case 4: return launch_wide_k(reinterpret_cast<const void*>(&w4a16_wide_m64), w4a16_wide_m64, 4, pl, a, s);
-    case 8: return launch_wide_k(reinterpret_cast<const void*>(&w4a16_wide_m128), w4a16_wide_m128, 8, pl, a, s);
     default: return hipErrorInvalidValue;
   }
 }
