@@ -9,11 +9,13 @@ fails loudly if its HIP build is missing.
                         W4A8), following the MARLIN abstract's problem statement
                         (fp16 activations times 4-bit weights, batched), the
                         OdysseyLLM abstract (W4A8) and the 2-bit page's mixed
-                        2/4-bit groups; plus the per-token dynamic int8
+                        2/4-bit groups; the 4-bit GEMM on a general grid
+                        (group length 64 .. K, stored zero points, fp16 or bf16
+                        activations); plus the per-token dynamic int8
                         activation quantization that feeds W4A8.
 * ``oracle.layout``  -- an independent implementation of the repacked weight
                         blob byte layout, for byte-exact checks of the GPU repack.
-* ``oracle.compare`` -- the fp16 output tolerance rule.
+* ``oracle.compare`` -- the fp16 and bf16 output tolerance rules.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values that
 do not come from the oracle itself (exact rational brute force, closed forms,

@@ -47,6 +47,17 @@ W2W4 mixed (format 3)
           32*(off(b, g) + rank(c)), rank(c) = set mask bits below c; quarter h
           at +8*h holds 2 words in the base-plane arrangement but with
           hi2 = (code >> 2) & 3.
+
+W4G (format 4: 4-bit codes on a general grid -- group length gs = 64 or a
+multiple of 128 dividing K, optional stored zero points, fp16 or bf16
+activations and scales)
+  codes   as W4A16 (chunks of 128 k, whatever gs is).
+  params  one entry per (group g = k // gs, column n): the scale's 16-bit
+          pattern (fp16 or bf16) when there are no stored zero points, else a
+          u32 = scale bits | zero point << 16. With P = 2 for gs = 64 and
+          P = 1 otherwise, entry (g, n) sits at index ((g // P)*N + n)*P + g % P,
+          so the entries of the two 64-k groups of one 128-k chunk of a column
+          are adjacent.
 """
 
 from __future__ import annotations
@@ -58,6 +69,7 @@ GROUP = 128
 FMT_W4A16 = 1
 FMT_W4A8 = 2
 FMT_W2W4 = 3
+FMT_W4G = 4
 
 
 def _align256(x: int) -> int:
@@ -140,20 +152,66 @@ def packed_bytes(fmt: int, K: int, N: int, n4: int = 0) -> int:
 
 
 # --------------------------------------------------------------------------- W4A16
-def blob_w4a16(qw: np.ndarray, scales: np.ndarray) -> bytes:
-    qw = np.asarray(qw, dtype=np.uint32)
-    K, N = qw.shape[0] * 8, qw.shape[1]
-    _check_shape(K, N)
+def _w4a16_codes(qw: np.ndarray, K: int, N: int) -> bytes:
     G, NB = K // GROUP, N // 16
     q = _codes_by_lane(_unpack_nibbles(qw), K, N)         # [G][NB][64][4][8]
     words = np.zeros(q.shape[:4], dtype=np.uint32)
     for e in range(8):
         words |= q[..., e].astype(np.uint32) << np.uint32(4 * _sigma(e))
-    codes = _pad_to(words.astype("<u4").tobytes(), _align256(NB * G * 1024))
+    return _pad_to(words.astype("<u4").tobytes(), _align256(NB * G * 1024))
+
+
+def blob_w4a16(qw: np.ndarray, scales: np.ndarray) -> bytes:
+    qw = np.asarray(qw, dtype=np.uint32)
+    K, N = qw.shape[0] * 8, qw.shape[1]
+    _check_shape(K, N)
+    G, NB = K // GROUP, N // 16
+    codes = _w4a16_codes(qw, K, N)
     sc = _pad_to(_scale_region(np.asarray(scales, dtype=np.float16), G, N, np.float16),
                  _align256(NB * ((G + 7) // 8) * 256))
     out = codes + sc
     assert len(out) == packed_bytes(FMT_W4A16, K, N)
+    return out
+
+
+# --------------------------------------------------------------------------- W4G
+def check_group_size(K: int, gs: int):
+    if not (gs == 64 or (gs > 0 and gs % GROUP == 0 and K % gs == 0)):
+        raise ValueError("group size must be 64 or a multiple of 128 that divides K")
+
+
+def packed_bytes_w4g(K: int, N: int, gs: int, has_zeros: bool) -> int:
+    _check_shape(K, N)
+    check_group_size(K, gs)
+    G, NB = K // GROUP, N // 16
+    return _align256(NB * G * 1024) + _align256((K // gs) * N * (4 if has_zeros else 2))
+
+
+def blob_w4g(qw: np.ndarray, scales: np.ndarray, zeros, gs: int, act: str) -> bytes:
+    """``scales``: fp16 array (act fp16) or bf16 bit patterns (act bf16), [K/gs][N];
+    ``zeros``: uint8 [K/gs][N] or None."""
+    qw = np.asarray(qw, dtype=np.uint32)
+    K, N = qw.shape[0] * 8, qw.shape[1]
+    _check_shape(K, N)
+    check_group_size(K, gs)
+    Gs, P = K // gs, (2 if gs == 64 else 1)
+    if act == "fp16":
+        s16 = np.asarray(scales, dtype=np.float16).view(np.uint16)
+    elif act == "bf16":
+        s16 = np.asarray(scales, dtype=np.uint16)
+    else:
+        raise ValueError("act must be fp16 or bf16")
+    assert s16.shape == (Gs, N)
+    if zeros is None:
+        ent = s16.astype("<u2")
+    else:
+        z = np.asarray(zeros).astype(np.uint32)
+        assert z.shape == (Gs, N) and z.max(initial=0) <= 15
+        ent = (s16.astype(np.uint32) | (z << np.uint32(16))).astype("<u4")
+    ent = np.ascontiguousarray(ent.reshape(Gs // P, P, N).transpose(0, 2, 1))
+    params = _pad_to(ent.tobytes(), _align256(Gs * N * ent.itemsize))
+    out = _w4a16_codes(qw, K, N) + params
+    assert len(out) == packed_bytes_w4g(K, N, gs, zeros is not None)
     return out
 
 

@@ -88,6 +88,69 @@ def gemm_w4a16(A: np.ndarray, qw: np.ndarray, scales: np.ndarray,
     return C
 
 
+# --------------------------------------------------------------------------- W4 general grid
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 values given as their 16-bit patterns -> fp64 (exact).
+
+    A bfloat16 number is the upper half of an IEEE binary32 number with the
+    same sign, exponent and leading 7 fraction bits, so widening the pattern to
+    32 bits with zero low bits gives the binary32 number exactly."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def act_to_f64(x: np.ndarray, act: str) -> np.ndarray:
+    """Activations or scales in the activation type -> fp64 (exact): fp16
+    arrays as they are, bf16 as uint16 bit patterns."""
+    if act == "fp16":
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
+    if act == "bf16":
+        return bf16_to_f64(x)
+    raise ValueError(f"unknown activation type {act!r}")
+
+
+def dequant_w4g(qw: np.ndarray, scales: np.ndarray, zeros: np.ndarray | None,
+                group_size: int, act: str = "fp16") -> np.ndarray:
+    """fp64 ``W[k, n] = (q[k, n] - z[g, n]) * s[g, n]`` with ``g = k // group_size``.
+
+    The quantization grid variants of the 4-bit weight GEMM: the 2-bit page's
+    abstract and the Atom review's method section both quantize weights by
+    groups without fixing the group length, so the group is any number of
+    consecutive k of one column (64, 128, ..., K for one scale per column);
+    ``zeros`` holds one stored integer zero point 0..15 per (group, column),
+    or None for the implicit zero point 8; the scales are in the activation
+    type. Every product is exact in fp64 (a 5-bit integer times a significand
+    of at most 11 bits)."""
+    q = unpack_u4(qw)
+    K, N = q.shape
+    if group_size <= 0 or K % group_size:
+        raise ValueError("group_size must divide K")
+    g = np.arange(K) // group_size
+    s = act_to_f64(scales, act)
+    if s.shape != (K // group_size, N):
+        raise ValueError(f"scales shape {s.shape} != {(K // group_size, N)}")
+    if zeros is None:
+        z = np.full((K // group_size, N), 8, dtype=np.int64)
+    else:
+        z = np.asarray(zeros).astype(np.int64)
+        if z.shape != s.shape:
+            raise ValueError("zeros shape must match scales")
+    return (q - z[g, :]).astype(np.float64) * s[g, :]
+
+
+def gemm_w4g(A: np.ndarray, qw: np.ndarray, scales: np.ndarray, zeros: np.ndarray | None,
+             group_size: int, act: str = "fp16", cols: np.ndarray | None = None) -> np.ndarray:
+    """fp64 ``C = A @ dequant_w4g(...)`` (A in the activation type: an fp16
+    array, or bf16 bit patterns as uint16); optionally only the listed columns."""
+    qw = np.asarray(qw)
+    scales = np.asarray(scales)
+    if cols is not None:
+        qw = qw[:, cols]
+        scales = scales[:, cols]
+        zeros = None if zeros is None else np.asarray(zeros)[:, cols]
+    return act_to_f64(A, act) @ dequant_w4g(qw, scales, zeros, group_size, act)
+
+
 # --------------------------------------------------------------------------- W4A8
 def w4a8_weights_int(qw: np.ndarray, group_scales: np.ndarray) -> np.ndarray:
     """Integer weights ``q[k, n] * s_g[k // 128, n]`` as int64."""

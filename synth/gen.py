@@ -30,6 +30,7 @@ GROUP = 128
 _KIND_W4A16 = 1
 _KIND_W4A8 = 2
 _KIND_W2W4 = 3
+_KIND_W4G = 4
 
 
 def rng_for(seed: int, *tags: int) -> np.random.Generator:
@@ -160,3 +161,39 @@ def w2w4_problem(M: int, K: int, N: int, seed: int = 0, frac4: float = 0.10,
         "mask": mask,
         "bitmap": bitmap_from_mask(mask),
     }
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite fp32 values to bfloat16 (round to nearest, ties to even) and
+    return the 16-bit patterns: the upper half of the binary32 pattern after
+    adding 0x7FFF plus the lowest kept bit."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def w4g_problem(M: int, K: int, N: int, group_size: int = 128, zeros: bool = False,
+                act: str = "fp16", seed: int = 0, weights: bool = True,
+                activations: bool = True) -> dict:
+    """4-bit weights on a general quantization grid: A ~ N(0,1) in the activation
+    type (fp16 array, or bf16 bit patterns as uint16); uint4 codes uniform 0..15;
+    one scale per (group of ``group_size`` consecutive k, column), uniform in
+    [0.005, 0.02] in the activation type; with ``zeros`` a stored zero point per
+    (group, column) uniform in 0..15 (asymmetric grids), else the implicit 8."""
+    if group_size <= 0 or K % group_size:
+        raise ValueError("group_size must divide K")
+    if act not in ("fp16", "bf16"):
+        raise ValueError("act must be fp16 or bf16")
+    tag = (_KIND_W4G, group_size, int(zeros), 0 if act == "fp16" else 1)
+    out = {"M": M, "K": K, "N": N, "group_size": group_size, "act": act}
+    cvt = (lambda x: x.astype(np.float16)) if act == "fp16" else to_bf16_bits
+    if activations:
+        out["A"] = cvt(rng_for(seed, *tag, 0, M, K).standard_normal(size=(M, K), dtype=np.float32))
+    if weights:
+        q = rng_for(seed, *tag, 1, K, N).integers(0, 16, size=(K, N), dtype=np.uint8)
+        out["codes"] = pack_nibbles_u32(q)
+        G = K // group_size
+        out["scales"] = cvt(rng_for(seed, *tag, 2, K, N).uniform(0.005, 0.02, size=(G, N)).astype(np.float32))
+        out["zeros"] = (rng_for(seed, *tag, 3, K, N).integers(0, 16, size=(G, N), dtype=np.uint8)
+                        if zeros else None)
+    return out

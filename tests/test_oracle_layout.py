@@ -170,3 +170,42 @@ def test_w2w4_all_four_bit_base_plus_high_reconstruct_w4a16_words():
         hi1 = high[..., s] & 0xCCCCCCCC
         assert np.array_equal(lo0 | hi0, w16[..., 2 * s])
         assert np.array_equal(lo1 | hi1, w16[..., 2 * s + 1])
+
+
+# --------------------------------------------------------------------------- W4G
+def test_w4g_codes_region_is_w4a16():
+    p = gen.w4a16_problem(1, 512, 128, seed=2)
+    a = layout.blob_w4a16(p["codes"], p["scales"])
+    b = layout.blob_w4g(p["codes"], p["scales"][::2], None, 256, "fp16")
+    n = 512 * 128 // 2
+    assert a[:n] == b[:n]
+
+
+def test_w4g_param_entries_hand_positions():
+    K, N = 256, 64
+    qw = np.zeros((K // 8, N), np.uint32)
+    # gs = 64, stored zeros: 4 groups; scales as bf16 patterns 0x1000 + 16 g + n % 16
+    s = np.array([[0x1000 + 16 * g + (n % 16) for n in range(N)] for g in range(4)], np.uint16)
+    z = np.array([[(g * 5 + n) % 16 for n in range(N)] for g in range(4)], np.uint8)
+    blob = layout.blob_w4g(qw, s, z, 64, "bf16")
+    base = K * N // 2
+    ent = np.frombuffer(blob[base:base + 4 * N * 4], dtype="<u4")
+    # group 3, column 5: chunk row 1, second of its pair -> index (1*64 + 5)*2 + 1 = 139
+    assert ent[139] == (0x1000 + 48 + 5) | (((15 + 5) % 16) << 16)
+    # group 0, column 63 -> index 63*2 = 126; group 1, column 0 -> index 1
+    assert ent[126] == (0x1000 + 15) | ((63 % 16) << 16)
+    assert ent[1] == (0x1000 + 16) | (5 << 16)
+    # gs = 128 without zeros: fp16 scale bits, entry (g, n) at g*N + n
+    s16 = np.arange(2 * N, dtype=np.float16).reshape(2, N) / 64
+    blob = layout.blob_w4g(qw, s16, None, 128, "fp16")
+    ent = np.frombuffer(blob[base:base + 2 * N * 2], dtype="<u2")
+    assert ent[N + 7] == s16[1, 7].view(np.uint16)
+    assert len(blob) == base + 256 + 0  # 2*64*2 = 256 bytes of entries
+
+
+def test_w4g_group_size_validation():
+    with pytest.raises(ValueError):
+        layout.packed_bytes_w4g(256, 64, 96, False)
+    with pytest.raises(ValueError):
+        layout.packed_bytes_w4g(384, 64, 256, False)
+    assert layout.packed_bytes_w4g(384, 64, 384, True) == 384 * 64 // 2 + 256
