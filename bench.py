@@ -178,12 +178,20 @@ SECONDARY = (
     + [("mixed 2/4-bit", 3, 4096, 4096, M) for M in (1, 16, 64)]
     + [("per-token int8 quantization", 4, 4096, 0, M) for M in (16, 64, 128)]
     + [("w4a8 from fp16 (quantize + GEMM)", 5, 4096, 11008, M) for M in (16, 64, 128)]
+    + [(name, 6, 4096, 11008, M) for name in ("w4g g64 fp16", "w4g g128 zeros fp16", "w4g per-channel fp16",
+                                              "w4g g128 bf16", "w4g g128 zeros bf16") for M in (1, 16)]
 )
+# general-grid variants: name -> (group size (0 = K), stored zero points, activation type)
+W4G_VARIANTS = {"w4g g64 fp16": (64, False, "fp16"), "w4g g128 zeros fp16": (128, True, "fp16"),
+                "w4g per-channel fp16": (0, False, "fp16"), "w4g g128 bf16": (128, False, "bf16"),
+                "w4g g128 zeros bf16": (128, True, "bf16")}
 
 
-def secondary_bytes_ops(fmt, K, N, M, n4=0):
+def secondary_bytes_ops(fmt, K, N, M, n4=0, gs=128, zeros=False):
     """Algorithmic bytes and ops of one launch (codes, scales, A, C)."""
     G = K // 128
+    if fmt == 6:   # codes, one 2-byte scale (4 with a zero point) per group, A, C
+        return K * N // 2 + (K // gs) * N * (4 if zeros else 2) + 2 * M * K + 2 * M * N, alg_flops(M, K, N)
     if fmt == 4:   # read fp16 A, write int8 codes and fp16 scales
         return 3 * M * K + 2 * M, M * K
     if fmt == 5:   # the quantization's bytes plus the W4A8 GEMM's
@@ -207,9 +215,19 @@ def secondary(torch, qg, dev, rotate_mb):
     rows = []
     built = {}
     for (name, fmt, K, N, M) in SECONDARY:
-        key = (fmt, K, N)
+        key = (fmt, K, N, name if fmt == 6 else "")
         if key not in built:
-            if fmt == 4:
+            if fmt == 6:
+                gs0, zeros, act = W4G_VARIANTS[name]
+                gs = gs0 or K
+                p = gen.w4g_problem(128, K, N, gs, zeros, act, seed=0)
+                sc = torch.from_numpy(p["scales"].view(np.int16)).to(dev)
+                zt = None if p["zeros"] is None else torch.from_numpy(p["zeros"]).to(dev)
+                blob = qg.repack_w4g(torch.from_numpy(p["codes"].view(np.int32)).to(dev), sc, zt, gs)
+                A = torch.from_numpy(p["A"].view(np.int16)).to(dev)
+                A = A.view(torch.float16) if act == "fp16" else A.view(torch.bfloat16)
+                extra = {"gs": gs, "zeros": zeros}
+            elif fmt == 4:
                 A = torch.from_numpy(gen.w4a16_problem(128, K, 128, seed=0, weights=False)["A"]).to(dev)
                 blob, extra = None, {}
             elif fmt == 1:
@@ -240,9 +258,11 @@ def secondary(torch, qg, dev, rotate_mb):
                 built = {key: (([blob] + [blob.clone() for _ in range(reps - 1)]), A, extra)}
         blobs, A_all, extra = built[key]
         A = A_all[:M].contiguous()
-        C = torch.empty((M, max(N, 1)), dtype=torch.float16, device=dev)
+        C = torch.empty((M, max(N, 1)), dtype=A.dtype if fmt == 6 else torch.float16, device=dev)
         ws = qg.Workspace()
-        if fmt == 1:
+        if fmt == 6:
+            run = lambda b: qg.w4g(A, b, K, N, extra["gs"], extra["zeros"], out=C, workspace=ws)
+        elif fmt == 1:
             run = lambda b: qg.w4a16(A, b, K, N, out=C, workspace=ws)
         elif fmt == 2:
             a_s = extra["a_scale"][:M].contiguous()
@@ -277,12 +297,13 @@ def secondary(torch, qg, dev, rotate_mb):
         b.record(stream)
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (5 * n)
-        byt, ops = secondary_bytes_ops(fmt, K, N, M, extra.get("n4", 0))
+        byt, ops = secondary_bytes_ops(fmt, K, N, M, extra.get("n4", 0), extra.get("gs", 128),
+                                       extra.get("zeros", False))
         peak = INT8_PEAK_TOPS if fmt in (2, 5) else FP16_PEAK_TFLOPS
         gbs = byt / (us * 1e-6) / 1e9
         tops = ops / (us * 1e-6) / 1e12
         roof_us = max(byt / (HBM_PEAK_GBS * 1e9), ops / (peak * 1e12)) * 1e6
-        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4", "quant_a8", "w4a8_fp16"][fmt],
+        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4", "quant_a8", "w4a8_fp16", "w4g"][fmt],
                      "K": K, "N": N, "M": M,
                      "us": round(us, 2), "tops": round(tops, 2), "gbs": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline_frac": round(roof_us / us, 4),

@@ -16,12 +16,16 @@ __all__ = [
     "FMT_W4A16", "FMT_W4A8", "FMT_W2W4", "QgemmError", "lib", "lib_path", "packed_bytes",
     "workspace_bytes", "plan", "set_plan_override", "repack", "repack_w4a16", "repack_w4a8",
     "repack_w2w4", "w4a16", "w4a8", "w2w4_mixed", "Workspace", "EXPORTED_SYMBOLS", "quantize_a8",
-    "w4a8_fp16",
+    "w4a8_fp16", "FMT_W4G", "DT_F16", "DT_BF16", "packed_bytes_w4g", "workspace_bytes_w4g",
+    "repack_w4g", "w4g",
 ]
 
 FMT_W4A16 = 1
 FMT_W4A8 = 2
 FMT_W2W4 = 3
+FMT_W4G = 4
+DT_F16 = 1
+DT_BF16 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqgemm.so")
@@ -30,7 +34,8 @@ _lib = None
 EXPORTED_SYMBOLS = (
     "qgemm_status_str", "qgemm_last_error", "qgemm_version", "qgemm_packed_bytes",
     "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16", "qgemm_w4a8", "qgemm_w2w4_mixed",
-    "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8",
+    "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8", "qgemm_w4g_packed_bytes",
+    "qgemm_w4g_workspace_bytes", "qgemm_w4g_repack", "qgemm_w4g",
 )
 
 
@@ -66,9 +71,15 @@ def lib() -> ctypes.CDLL:
         L.qgemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
         L.qgemm_set_plan_override.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.qgemm_quantize_a8.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+        i32 = ctypes.c_int32
+        L.qgemm_w4g_packed_bytes.argtypes = [i64, i64, i32, i32, u64p]
+        L.qgemm_w4g_workspace_bytes.argtypes = [i64, i64, i64, u64p]
+        L.qgemm_w4g_repack.argtypes = [i64, i64, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.qgemm_w4g.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
-                     "qgemm_quantize_a8"):
+                     "qgemm_quantize_a8", "qgemm_w4g_packed_bytes", "qgemm_w4g_workspace_bytes",
+                     "qgemm_w4g_repack", "qgemm_w4g"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -266,3 +277,51 @@ def w4a8_fp16(A, blob, K: int, N: int, out=None, acc_out=None, workspace: Worksp
     int8 x int4 GEMM (two launches on the current stream)."""
     A_q, a_s = quantize_a8(A)
     return w4a8(A_q, a_s, blob, K, N, out=out, acc_out=acc_out, workspace=workspace)
+
+
+# ----------------------------------------------------------------------------- general grid
+def packed_bytes_w4g(K: int, N: int, group_size: int, has_zeros: bool) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qgemm_w4g_packed_bytes(K, N, group_size, int(bool(has_zeros)), ctypes.byref(out)),
+           "qgemm_w4g_packed_bytes")
+    return out.value
+
+
+def workspace_bytes_w4g(M: int, K: int, N: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qgemm_w4g_workspace_bytes(M, K, N, ctypes.byref(out)), "qgemm_w4g_workspace_bytes")
+    return out.value
+
+
+def repack_w4g(codes, scales, zeros, group_size: int):
+    """codes: int32 [K/8][N]; scales: fp16 or bf16 (any 16-bit dtype) [K/gs][N];
+    zeros: uint8 [K/gs][N] or None (implicit zero point 8)."""
+    torch = _torch()
+    _require_cuda(codes, scales, zeros)
+    K, N = codes.shape[0] * 8, codes.shape[1]
+    nbytes = packed_bytes_w4g(K, N, group_size, zeros is not None)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib().qgemm_w4g_repack(K, N, group_size, _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(out),
+                                  nbytes, _stream_ptr(codes.device)), "qgemm_w4g_repack")
+    return out
+
+
+def w4g(A, blob, K: int, N: int, group_size: int, has_zeros: bool, out=None,
+        workspace: Workspace | None = None):
+    """General-grid 4-bit GEMM; A fp16 or bf16 [M][K] (sets the activation,
+    scale and output type); returns C of A's dtype."""
+    torch = _torch()
+    _require_cuda(A, blob)
+    if A.dtype == torch.float16:
+        dt = DT_F16
+    elif A.dtype == torch.bfloat16:
+        dt = DT_BF16
+    else:
+        raise ValueError("A must be float16 or bfloat16")
+    M = A.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    ws, wsb = (workspace or _default_ws).get(workspace_bytes_w4g(M, K, N), A.device)
+    _check(lib().qgemm_w4g(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K, N, group_size,
+                           int(bool(has_zeros)), dt, _ptr(ws), wsb, _stream_ptr(A.device)), "qgemm_w4g")
+    return out

@@ -51,6 +51,11 @@ int check_kn(int fmt, int64_t K, int64_t N) {
   return QGEMM_OK;
 }
 
+// General grid: 64, or a multiple of 128 dividing K (K itself: one group per column).
+bool valid_group_size(int64_t K, int64_t gs) {
+  return gs == 64 || (gs > 0 && gs % qg::kGroup == 0 && K % gs == 0);
+}
+
 // The current device must be a gfx950 GPU; cached per device ordinal.
 int check_device() {
   int dev = 0;
@@ -118,6 +123,19 @@ BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4) {
     L.high = L.scales + align256((size_t)L.NB * L.G8 * 256);
     L.total = L.high + align256((size_t)n4 * 32);
   }
+  return L;
+}
+
+BlobLayout blob_layout_w4g(int64_t K, int64_t N, int gs, bool zeros) {
+  BlobLayout L;
+  L.K = K;
+  L.N = N;
+  L.G = K / kGroup;
+  L.NB = N / 16;
+  L.G8 = (L.G + 7) / 8;
+  L.codes = 0;
+  L.scales = align256((size_t)(L.NB * L.G) * 1024);
+  L.total = L.scales + align256((size_t)(K / gs) * (size_t)N * (zeros ? 4 : 2));
   return L;
 }
 
@@ -214,7 +232,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
       if (kp > G) continue;
       // 1024-thread workgroups leave 128 VGPRs per wave: these tiles would spill
       if (kp == 4 && !force_wpt && nb == 2 &&
-          (fmt == QGEMM_FMT_W2W4 || (fmt == QGEMM_FMT_W4A8 && pl.mb == 2)))
+          (fmt == QGEMM_FMT_W2W4 || ((fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W4G) && pl.mb == 2)))
         continue;
       const int smax = tiles > kMaxCounters ? 1 : std::min(G, 64);
       for (int s0 = 1; s0 <= smax; ++s0) {
@@ -228,7 +246,8 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
         c.wpt = 4 * kp;
         c.gps = gps;
         const size_t lds = fmt == QGEMM_FMT_W4A16 ? lds_bytes_w4a16(c, G)
-                           : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G) : lds_bytes_w2w4(c, G);
+                           : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G)
+                           : fmt == QGEMM_FMT_W4G  ? lds_bytes_w4g(c, G) : lds_bytes_w2w4(c, G);
         if (lds > 160 * 1024) continue;
         const int64_t wgs = tiles * s;
         const int64_t waves = wgs * 4 * kp;
@@ -333,7 +352,7 @@ int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* byte
 }
 
 int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10) {
-  if (!valid_fmt(fmt)) return QGEMM_ERR_FORMAT;
+  if (!valid_fmt(fmt) && fmt != QGEMM_FMT_W4G) return QGEMM_ERR_FORMAT;
   if (!out10) return QGEMM_ERR_NULL;
   int st = check_kn(fmt, K, N);
   if (st) return st;
@@ -437,10 +456,13 @@ struct GemmCall {
   void* ws;
   size_t ws_bytes;
   void* stream;
+  int gs = qg::kGroup;    // general grid only
+  bool zeros = false;
+  bool bf16 = false;
 };
 
 int run_gemm(const GemmCall& g) {
-  if (!valid_fmt(g.fmt)) return QGEMM_ERR_FORMAT;
+  if (!valid_fmt(g.fmt) && g.fmt != QGEMM_FMT_W4G) return QGEMM_ERR_FORMAT;
   int st = check_kn(g.fmt, g.K, g.N);
   if (st) return st;
   if (g.M < 0 || g.M > kMaxM) return QGEMM_ERR_SHAPE;
@@ -460,7 +482,8 @@ int run_gemm(const GemmCall& g) {
     if (!aligned(g.ws, 16)) return QGEMM_ERR_ALIGN;
   }
   // the fixed-size part of the blob (everything before a mixed blob's high plane)
-  const qg::BlobLayout L = qg::blob_layout(g.fmt, g.K, g.N, 0);
+  const qg::BlobLayout L = g.fmt == QGEMM_FMT_W4G ? qg::blob_layout_w4g(g.K, g.N, g.gs, g.zeros)
+                                                   : qg::blob_layout(g.fmt, g.K, g.N, 0);
   const size_t blob_fixed = g.fmt == QGEMM_FMT_W2W4 ? L.high : L.total;
   const size_t c_bytes = (size_t)((g.M - 1) * g.ldc + g.N) * 2;
   const size_t a_bytes = (size_t)((g.M - 1) * g.lda + g.K) * aelt;
@@ -497,6 +520,7 @@ int run_gemm(const GemmCall& g) {
   a.gps = pl.gps;
   a.mt = pl.mt;
   a.nt = pl.nt;
+  a.gs = g.gs;
   if (pl.ws_bytes) {
     a.counters = static_cast<uint32_t*>(g.ws);
     a.partial = static_cast<char*>(g.ws) + pl.counter_bytes;
@@ -505,6 +529,7 @@ int run_gemm(const GemmCall& g) {
   hipError_t e;
   if (g.fmt == QGEMM_FMT_W4A16) e = pl.kernel == 2 ? qg::launch_w4a16_wide(pl, a, s) : qg::launch_w4a16(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4A8) e = qg::launch_w4a8(pl, a, s);
+  else if (g.fmt == QGEMM_FMT_W4G) e = qg::launch_w4g(pl, a, g.bf16, g.zeros, s);
   else e = qg::launch_w2w4(pl, a, s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return QGEMM_OK;
@@ -532,6 +557,63 @@ int qgemm_w2w4_mixed(const void* A, int64_t lda, const void* packed, void* C, in
                      void* stream) {
   return run_gemm({QGEMM_FMT_W2W4, A, lda, nullptr, packed, C, ldc, nullptr, M, K, N, workspace,
                    workspace_bytes, stream});
+}
+
+int qgemm_w4g_packed_bytes(int64_t K, int64_t N, int32_t group_size, int32_t has_zeros,
+                           size_t* bytes) {
+  if (!bytes) return QGEMM_ERR_NULL;
+  int st = check_kn(QGEMM_FMT_W4G, K, N);
+  if (st) return st;
+  if (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1)) return QGEMM_ERR_RANGE;
+  *bytes = qg::blob_layout_w4g(K, N, group_size, has_zeros != 0).total;
+  return QGEMM_OK;
+}
+
+int qgemm_w4g_workspace_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
+  if (!bytes) return QGEMM_ERR_NULL;
+  int st = check_kn(QGEMM_FMT_W4G, K, N);
+  if (st) return st;
+  if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
+  *bytes = M == 0 ? 0 : qg::make_plan(QGEMM_FMT_W4G, M, K, N).ws_bytes;
+  return QGEMM_OK;
+}
+
+int qgemm_w4g_repack(int64_t K, int64_t N, int32_t group_size, const void* codes, const void* scales,
+                     const void* zeros, void* packed, size_t packed_bytes, void* stream) {
+  if (!codes || !scales || !packed) return QGEMM_ERR_NULL;
+  int st = check_kn(QGEMM_FMT_W4G, K, N);
+  if (st) return st;
+  if (!valid_group_size(K, group_size)) return QGEMM_ERR_RANGE;
+  const qg::BlobLayout L = qg::blob_layout_w4g(K, N, group_size, zeros != nullptr);
+  if (packed_bytes != L.total) return QGEMM_ERR_SIZE;
+  if (!aligned(packed, 16) || !aligned(codes, 4) || !aligned(scales, 2)) return QGEMM_ERR_ALIGN;
+  const size_t ng = (size_t)(K / group_size) * (size_t)N;
+  if (overlap(packed, L.total, codes, (size_t)(K / 2 * N)) || overlap(packed, L.total, scales, ng * 2) ||
+      overlap(packed, L.total, zeros, zeros ? ng : 0))
+    return QGEMM_ERR_ALIAS;
+  st = check_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = qg::launch_zero_fill(packed, L.total, s);
+  if (e != hipSuccess) return hip_fail(e, "zero fill");
+  e = qg::launch_repack_w4g(L, group_size, codes, scales, zeros, packed, s);
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  return QGEMM_OK;
+}
+
+int qgemm_w4g(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M,
+              int64_t K, int64_t N, int32_t group_size, int32_t has_zeros, int32_t act_dtype,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (check_kn(QGEMM_FMT_W4G, K, N) == QGEMM_OK &&
+      (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1) ||
+       (act_dtype != QGEMM_DT_F16 && act_dtype != QGEMM_DT_BF16)))
+    return QGEMM_ERR_RANGE;
+  GemmCall g{QGEMM_FMT_W4G, A, lda, nullptr, packed, C, ldc, nullptr, M, K, N, workspace,
+             workspace_bytes, stream};
+  g.gs = group_size;
+  g.zeros = has_zeros != 0;
+  g.bf16 = act_dtype == QGEMM_DT_BF16;
+  return run_gemm(g);
 }
 
 int qgemm_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* A_q, int64_t ldq,

@@ -46,6 +46,9 @@ __device__ __forceinline__ void store16_coherent(f32x4 v, rsrc_t r, uint32_t vof
 
 // v_and_or_b32 with the mask in an SGPR and the OR operand in a VGPR: one VALU
 // op (gfx9 VOP3 cannot carry two literal constants, so plain C++ would split it).
+// Its result must reach an MFMA only through a compiler-generated instruction:
+// the compiler does not count inline asm as a VALU write when it inserts the
+// wait states an MFMA operand needs after one.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(orv));

@@ -72,15 +72,18 @@ struct GemmArgs {
   int64_t lda, ldc;
   int M, K, N, G, G8;
   int splits, gps, mt, nt;
+  int gs;                 // general-grid format: k per quantization group
 };
 
 size_t lds_bytes_w4a16(const Plan& pl, int G);
 size_t lds_bytes_w4a8(const Plan& pl, int G);
 size_t lds_bytes_w2w4(const Plan& pl, int G);
+size_t lds_bytes_w4g(const Plan& pl, int G);
 hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);
+hipError_t launch_w4g(const Plan& pl, const GemmArgs& a, bool bf16, bool zeros, hipStream_t s);
 
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* Q, int64_t ldq,
@@ -89,6 +92,12 @@ hipError_t launch_repack_w4a16(const BlobLayout& L, const void* codes, const voi
                                void* packed, hipStream_t s);
 hipError_t launch_repack_w4a8(const BlobLayout& L, const void* codes, const void* gscales,
                               const void* cscales, void* packed, hipStream_t s);
+// General-grid blob: W4A16 codes, then one entry per (group, column) in the
+// scales region (see repack.hip); Gs = K / gs groups, P = 2 entries per 128-k
+// chunk when gs = 64, else 1.
+BlobLayout blob_layout_w4g(int64_t K, int64_t N, int gs, bool zeros);
+hipError_t launch_repack_w4g(const BlobLayout& L, int gs, const void* codes, const void* scales,
+                             const void* zeros, void* packed, hipStream_t s);
 // desc (already uploaded into the blob's descriptor region) gives the high-plane slots.
 hipError_t launch_repack_w2w4(const BlobLayout& L, const void* codes, const void* scales,
                               void* packed, hipStream_t s);

@@ -32,6 +32,12 @@
 //  W2W4 desc   : per chunk (b, g), at index g*NB + b: u32 off, u32 mask16 (bit c =
 //                column 16b + c is a 4-bit group; off = 4-bit groups in all
 //                earlier chunks of that order).
+//  W4G codes   : as W4A16 (128-k chunks whatever the group length gs).
+//  W4G entries : one per (group g = k / gs, column n): the 16-bit scale pattern
+//                (fp16 or bf16), or with stored zero points a u32 = scale bits |
+//                zero << 16; entry (g, n) at index ((g / P)*N + n)*P + g % P with
+//                P = 2 for gs = 64 (the two groups of a 128-k chunk adjacent)
+//                and P = 1 otherwise.
 //  W2W4 high   : per 4-bit group, 32 B at 32*(off + rank(c)), quarter h at +8h,
 //                the upper 2 code bits in the base-plane arrangement.
 #include "qgemm_device.h"
@@ -137,6 +143,17 @@ __global__ void repack_w2w4_kernel(const uint8_t* __restrict__ codes, const u32x
   }
 }
 
+// One thread per (group, column) entry of the general-grid format.
+__global__ void repack_w4g_entries(const uint16_t* __restrict__ s, const uint8_t* __restrict__ z,
+                                   void* __restrict__ out, int N, int P, int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int64_t g = tid / N, n = tid % N;
+  const int64_t dst = ((g / P) * N + n) * P + g % P;
+  if (z) static_cast<uint32_t*>(out)[dst] = (uint32_t)s[tid] | ((uint32_t)(z[tid] & 0xF) << 16);
+  else static_cast<uint16_t*>(out)[dst] = s[tid];
+}
+
 __global__ void zero_fill16(u32x4* __restrict__ dst, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
@@ -168,6 +185,22 @@ hipError_t launch_repack_w4a16(const BlobLayout& L, const void* codes, const voi
   hipLaunchKernelGGL((repack_scales<uint16_t>), dim3(grid_for(ns, 256)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(scales), reinterpret_cast<uint16_t*>(out + L.scales),
                      (int)L.G, (int)L.G8, (int)L.N, ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_w4g(const BlobLayout& L, int gs, const void* codes, const void* scales,
+                             const void* zeros, void* packed, hipStream_t s) {
+  char* out = static_cast<char*>(packed);
+  const int64_t nc = L.NB * L.G * 64;
+  hipLaunchKernelGGL((repack_codes_u4<false>), dim3(grid_for(nc, 256)), dim3(256), 0, s,
+                     static_cast<const uint32_t*>(codes), reinterpret_cast<uint32_t*>(out + L.codes),
+                     (int)L.G, (int)L.N, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ne = (L.K / gs) * L.N;
+  hipLaunchKernelGGL(repack_w4g_entries, dim3(grid_for(ne, 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(scales), static_cast<const uint8_t*>(zeros),
+                     static_cast<void*>(out + L.scales), (int)L.N, gs == 64 ? 2 : 1, ne);
   return hipGetLastError();
 }
 

@@ -1,0 +1,234 @@
+// 4-bit weights on a general quantization grid, on the streaming driver:
+//   C[M,N] = A[M,K] * W[K,N],  W[k,n] = (q[k,n] - z[g,n]) * s[g,n],  g = k / gs,
+// with gs = 64 or a multiple of 128 dividing K (gs = K: one scale per column),
+// z a stored 4-bit zero point per (group, column) or the implicit 8, and
+// activations, scales and output all fp16 or all bf16. The 2-bit page's
+// abstract and the Atom review's method section quantize weights by groups
+// without fixing the group length; asymmetric grids store a zero point per
+// group.
+//
+// The codes are the W4A16 blob's 128-k chunks; each lane loads, with its 16 B
+// of codes, the grid entries of its column for the chunk: the two 64-k groups
+// of the chunk when gs = 64, else the one group that contains it. Every chunk
+// is treated as two 64-k halves (k-steps 0-1 and 2-3 of the 16x16x32 MFMA),
+// each with its own partial sum and grid entry; for gs >= 128 both halves use
+// the same entry. Applying a group's scale per chunk is exact regrouping of
+// the same sum, so k-splits and K-parts need not align with gs.
+//
+//   fp16: the magic-exponent trick gives 1024 + q (and 1024 + 16 q) exactly;
+//         one packed add of -(1024 + z) (or fma with 1/16 and -(64 + z)) with
+//         the lane's own zero point gives q - z exactly, so the B operand is
+//         exact and each half's fp32 partial is scaled once: acc += s * part.
+//   bf16: gfx950 has no packed bf16 add, so B is 128 + q (bit pattern
+//         0x4300 | q, exact: the bf16 ulp at 128 is 1), and the zero point is
+//         removed after the MFMA with the half's row sums of A, obtained from
+//         one extra MFMA of A against ones per 16-row block and k-step:
+//             acc += s * (sum_k a (128 + q) - (128 + z) * sum_k a).
+//         Products of two bf16 values are exact in fp32; the subtraction
+//         cancels at most a factor ~20 of magnitude, far inside fp32.
+#include "skinny.h"
+
+namespace qg {
+namespace fmt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <bool kBF16, bool kZ>
+struct PolicyW4G : Tile16 {
+  using Acc = f32x4;
+  using Elem = float;
+  static constexpr int kScaleChunk = 0;
+  static constexpr int kFrag = 4;           // A fragments (16 rows x 32 k) per chunk
+  static constexpr int kAElem = 2;
+  static constexpr bool kStageScales = false;
+  static constexpr uint32_t kEntry = kZ ? 4u : 2u;   // bytes per grid entry
+  __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
+    return a_voff16<kFrag>(fr, lane, rows, arow);
+  }
+
+  struct Consts {
+    uint32_t magic = kBF16 ? 0x43004300u : 0x64006400u;
+  };
+
+  template <int NBW>
+  struct Stage {
+    static constexpr int kVmem = 2 * NBW;   // codes + grid entries per column block
+    u32x4 code[NBW];
+    u32x2 e[NBW];                           // entries of the chunk's two 64-k halves
+  };
+
+  __host__ __device__ static int extra_lds(int, int) { return 0; }
+  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
+
+  template <int NBW>
+  struct View {
+    rsrc_t rc, re;
+    uint32_t cvoff, gstep, evoff, rowb;
+    int gw0, cpg;     // chunks per group (0 for gs = 64)
+
+    __device__ View(const GemmArgs& p, const char*, const SkinnyLds&, const TileInfo&, int bw,
+                    int gw0_, int nload, int lane)
+        : gw0(gw0_) {
+      const uint32_t nbt = (uint32_t)(p.N / 16);
+      gstep = nbt * 1024u;
+      cvoff = lane * 16u;
+      rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)gw0 * nbt + bw) * 1024,
+                     (uint32_t)(nload - 1) * gstep + NBW * 1024u);
+      cpg = p.gs == 64 ? 0 : p.gs / 128;
+      const uint32_t per = cpg ? 1u : 2u;                 // entries per (row, column)
+      rowb = (uint32_t)p.N * per * kEntry;                // bytes per entry row
+      evoff = (uint32_t)(bw * 16 + (lane & 15)) * per * kEntry;
+      re = make_rsrc(p.scales, (uint32_t)(p.K / (cpg ? p.gs : 64)) * (uint32_t)p.N * kEntry);
+    }
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+      const int g = gw0 + rel;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * 1024u + rel * gstep);
+      // wave-uniform: one load per block either way
+      if (cpg == 0) {
+        const uint32_t soff = (uint32_t)g * rowb;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const uint32_t vo = evoff + j * 16u * 2u * kEntry;
+          if (kZ) {
+            st.e[j] = load8(re, vo, soff);
+          } else {
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(re, vo, soff, 0);
+            st.e[j] = u32x2{w & 0xFFFFu, w >> 16};
+          }
+        }
+      } else {
+        const uint32_t soff = (uint32_t)(g / cpg) * rowb;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const uint32_t vo = evoff + j * 16u * kEntry;
+          const uint32_t w = kZ ? __builtin_amdgcn_raw_buffer_load_b32(re, vo, soff, 0)
+                                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(re, vo, soff, 0);
+          st.e[j] = u32x2{w, w};
+        }
+      }
+    }
+    __device__ __forceinline__ void load_lds(Stage<NBW>&, int) const {}
+  };
+
+  __device__ static float scale_of(uint32_t e) {
+    const uint32_t s16 = e & 0xFFFFu;
+    return kBF16 ? __builtin_bit_cast(float, s16 << 16) : (float)as_h2(s16)[0];
+  }
+  __device__ static uint32_t zero_of(uint32_t e) { return kZ ? (e >> 16) & 0xFu : 8u; }
+
+  template <int MB, int NBW>
+  __device__ __forceinline__ static void compute(const Stage<NBW>& cur, const char* aslot, Acc (&acc)[MB][NBW],
+                                                 bool valid, const Consts& k, int lane) {
+    u32x4 a[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[mb][t] = *reinterpret_cast<const u32x4*>(aslot + (mb * 4 + t) * 1024 + lane * 16);
+    if constexpr (!kBF16) {
+      const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        f16x8 bf[4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint32_t z = zero_of(cur.e[j][hf]);
+          const uint32_t zz = z | (z << 16);
+          const f16x2 lo_off = as_h2(zz | 0xE400E400u);            // -(1024 + z)
+          const f16x2 hi_off = as_h2((zz << 4) | 0xD400D400u);     // -(64 + z)
+#pragma unroll
+          for (int t = 2 * hf; t < 2 * hf + 2; ++t) {
+            const uint32_t w = cur.code[j][t], w8 = w >> 8;
+            const f16x2 p0 = as_h2(and_or(w, 0x000F000Fu, k.magic)) + lo_off;
+            const f16x2 p1 = __builtin_elementwise_fma(as_h2(and_or(w, 0x00F000F0u, k.magic)), sixteenth, hi_off);
+            const f16x2 p2 = as_h2(and_or(w8, 0x000F000Fu, k.magic)) + lo_off;
+            const f16x2 p3 = __builtin_elementwise_fma(as_h2(and_or(w8, 0x00F000F0u, k.magic)), sixteenth, hi_off);
+            bf[t] = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          }
+        }
+        const float s0 = valid ? scale_of(cur.e[j][0]) : 0.f;
+        const float s1 = valid ? scale_of(cur.e[j][1]) : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][0]), bf[0], p0, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][1]), bf[1], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][2]), bf[2], p1, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][3]), bf[3], p1, 0, 0, 0);
+          acc[mb][j] += s0 * p0 + s1 * p1;
+        }
+      }
+    } else {
+      // row sums of A per 64-k half, once for all column blocks
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      f32x4 r0[MB], r1[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        r0[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        r1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        r0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][0]), ones, r0[mb], 0, 0, 0);
+        r0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][1]), ones, r0[mb], 0, 0, 0);
+        r1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][2]), ones, r1[mb], 0, 0, 0);
+        r1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][3]), ones, r1[mb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        bf16x8 bf[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = cur.code[j][t];
+          // pairs (nibble i, nibble i + 4) land in k order: sigma-ordered words.
+          // Plain C++ here, not the inline-asm and_or: these registers feed the
+          // MFMA directly, and the compiler inserts the wait states an MFMA
+          // operand needs after a VALU write only for instructions it generated.
+          constexpr uint32_t m = 0x000F000Fu;
+          const u32x4 b = {(w & m) | k.magic, ((w >> 4) & m) | k.magic, ((w >> 8) & m) | k.magic,
+                           ((w >> 12) & m) | k.magic};
+          bf[t] = __builtin_bit_cast(bf16x8, b);
+        }
+        const float s0 = valid ? scale_of(cur.e[j][0]) : 0.f;
+        const float s1 = valid ? scale_of(cur.e[j][1]) : 0.f;
+        const float c0 = (float)(128u + zero_of(cur.e[j][0]));
+        const float c1 = (float)(128u + zero_of(cur.e[j][1]));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][0]), bf[0], p0, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][1]), bf[1], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][2]), bf[2], p1, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][3]), bf[3], p1, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[mb][j][i] += s0 * (p0[i] - c0 * r0[mb][i]) + s1 * (p1[i] - c1 * r1[mb][i]);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void store(const GemmArgs& p, int row, int col, float v) {
+    if constexpr (kBF16) {
+      const __bf16 h = (__bf16)v;   // round to nearest even
+      static_cast<uint16_t*>(p.C)[(size_t)row * p.ldc + col] = __builtin_bit_cast(uint16_t, h);
+    } else {
+      static_cast<f16*>(p.C)[(size_t)row * p.ldc + col] = (f16)v;
+    }
+  }
+};
+
+}  // namespace fmt
+
+using namespace fmt;
+
+size_t lds_bytes_w4g(const Plan& pl, int G) {
+  // the LDS layout does not depend on the grid variant
+  return skinny_lds_bytes<PolicyW4G<false, false>>(pl, G);
+}
+
+hipError_t launch_w4g(const Plan& pl, const GemmArgs& a, bool bf16, bool zeros, hipStream_t s) {
+  if (bf16) {
+    return zeros ? dispatch_skinny<PolicyW4G<true, true>>(pl, a, s) : dispatch_skinny<PolicyW4G<true, false>>(pl, a, s);
+  }
+  return zeros ? dispatch_skinny<PolicyW4G<false, true>>(pl, a, s) : dispatch_skinny<PolicyW4G<false, false>>(pl, a, s);
+}
+
+}  // namespace qg

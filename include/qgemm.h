@@ -5,7 +5,8 @@
  * batches (M = 1..128 is the design range; larger M is accepted), the
  * mixed-precision auto-regressive linear layer of the MARLIN paper (abstract:
  * weights compressed to about 4 bits per element, batched decode with 1..128
- * parallel clients, memory-bound up to batch 16..32). Three weight formats:
+ * parallel clients, memory-bound up to batch 16..32). Three weight formats,
+ * and a general-grid 4-bit variant (qgemm_w4g, below):
  *
  *   W4A16  fp16 activations; unsigned 4-bit codes q (0..15) with an implicit
  *          zero point 8 and one fp16 scale s per group of 128 consecutive k of
@@ -66,8 +67,15 @@ typedef enum qgemm_status {
 typedef enum qgemm_fmt {
   QGEMM_FMT_W4A16 = 1,
   QGEMM_FMT_W4A8 = 2,
-  QGEMM_FMT_W2W4 = 3
+  QGEMM_FMT_W2W4 = 3,
+  QGEMM_FMT_W4G = 4   /* general grid: only through the qgemm_w4g_* entry points */
 } qgemm_fmt;
+
+/* Activation (and scale, output) type of the general-grid 4-bit GEMM. */
+typedef enum qgemm_dtype {
+  QGEMM_DT_F16 = 1,   /* IEEE binary16 */
+  QGEMM_DT_BF16 = 2   /* bfloat16 (upper half of binary32) */
+} qgemm_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* qgemm_status_str(int status);
@@ -179,11 +187,49 @@ int qgemm_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* A_
                       void* a_scale, void* stream);
 
 /*
+ * 4-bit weights on a general quantization grid. The 2-bit page's abstract and
+ * the Atom review's method section quantize weights by groups without fixing
+ * the group length, and asymmetric grids keep a zero point per group:
+ *
+ *   W[k,n] = (q[k,n] - z[g,n]) * s[g,n],  g = k / group_size,
+ *
+ * with unsigned 4-bit codes q, group_size 64 or a multiple of 128 that divides
+ * K (group_size == K gives one scale per column), z a stored zero point 0..15
+ * per (group, column) or, without stored zero points, the constant 8, and
+ * activations A, scales s and output C all of one type (act_dtype,
+ * QGEMM_DT_F16 or QGEMM_DT_BF16). Accumulation is fp32; each output is
+ * rounded once (to nearest even) to act_dtype. Shapes and alignment as for
+ * qgemm_w4a16; an invalid group_size or act_dtype is QGEMM_ERR_RANGE.
+ *
+ * qgemm_w4g_packed_bytes: blob size (has_zeros 0 or 1).
+ * qgemm_w4g_workspace_bytes: workspace for a call of this shape (same
+ *   contract as qgemm_workspace_bytes).
+ * qgemm_w4g_repack: codes uint32[K/8][N] (as W4A16), scales 16-bit
+ *   [K/group_size][N] in the activation type (copied bit for bit), zeros
+ *   uint8[K/group_size][N] or NULL (implicit 8; only the low 4 bits of each
+ *   stored value are used). packed must hold exactly qgemm_w4g_packed_bytes()
+ *   bytes with has_zeros = (zeros != NULL). Asynchronous on `stream`.
+ * qgemm_w4g: the GEMM; group_size and has_zeros must be those the blob was
+ *   repacked with (they are not recorded in it), act_dtype the type of A, of
+ *   the scales given to the repack and of C (C is act_dtype[M][ldc]).
+ */
+int qgemm_w4g_packed_bytes(int64_t K, int64_t N, int32_t group_size, int32_t has_zeros,
+                           size_t* bytes);
+int qgemm_w4g_workspace_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes);
+int qgemm_w4g_repack(int64_t K, int64_t N, int32_t group_size, const void* codes,
+                     const void* scales, const void* zeros, void* packed, size_t packed_bytes,
+                     void* stream);
+int qgemm_w4g(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M,
+              int64_t K, int64_t N, int32_t group_size, int32_t has_zeros, int32_t act_dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Work decomposition used for a call of this shape (for tests and tuning).
  * Fills out10[0..9] = {kernel id (1 streaming, 2 wide), 16-row blocks per tile
  * (per wave for kernel 2), 16-column blocks per wave, waves per workgroup,
  * k-splits across workgroups, groups per k-split, m-tiles, n-tiles,
- * workgroups, waves}. Host-only; no HIP call.
+ * workgroups, waves}. fmt may also be QGEMM_FMT_W4G (the plan does not depend
+ * on its grid). Host-only; no HIP call.
  */
 int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 

@@ -151,7 +151,7 @@ def test_repack_validation_without_gpu(L):
     assert L.qgemm_repack(1, K, N, codes, sc, None, None, _fake(0x10000000 + 4096), nb, None) == ERR_ALIAS
 
 
-def _check_plan(p, M, K, N):
+def _check_plan(p, M, K, N, ws=None):
     G = K // 128
     if p["kernel"] == 2:
         assert p["mb"] == 4 and p["nb"] == 4 and p["wpt"] == 8
@@ -183,7 +183,8 @@ def _check_plan(p, M, K, N):
             if g1 > g0:
                 cover[g0:g1] += 1
     assert np.all(cover == 1)
-    ws = qg.workspace_bytes(qg.FMT_W4A16, M, K, N)
+    if ws is None:
+        ws = qg.workspace_bytes(qg.FMT_W4A16, M, K, N)
     if p["splits"] == 1:
         assert ws == 0
     else:
@@ -241,3 +242,49 @@ def test_binding_needs_built_library_and_no_cpu_path():
     import inspect
     src = inspect.getsource(qg)
     assert "oracle" not in src and "numpy.matmul" not in src and "torch.matmul" not in src
+
+
+# --------------------------------------------------------------------------- general grid
+@pytest.mark.parametrize("K,N,gs", [(1024, 1024, 64), (1024, 1024, 128), (1024, 1024, 1024),
+                                    (4096, 11008, 256), (11008, 4096, 11008), (384, 64, 384)])
+@pytest.mark.parametrize("zeros", [False, True])
+def test_w4g_packed_bytes_match_independent_layout(K, N, gs, zeros):
+    assert qg.packed_bytes_w4g(K, N, gs, zeros) == layout.packed_bytes_w4g(K, N, gs, zeros)
+
+
+def test_w4g_validation_without_gpu(L):
+    out = ctypes.c_size_t(0)
+    K, N = 1024, 1024
+    for gs in (0, 32, 96, 192, 2048, -128):
+        assert L.qgemm_w4g_packed_bytes(K, N, gs, 0, ctypes.byref(out)) == ERR_RANGE, gs
+    assert L.qgemm_w4g_packed_bytes(K, N, 128, 2, ctypes.byref(out)) == ERR_RANGE
+    assert L.qgemm_w4g_packed_bytes(K, 96, 128, 0, ctypes.byref(out)) == ERR_SHAPE
+    assert L.qgemm_w4g_packed_bytes(K, N, 128, 0, None) == ERR_NULL
+    nb = qg.packed_bytes_w4g(K, N, 64, True)
+    codes, sc, z, blob = _fake(0x10000000), _fake(0x20000000), _fake(0x28000000), _fake(0x30000000)
+    assert L.qgemm_w4g_repack(K, N, 64, None, sc, z, blob, nb, None) == ERR_NULL
+    assert L.qgemm_w4g_repack(K, N, 96, codes, sc, z, blob, nb, None) == ERR_RANGE
+    assert L.qgemm_w4g_repack(K, N, 64, codes, sc, None, blob, nb, None) == ERR_SIZE   # blob sized for zeros
+    assert L.qgemm_w4g_repack(K, N, 64, codes, _fake(0x20000001), z, blob, nb, None) == ERR_ALIGN
+    assert L.qgemm_w4g_repack(K, N, 64, codes, sc, _fake(0x30000000 + 512), blob, nb, None) == ERR_ALIAS
+    A, P, C, W = _fake(0x10000000), _fake(0x20000000), _fake(0x30000000), _fake(0x40000000)
+    M = 16
+    ws = qg.workspace_bytes_w4g(M, K, N)
+    assert L.qgemm_w4g(None, K, None, None, N, 0, K, N, 128, 0, 1, None, 0, None) == OK
+    assert L.qgemm_w4g(A, K, P, C, N, M, K, N, 96, 0, 1, W, ws, None) == ERR_RANGE
+    assert L.qgemm_w4g(A, K, P, C, N, M, K, N, 128, 3, 1, W, ws, None) == ERR_RANGE
+    assert L.qgemm_w4g(A, K, P, C, N, M, K, N, 128, 0, 3, W, ws, None) == ERR_RANGE
+    assert L.qgemm_w4g(A, K, P, C, N, M, 1000, N, 128, 0, 1, W, ws, None) == ERR_SHAPE
+    assert L.qgemm_w4g(None, K, P, C, N, M, K, N, 128, 0, 2, W, ws, None) == ERR_NULL
+    assert L.qgemm_w4g(A, K, P, _fake(0x10000000 + 256), N, M, K, N, 64, 1, 2, W, ws, None) == ERR_ALIAS
+    st = L.qgemm_w4g(A, K, P, C, N, M, K, N, 64, 1, 2, W, ws, None)
+    if st != OK:
+        assert st in (ERR_HIP, ERR_DEV)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 11008), (11008, 4096), (1024, 1024), (8192, 28672)])
+@pytest.mark.parametrize("M", [1, 16, 32, 64, 128])
+def test_w4g_plan_covers_every_unit_once(K, N, M):
+    p = qg.plan(qg.FMT_W4G, M, K, N)
+    assert p["kernel"] == 1
+    _check_plan(p, M, K, N, ws=qg.workspace_bytes_w4g(M, K, N))

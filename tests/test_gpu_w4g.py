@@ -1,0 +1,180 @@
+"""GPU parity of the general-grid 4-bit GEMM (group length 64 / 128 / ... / K,
+stored zero points, fp16 or bf16 activations) against the CPU oracle, through
+the C ABI.
+
+Bars: repacked blobs byte-identical to the independent layout oracle; one-hot
+activations reproduce round((q - z) * s) bit-exactly in the activation type
+(the kernel forms the exact integer q - z and multiplies by s once in fp32);
+codes equal to their zero points give exactly zero (fp16; bf16 up to the fp32
+rounding of its post-MFMA zero-point removal); every other output within
+the fp16 rule (max|e| <= 2e-3 sqrt(K) rms(C_ref), rel. Frobenius <= 1e-3) or
+the bf16 rule (same max term plus 2^-8 max|C_ref|, rel. Frobenius <= 4e-3).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_quantized_qgemm_amd as qg
+from oracle import compare, layout, ref
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ACTS = ["fp16", "bf16"]
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _t(x, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(DEV)
+
+
+def _act_t(x, act):
+    return _t(x) if act == "fp16" else _t(x.view(np.int16), torch.bfloat16)
+
+
+def _upload(p):
+    s = _t(p["scales"]) if p["act"] == "fp16" else _t(p["scales"].view(np.int16))
+    z = None if p["zeros"] is None else _t(p["zeros"])
+    return qg.repack_w4g(_t(p["codes"].view(np.int32)), s, z, p["group_size"])
+
+
+def _run(p, A=None, M=None):
+    A = p["A"] if A is None else A
+    C = qg.w4g(_act_t(A, p["act"]), _upload(p), p["K"], p["N"], p["group_size"], p["zeros"] is not None)
+    return C.cpu().view(torch.int16).numpy().view(np.uint16) if p["act"] == "bf16" else C.cpu().numpy()
+
+
+def _ok(C_gpu, C_ref, K, act, what):
+    r = compare.check_fp16(C_gpu, C_ref, K) if act == "fp16" else compare.check_bf16(C_gpu, C_ref, K)
+    assert r["ok"], (what, r)
+    return r
+
+
+@pytest.fixture(autouse=True)
+def _reset_plan():
+    qg.set_plan_override()
+    yield
+    qg.set_plan_override()
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("K,N,gs,zeros", [(128, 64, 64, True), (1152, 320, 128, True), (1152, 320, 384, False),
+                                          (1024, 1024, 64, False), (4096, 11008, 4096, True)])
+def test_repack_w4g_bytes(K, N, gs, zeros, act):
+    _say("repack w4g", K, N, gs, zeros, act)
+    p = gen.w4g_problem(1, K, N, gs, zeros, act, seed=K ^ N, activations=False)
+    blob = _upload(p).cpu().numpy().tobytes()
+    assert blob == layout.blob_w4g(p["codes"], p["scales"], p["zeros"], gs, act)
+
+
+def _one_hot(M, K, rng, act):
+    ks = rng.choice(K, size=M, replace=False)
+    A = np.zeros((M, K), dtype=np.float16 if act == "fp16" else np.uint16)
+    A[np.arange(M), ks] = 1.0 if act == "fp16" else 0x3F80
+    return A, ks
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("gs,zeros,M,K,N,force", [(64, True, 16, 1024, 512, None), (128, True, 5, 2048, 256, (1, 8, 2)),
+                                                  (256, False, 32, 1024, 384, (2, 16, 1)),
+                                                  (1024, True, 20, 1024, 128, (2, 4, 3)),
+                                                  (64, False, 33, 512, 256, None)])
+def test_w4g_one_hot_bit_exact(act, gs, zeros, M, K, N, force):
+    _say("w4g one-hot", act, gs, zeros, M, K, N, force)
+    rng = np.random.default_rng(M * 7 + K + gs)
+    p = gen.w4g_problem(1, K, N, gs, zeros, act, seed=M + K, activations=False)
+    A, ks = _one_hot(M, K, rng, act)
+    if force:
+        qg.set_plan_override(*force)
+    C = _run(p, A)
+    q = ref.unpack_u4(p["codes"])
+    z = 8 if p["zeros"] is None else p["zeros"][ks // gs].astype(np.int64)
+    w = (q[ks] - z).astype(np.float64) * ref.act_to_f64(p["scales"], act)[ks // gs]
+    if act == "fp16":
+        expect = w.astype(np.float16).view(np.uint16)
+        assert np.array_equal(C.view(np.uint16), expect)
+    else:
+        expect = gen.to_bf16_bits(w.astype(np.float32))   # (q - z) * s is exact in fp32
+        assert np.array_equal(C, expect)
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("gs", [64, 128, 512])
+def test_w4g_codes_at_zero_points_give_zero(act, gs):
+    _say("w4g zero", act, gs)
+    K, N, M = 1024, 256, 9
+    p = gen.w4g_problem(M, K, N, gs, True, act, seed=5)
+    q = np.repeat(p["zeros"], gs, axis=0)
+    p = dict(p, codes=gen.pack_nibbles_u32(q))
+    C = _run(p)
+    if act == "fp16":
+        # B = q - z is exactly zero
+        assert np.all(C.view(np.uint16) & 0x7FFF == 0)   # +0 or -0
+    else:
+        # bf16 removes the zero point after the MFMA: sum a (128 + z) - (128 + z) sum a
+        # cancels up to fp32 rounding of the two sums (~1e-5 here, against rms(C) ~ 1)
+        assert np.abs(ref.bf16_to_f64(C)).max() < 1e-3
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("gs,zeros", [(64, False), (64, True), (128, True), (256, True), (2048, False), (2048, True)])
+@pytest.mark.parametrize("M", [1, 7, 16, 33])
+def test_w4g_gemm(act, gs, zeros, M):
+    K, N = 2048, 512
+    _say("w4g gemm", act, gs, zeros, M)
+    p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=M + gs)
+    C = _run(p)
+    _ok(C, ref.gemm_w4g(p["A"], p["codes"], p["scales"], p["zeros"], gs, act), K, act, (gs, zeros, M))
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("force", [(1, 4, 1), (2, 8, 2), (2, 16, 1), (1, 4, 5), (2, 4, 7)])
+def test_w4g_forced_splits(act, force):
+    K, N, M, gs = 4096, 1024, 20, 64
+    _say("w4g forced", act, force)
+    p = gen.w4g_problem(M, K, N, gs, True, act, seed=13)
+    qg.set_plan_override(*force)
+    blob = _upload(p)
+    A = _act_t(p["A"], act)
+    C1 = qg.w4g(A, blob, K, N, gs, True)
+    C2 = qg.w4g(A, blob, K, N, gs, True)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    C = C1.cpu().view(torch.int16).numpy().view(np.uint16) if act == "bf16" else C1.cpu().numpy()
+    _ok(C, ref.gemm_w4g(p["A"], p["codes"], p["scales"], p["zeros"], gs, act), K, act, force)
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("gs,zeros", [(128, True), (64, False), (11008, True)])
+def test_w4g_7b_layer(act, gs, zeros):
+    K, N, M = 11008, 4096, 16
+    _say("w4g 7b", act, gs, zeros)
+    p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=21)
+    C = _run(p)
+    _ok(C, ref.gemm_w4g(p["A"], p["codes"], p["scales"], p["zeros"], gs, act), K, act, (gs, zeros))
+
+
+def test_w4g_matches_w4a16_on_its_grid():
+    # group 128 with stored zero points 8, fp16: the W4A16 GEMM within tolerance
+    K, N, M = 4096, 1024, 16
+    _say("w4g vs w4a16")
+    p = gen.w4a16_problem(M, K, N, seed=3)
+    blob16 = qg.repack_w4a16(_t(p["codes"].view(np.int32)), _t(p["scales"]))
+    C16 = qg.w4a16(_t(p["A"]), blob16, K, N).cpu().numpy()
+    blobg = qg.repack_w4g(_t(p["codes"].view(np.int32)), _t(p["scales"]),
+                          _t(np.full((K // 128, N), 8, np.uint8)), 128)
+    Cg = qg.w4g(_t(p["A"]), blobg, K, N, 128, True).cpu().numpy()
+    C_ref = ref.gemm_w4a16(p["A"], p["codes"], p["scales"])
+    _ok(Cg, C_ref, K, "fp16", "w4g")
+    _ok(C16, C_ref, K, "fp16", "w4a16")
