@@ -11,7 +11,9 @@ fails loudly if its HIP build is missing.
                         OdysseyLLM abstract (W4A8) and the 2-bit page's mixed
                         2/4-bit groups; the 4-bit GEMM on a general grid
                         (group length 64 .. K, stored zero points, fp16 or bf16
-                        activations); plus the per-token dynamic int8
+                        activations); the 2:4 structure check of sparse
+                        W4A16 (whose GEMM is the W4A16 definition on the
+                        dense codes); plus the per-token dynamic int8
                         activation quantization that feeds W4A8.
 * ``oracle.layout``  -- an independent implementation of the repacked weight
                         blob byte layout, for byte-exact checks of the GPU repack.

@@ -58,6 +58,22 @@ activations and scales)
           P = 1 otherwise, entry (g, n) sits at index ((g // P)*N + n)*P + g % P,
           so the entries of the two 64-k groups of one 128-k chunk of a column
           are adjacent.
+
+W4A16 2:4 sparse (format 5: at most two nonzero weights, i.e. codes other
+than 8, in every 4 consecutive k of a column)
+  codes   G*NB chunks of 512 B, chunk (b, g) at (g*NB + b)*512. Lane l owns
+          8 B at +8*l: words s = 0, 1 (64-k steps). Word s covers
+          k = 128*g + 64*s + 16*h + 4*j + p (quads j = 0..3, positions p = 0..3)
+          of column n = 16*b + c; each quad keeps two positions p0 < p1 (the
+          positions of its codes other than 8, completed with the lowest other
+          positions); kept value v = 2*j + i (i = 0 for p0, 1 for p1) sits in
+          nibble sigma(v) (the W4A16 nibble order).
+  meta    G*NB chunks of 256 B, chunk (b, g) at (g*NB + b)*256; lane l owns the
+          u32 at +4*l: bits 16*s + 2*v .. +1 = the position p of kept value v
+          of word s.
+  scales  as W4A16.
+  status  256 B; u32 at +0 = number of quads that break the 2:4 structure
+          (0 for a valid blob), the rest zero.
 """
 
 from __future__ import annotations
@@ -70,6 +86,7 @@ FMT_W4A16 = 1
 FMT_W4A8 = 2
 FMT_W2W4 = 3
 FMT_W4G = 4
+FMT_SP24 = 5
 
 
 def _align256(x: int) -> int:
@@ -148,6 +165,8 @@ def packed_bytes(fmt: int, K: int, N: int, n4: int = 0) -> int:
     if fmt == FMT_W2W4:
         return (_align256(NB * G * 512) + _align256(NB * G * 8) + _align256(NB * G8 * 256)
                 + _align256(32 * n4))
+    if fmt == FMT_SP24:
+        return _align256(NB * G * 512) + _align256(NB * G * 256) + _align256(NB * G8 * 256) + 256
     raise ValueError("unknown format")
 
 
@@ -171,6 +190,45 @@ def blob_w4a16(qw: np.ndarray, scales: np.ndarray) -> bytes:
                  _align256(NB * ((G + 7) // 8) * 256))
     out = codes + sc
     assert len(out) == packed_bytes(FMT_W4A16, K, N)
+    return out
+
+
+# --------------------------------------------------------------------------- 2:4 sparse
+def blob_sp24(qw: np.ndarray, scales: np.ndarray) -> bytes:
+    """Blob of format 5 from dense canonical codes (pruned weights hold code 8)
+    and fp16 scales [K/128][N]. Raises ValueError if a quad keeps more than two
+    codes other than 8."""
+    qw = np.asarray(qw, dtype=np.uint32)
+    K, N = qw.shape[0] * 8, qw.shape[1]
+    _check_shape(K, N)
+    G, NB = K // GROUP, N // 16
+    q = _unpack_nibbles(qw).astype(np.int64)                      # [K][N]
+    # [g][s][h][j][p][b][c] with k = 128g + 64s + 16h + 4j + p, n = 16b + c
+    x = q.reshape(G, 2, 4, 4, 4, NB, 16)
+    nz = x != 8
+    if (nz.sum(axis=4) > 2).any():
+        raise ValueError("codes break the 2:4 structure")
+    # kept positions per quad: nonzero positions first, then the lowest others,
+    # sorted ascending (a stable sort of the key "zero?" then position)
+    key = (~nz).astype(np.int64) * 4 + np.arange(4).reshape(1, 1, 1, 1, 4, 1, 1)
+    order = np.argsort(key, axis=4, kind="stable")[:, :, :, :, :2]
+    pos = np.sort(order, axis=4)                                   # [g][s][h][j][2][b][c]
+    vals = np.take_along_axis(x, pos, axis=4)
+    # to [g][b][h][c][s][v = 2j + i]
+    vals = vals.transpose(0, 5, 2, 6, 1, 3, 4).reshape(G, NB, 4, 16, 2, 8)
+    pos = pos.transpose(0, 5, 2, 6, 1, 3, 4).reshape(G, NB, 4, 16, 2, 8)
+    words = np.zeros((G, NB, 4, 16, 2), dtype=np.uint32)
+    meta = np.zeros((G, NB, 4, 16), dtype=np.uint32)
+    for v in range(8):
+        words |= vals[..., v].astype(np.uint32) << np.uint32(4 * _sigma(v))
+        for st in range(2):
+            meta |= pos[..., st, v].astype(np.uint32) << np.uint32(16 * st + 2 * v)
+    codes = _pad_to(words.reshape(G, NB, 64, 2).astype("<u4").tobytes(), _align256(NB * G * 512))
+    metab = _pad_to(meta.reshape(G, NB, 64).astype("<u4").tobytes(), _align256(NB * G * 256))
+    sc = _pad_to(_scale_region(np.asarray(scales, dtype=np.float16), G, N, np.float16),
+                 _align256(NB * ((G + 7) // 8) * 256))
+    out = codes + metab + sc + bytes(256)
+    assert len(out) == packed_bytes(FMT_SP24, K, N)
     return out
 
 

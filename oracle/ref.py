@@ -88,6 +88,21 @@ def gemm_w4a16(A: np.ndarray, qw: np.ndarray, scales: np.ndarray,
     return C
 
 
+# --------------------------------------------------------------------------- 2:4 sparse W4A16
+def sparse24_violations(qw: np.ndarray, zero: int = 8) -> int:
+    """Number of runs of 4 consecutive k of one column (k = 4j .. 4j+3) holding
+    more than two nonzero weights, i.e. more than two codes other than the
+    zero point. The MARLIN abstract extends its kernel to 2:4 sparsity: at most
+    two of every four consecutive weights along K are nonzero. Such weights are
+    an ordinary W4A16 matrix whose pruned entries hold the zero point, so the
+    2:4 GEMM's value is ``gemm_w4a16`` on the dense codes; this function checks
+    the structure the sparse kernel relies on."""
+    q = unpack_u4(qw)
+    K, N = q.shape
+    nz = (q != zero).reshape(K // 4, 4, N).sum(axis=1)
+    return int((nz > 2).sum())
+
+
 # --------------------------------------------------------------------------- W4 general grid
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """bfloat16 values given as their 16-bit patterns -> fp64 (exact).

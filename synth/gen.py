@@ -31,6 +31,7 @@ _KIND_W4A16 = 1
 _KIND_W4A8 = 2
 _KIND_W2W4 = 3
 _KIND_W4G = 4
+_KIND_SP24 = 5
 
 
 def rng_for(seed: int, *tags: int) -> np.random.Generator:
@@ -196,4 +197,32 @@ def w4g_problem(M: int, K: int, N: int, group_size: int = 128, zeros: bool = Fal
         out["scales"] = cvt(rng_for(seed, *tag, 2, K, N).uniform(0.005, 0.02, size=(G, N)).astype(np.float32))
         out["zeros"] = (rng_for(seed, *tag, 3, K, N).integers(0, 16, size=(G, N), dtype=np.uint8)
                         if zeros else None)
+    return out
+
+
+def w4a16_sp24_problem(M: int, K: int, N: int, seed: int = 0, weights: bool = True,
+                       activations: bool = True) -> dict:
+    """2:4 structured-sparse W4A16 workload (the MARLIN abstract's sparse
+    extension): fp16 A ~ N(0,1); in every run of 4 consecutive k of a column
+    two positions, chosen uniformly among the 6 pairs, keep a uint4 code uniform
+    in 0..15, and the other two hold the zero point 8 (weight exactly 0); fp16
+    scales uniform in [0.005, 0.02] per (group of 128 k, column). Codes are
+    returned dense, in the W4A16 canonical packing."""
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 128")
+    out = {"M": M, "K": K, "N": N, "zero": 8}
+    if activations:
+        out["A"] = _fp16_normal(rng_for(seed, _KIND_SP24, 0, M, K), (M, K))
+    if weights:
+        r = rng_for(seed, _KIND_SP24, 1, K, N)
+        pairs = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)])
+        choice = r.integers(0, 6, size=(K // 4, N))
+        kept = np.zeros((K // 4, 4, N), dtype=bool)
+        jj, nn = np.meshgrid(np.arange(K // 4), np.arange(N), indexing="ij")
+        kept[jj, pairs[choice, 0], nn] = True
+        kept[jj, pairs[choice, 1], nn] = True
+        vals = r.integers(0, 16, size=(K // 4, 4, N), dtype=np.uint8)
+        q = np.where(kept, vals, np.uint8(8)).reshape(K, N)
+        out["codes"] = pack_nibbles_u32(q)
+        out["scales"] = _fp16_uniform(rng_for(seed, _KIND_SP24, 2, K, N), 0.005, 0.02, (K // GROUP, N))
     return out
