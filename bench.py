@@ -178,6 +178,7 @@ SECONDARY = (
     + [("mixed 2/4-bit", 3, 4096, 4096, M) for M in (1, 16, 64)]
     + [("per-token int8 quantization", 4, 4096, 0, M) for M in (16, 64, 128)]
     + [("w4a8 from fp16 (quantize + GEMM)", 5, 4096, 11008, M) for M in (16, 64, 128)]
+    + [("w4a16 2:4 sparse", 7, K, N, M) for (K, N) in [(8192, 28672), (4096, 11008)] for M in (1, 16, 64)]
     + [(name, 6, 4096, 11008, M) for name in ("w4g g64 fp16", "w4g g128 zeros fp16", "w4g per-channel fp16",
                                               "w4g g128 bf16", "w4g g128 zeros bf16") for M in (1, 16)]
 )
@@ -190,6 +191,8 @@ W4G_VARIANTS = {"w4g g64 fp16": (64, False, "fp16"), "w4g g128 zeros fp16": (128
 def secondary_bytes_ops(fmt, K, N, M, n4=0, gs=128, zeros=False):
     """Algorithmic bytes and ops of one launch (codes, scales, A, C)."""
     G = K // 128
+    if fmt == 7:   # kept codes (half the weights x 4 bits) + 2-bit positions + scales, A, C
+        return K * N // 4 + K * N // 8 + G * N * 2 + 2 * M * K + 2 * M * N, alg_flops(M, K, N)
     if fmt == 6:   # codes, one 2-byte scale (4 with a zero point) per group, A, C
         return K * N // 2 + (K // gs) * N * (4 if zeros else 2) + 2 * M * K + 2 * M * N, alg_flops(M, K, N)
     if fmt == 4:   # read fp16 A, write int8 codes and fp16 scales
@@ -217,7 +220,13 @@ def secondary(torch, qg, dev, rotate_mb):
     for (name, fmt, K, N, M) in SECONDARY:
         key = (fmt, K, N, name if fmt == 6 else "")
         if key not in built:
-            if fmt == 6:
+            if fmt == 7:
+                p = gen.w4a16_sp24_problem(128, K, N, seed=0)
+                blob = qg.repack_sp24(torch.from_numpy(p["codes"].view(np.int32)).to(dev),
+                                      torch.from_numpy(p["scales"]).to(dev))
+                A = torch.from_numpy(p["A"]).to(dev)
+                extra = {}
+            elif fmt == 6:
                 gs0, zeros, act = W4G_VARIANTS[name]
                 gs = gs0 or K
                 p = gen.w4g_problem(128, K, N, gs, zeros, act, seed=0)
@@ -260,7 +269,9 @@ def secondary(torch, qg, dev, rotate_mb):
         A = A_all[:M].contiguous()
         C = torch.empty((M, max(N, 1)), dtype=A.dtype if fmt == 6 else torch.float16, device=dev)
         ws = qg.Workspace()
-        if fmt == 6:
+        if fmt == 7:
+            run = lambda b: qg.w4a16_sp24(A, b, K, N, out=C, workspace=ws)
+        elif fmt == 6:
             run = lambda b: qg.w4g(A, b, K, N, extra["gs"], extra["zeros"], out=C, workspace=ws)
         elif fmt == 1:
             run = lambda b: qg.w4a16(A, b, K, N, out=C, workspace=ws)
@@ -303,7 +314,7 @@ def secondary(torch, qg, dev, rotate_mb):
         gbs = byt / (us * 1e-6) / 1e9
         tops = ops / (us * 1e-6) / 1e12
         roof_us = max(byt / (HBM_PEAK_GBS * 1e9), ops / (peak * 1e12)) * 1e6
-        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4", "quant_a8", "w4a8_fp16", "w4g"][fmt],
+        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4", "quant_a8", "w4a8_fp16", "w4g", "w4a16_sp24"][fmt],
                      "K": K, "N": N, "M": M,
                      "us": round(us, 2), "tops": round(tops, 2), "gbs": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline_frac": round(roof_us / us, 4),

@@ -17,13 +17,14 @@ __all__ = [
     "workspace_bytes", "plan", "set_plan_override", "repack", "repack_w4a16", "repack_w4a8",
     "repack_w2w4", "w4a16", "w4a8", "w2w4_mixed", "Workspace", "EXPORTED_SYMBOLS", "quantize_a8",
     "w4a8_fp16", "FMT_W4G", "DT_F16", "DT_BF16", "packed_bytes_w4g", "workspace_bytes_w4g",
-    "repack_w4g", "w4g",
+    "repack_w4g", "w4g", "FMT_W4A16_SP24", "repack_sp24", "w4a16_sp24",
 ]
 
 FMT_W4A16 = 1
 FMT_W4A8 = 2
 FMT_W2W4 = 3
 FMT_W4G = 4
+FMT_W4A16_SP24 = 5
 DT_F16 = 1
 DT_BF16 = 2
 
@@ -35,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "qgemm_status_str", "qgemm_last_error", "qgemm_version", "qgemm_packed_bytes",
     "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16", "qgemm_w4a8", "qgemm_w2w4_mixed",
     "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8", "qgemm_w4g_packed_bytes",
-    "qgemm_w4g_workspace_bytes", "qgemm_w4g_repack", "qgemm_w4g",
+    "qgemm_w4g_workspace_bytes", "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24",
 )
 
 
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.qgemm_w4a16.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.qgemm_w4a8.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.qgemm_w2w4_mixed.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
+        L.qgemm_w4a16_sp24.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, ctypes.c_size_t, vp]
         L.qgemm_plan.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
         L.qgemm_set_plan_override.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.qgemm_quantize_a8.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
@@ -79,7 +81,7 @@ def lib() -> ctypes.CDLL:
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
                      "qgemm_quantize_a8", "qgemm_w4g_packed_bytes", "qgemm_w4g_workspace_bytes",
-                     "qgemm_w4g_repack", "qgemm_w4g"):
+                     "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -242,6 +244,24 @@ def w4a8(A_i8, a_scale, blob, K: int, N: int, out=None, acc_out=None,
     _check(lib().qgemm_w4a8(_ptr(A_i8), A_i8.stride(0), _ptr(a_scale), _ptr(blob), _ptr(out),
                             out.stride(0), _ptr(acc_out), M, K, N, _ptr(ws), wsb,
                             _stream_ptr(A_i8.device)), "qgemm_w4a8")
+    return out
+
+
+def repack_sp24(codes, scales):
+    """codes: int32 [K/8][N] dense W4A16 codes with pruned weights = 8 (at most two
+    other codes in every 4 consecutive k of a column), scales: fp16 [K/128][N]."""
+    K, N = codes.shape[0] * 8, codes.shape[1]
+    return repack(FMT_W4A16_SP24, K, N, codes, scales)
+
+
+def w4a16_sp24(A, blob, K: int, N: int, out=None, workspace: Workspace | None = None):
+    """C = A @ dequant(W) with a 2:4 sparse W4A16 blob; A fp16 [M][K] on the GPU."""
+    _require_cuda(A, blob)
+    M = A.shape[0]
+    out = _gemm_out(M, N, A.device, out)
+    ws, wsb = (workspace or _default_ws).get(workspace_bytes(FMT_W4A16_SP24, M, K, N), A.device)
+    _check(lib().qgemm_w4a16_sp24(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K, N,
+                                  _ptr(ws), wsb, _stream_ptr(A.device)), "qgemm_w4a16_sp24")
     return out
 
 

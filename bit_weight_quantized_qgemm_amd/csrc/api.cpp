@@ -41,7 +41,9 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-bool valid_fmt(int fmt) { return fmt == QGEMM_FMT_W4A16 || fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W2W4; }
+bool valid_fmt(int fmt) {
+  return fmt == QGEMM_FMT_W4A16 || fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W2W4 || fmt == QGEMM_FMT_W4A16_SP24;
+}
 
 int check_kn(int fmt, int64_t K, int64_t N) {
   if (K <= 0 || K % qg::kGroup != 0 || K > kMaxKN) return QGEMM_ERR_SHAPE;
@@ -116,6 +118,11 @@ BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4) {
     L.scales = align256(chunks * 1024);
     L.aux = L.scales + align256((size_t)L.NB * L.G8 * 128);
     L.total = L.aux + align256((size_t)N * 2);
+  } else if (fmt == QGEMM_FMT_W4A16_SP24) {
+    L.codes = 0;
+    L.scales = align256(chunks * 768);
+    L.high = L.scales + align256((size_t)L.NB * L.G8 * 256);
+    L.total = L.high + 256;
   } else {
     L.codes = 0;
     L.aux = align256(chunks * 512);
@@ -205,7 +212,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
   const int force_nb = g_force_nb.load();
   const int force_wpt = g_force_wpt.load();
   const int force_splits = g_force_splits.load();
-  const double chunk = fmt == QGEMM_FMT_W2W4 ? 560.0 : 1024.0;   // streamed bytes per 16 x 128 chunk
+  const double chunk = fmt == QGEMM_FMT_W2W4 ? 560.0 : fmt == QGEMM_FMT_W4A16_SP24 ? 768.0 : 1024.0;   // streamed bytes per 16 x 128 chunk
   const double blob = (double)G * (double)(N / 16) * chunk;
   const double inflight_target = std::min(8.0 * 1048576.0, blob / 2);
   const int pref_nb = M > 4 ? 2 : 1;
@@ -247,7 +254,8 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
         c.gps = gps;
         const size_t lds = fmt == QGEMM_FMT_W4A16 ? lds_bytes_w4a16(c, G)
                            : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G)
-                           : fmt == QGEMM_FMT_W4G  ? lds_bytes_w4g(c, G) : lds_bytes_w2w4(c, G);
+                           : fmt == QGEMM_FMT_W4G  ? lds_bytes_w4g(c, G)
+                           : fmt == QGEMM_FMT_W4A16_SP24 ? lds_bytes_sp24(c, G) : lds_bytes_w2w4(c, G);
         if (lds > 160 * 1024) continue;
         const int64_t wgs = tiles * s;
         const int64_t waves = wgs * 4 * kp;
@@ -412,6 +420,19 @@ int qgemm_repack(int fmt, int64_t K, int64_t N, const void* codes, const void* g
   if (e != hipSuccess) return hip_fail(e, "zero fill");
   if (fmt == QGEMM_FMT_W4A16) {
     e = qg::launch_repack_w4a16(L, codes, group_scales, packed, s);
+  } else if (fmt == QGEMM_FMT_W4A16_SP24) {
+    e = qg::launch_repack_sp24(L, codes, group_scales, packed, s);
+    if (e != hipSuccess) return hip_fail(e, "repack launch");
+    // the structure check: the kernel counted quads with more than two nonzero codes
+    uint32_t bad = 0;
+    e = hipMemcpyAsync(&bad, static_cast<char*>(packed) + L.high, 4, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    if (bad != 0) {
+      g_last_error = std::to_string(bad) + " runs of 4 consecutive k hold more than two nonzero codes";
+      return QGEMM_ERR_RANGE;
+    }
   } else if (fmt == QGEMM_FMT_W4A8) {
     e = qg::launch_repack_w4a8(L, codes, group_scales, chan_scales, packed, s);
   } else {
@@ -530,6 +551,7 @@ int run_gemm(const GemmCall& g) {
   if (g.fmt == QGEMM_FMT_W4A16) e = pl.kernel == 2 ? qg::launch_w4a16_wide(pl, a, s) : qg::launch_w4a16(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4A8) e = qg::launch_w4a8(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4G) e = qg::launch_w4g(pl, a, g.bf16, g.zeros, s);
+  else if (g.fmt == QGEMM_FMT_W4A16_SP24) e = qg::launch_sp24(pl, a, s);
   else e = qg::launch_w2w4(pl, a, s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return QGEMM_OK;
@@ -549,6 +571,12 @@ int qgemm_w4a8(const void* A, int64_t lda, const void* a_scale, const void* pack
                int64_t ldc, int32_t* acc_out, int64_t M, int64_t K, int64_t N, void* workspace,
                size_t workspace_bytes, void* stream) {
   return run_gemm({QGEMM_FMT_W4A8, A, lda, a_scale, packed, C, ldc, acc_out, M, K, N, workspace,
+                   workspace_bytes, stream});
+}
+
+int qgemm_w4a16_sp24(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M,
+                     int64_t K, int64_t N, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_gemm({QGEMM_FMT_W4A16_SP24, A, lda, nullptr, packed, C, ldc, nullptr, M, K, N, workspace,
                    workspace_bytes, stream});
 }
 

@@ -30,7 +30,7 @@ struct BlobLayout {
   size_t codes = 0;    // W4A16/W4A8 1 KB chunks; W2W4 512 B base chunks
   size_t scales = 0;   // fp16 (W4A16, W2W4) or int8 (W4A8) group scales
   size_t aux = 0;      // W4A8: fp16 channel scales; W2W4: per-chunk descriptors
-  size_t high = 0;     // W2W4: 4-bit high plane
+  size_t high = 0;     // W2W4: 4-bit high plane; SP24: status word
   size_t total = 0;
 };
 
@@ -79,11 +79,13 @@ size_t lds_bytes_w4a16(const Plan& pl, int G);
 size_t lds_bytes_w4a8(const Plan& pl, int G);
 size_t lds_bytes_w2w4(const Plan& pl, int G);
 size_t lds_bytes_w4g(const Plan& pl, int G);
+size_t lds_bytes_sp24(const Plan& pl, int G);
 hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4g(const Plan& pl, const GemmArgs& a, bool bf16, bool zeros, hipStream_t s);
+hipError_t launch_sp24(const Plan& pl, const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* Q, int64_t ldq,
@@ -96,6 +98,9 @@ hipError_t launch_repack_w4a8(const BlobLayout& L, const void* codes, const void
 // scales region (see repack.hip); Gs = K / gs groups, P = 2 entries per 128-k
 // chunk when gs = 64, else 1.
 BlobLayout blob_layout_w4g(int64_t K, int64_t N, int gs, bool zeros);
+// 2:4 sparse W4A16: 768-byte chunks of kept codes and positions, scales, status word (high).
+hipError_t launch_repack_sp24(const BlobLayout& L, const void* codes, const void* scales, void* packed,
+                              hipStream_t s);
 hipError_t launch_repack_w4g(const BlobLayout& L, int gs, const void* codes, const void* scales,
                              const void* zeros, void* packed, hipStream_t s);
 // desc (already uploaded into the blob's descriptor region) gives the high-plane slots.

@@ -38,6 +38,16 @@
 //                zero << 16; entry (g, n) at index ((g / P)*N + n)*P + g % P with
 //                P = 2 for gs = 64 (the two groups of a 128-k chunk adjacent)
 //                and P = 1 otherwise.
+//  SP24 chunks : 2:4 sparse W4A16; chunk (b, g) of 768 B at (g*NB + b)*768; lane l
+//                owns 12 B = code words s = 0, 1 (64-k steps) and a position word
+//                (one 12-byte lane load per chunk); code word s covers
+//                k = 128g + 64s + 16h + 4j + p (quads j, positions p) of column
+//                16b + c; each quad keeps two positions p0 < p1 (its codes other
+//                than 8, completed with the lowest other positions), kept value
+//                v = 2j + i in nibble sigma(v).
+//                The position word's bits 16s + 2v .. +1 hold the position of
+//                kept value v of code word s.
+//  SP24 status : u32 count of quads with more than two codes other than 8.
 //  W2W4 high   : per 4-bit group, 32 B at 32*(off + rank(c)), quarter h at +8h,
 //                the upper 2 code bits in the base-plane arrangement.
 #include "qgemm_device.h"
@@ -143,6 +153,57 @@ __global__ void repack_w2w4_kernel(const uint8_t* __restrict__ codes, const u32x
   }
 }
 
+// One thread per (chunk, lane) of the 2:4 sparse format: 16 canonical words
+// (2 steps x 16 k x ... one column) -> 2 code words and 1 position word.
+__global__ void repack_sp24_kernel(const uint32_t* __restrict__ codes, uint32_t* __restrict__ out,
+                                   uint32_t* __restrict__ status, int N, int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int lane = (int)(tid & 63);
+  const int64_t chunk = tid >> 6;
+  const int NB = N / 16;
+  const int g = (int)(chunk / NB), b = (int)(chunk % NB);
+  const int c = lane & 15, h = lane >> 4;
+  const int n = 16 * b + c;
+  u32x2 w = {0u, 0u};
+  uint32_t m = 0, bad = 0;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    // k = 128g + 64st + 16h + 0..15: canonical rows r = k / 8, two words
+    const int r0 = 16 * g + 8 * st + 2 * h;
+    const uint32_t src[2] = {codes[(size_t)r0 * N + n], codes[(size_t)(r0 + 1) * N + n]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t quad = (src[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;   // positions p at bits 4p
+      int p0 = -1, p1 = -1, cnt = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (((quad >> (4 * p)) & 0xFu) != 8u) {
+          ++cnt;
+          if (p0 < 0) p0 = p;
+          else if (p1 < 0) p1 = p;
+        }
+      }
+      if (cnt > 2) bad = 1;
+      // complete with the lowest positions not yet kept, then order
+      for (int p = 0; p < 4 && p1 < 0; ++p) {
+        if (p == p0) continue;
+        if (p0 < 0) p0 = p;
+        else p1 = p;
+      }
+      if (p0 > p1) { const int t = p0; p0 = p1; p1 = t; }
+      const int v0 = 2 * j, v1 = 2 * j + 1;
+      w[st] |= ((quad >> (4 * p0)) & 0xFu) << (4 * sigma(v0));
+      w[st] |= ((quad >> (4 * p1)) & 0xFu) << (4 * sigma(v1));
+      m |= ((uint32_t)p0 << (16 * st + 2 * v0)) | ((uint32_t)p1 << (16 * st + 2 * v1));
+    }
+  }
+  out[tid * 3] = w[0];
+  out[tid * 3 + 1] = w[1];
+  out[tid * 3 + 2] = m;
+  if (bad) __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One thread per (group, column) entry of the general-grid format.
 __global__ void repack_w4g_entries(const uint16_t* __restrict__ s, const uint8_t* __restrict__ z,
                                    void* __restrict__ out, int N, int P, int64_t total) {
@@ -179,6 +240,22 @@ hipError_t launch_repack_w4a16(const BlobLayout& L, const void* codes, const voi
   hipLaunchKernelGGL((repack_codes_u4<false>), dim3(grid_for(nc, 256)), dim3(256), 0, s,
                      static_cast<const uint32_t*>(codes), reinterpret_cast<uint32_t*>(out + L.codes),
                      (int)L.G, (int)L.N, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ns = L.NB * L.G8 * 16;
+  hipLaunchKernelGGL((repack_scales<uint16_t>), dim3(grid_for(ns, 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(scales), reinterpret_cast<uint16_t*>(out + L.scales),
+                     (int)L.G, (int)L.G8, (int)L.N, ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_sp24(const BlobLayout& L, const void* codes, const void* scales, void* packed,
+                              hipStream_t s) {
+  char* out = static_cast<char*>(packed);
+  const int64_t nc = L.NB * L.G * 64;
+  hipLaunchKernelGGL(repack_sp24_kernel, dim3(grid_for(nc, 256)), dim3(256), 0, s,
+                     static_cast<const uint32_t*>(codes), reinterpret_cast<uint32_t*>(out + L.codes),
+                     reinterpret_cast<uint32_t*>(out + L.high), (int)L.N, nc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ns = L.NB * L.G8 * 16;

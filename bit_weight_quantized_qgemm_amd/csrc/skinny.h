@@ -87,8 +87,8 @@ __device__ __forceinline__ void stage_scales(const void* scales, char* lds, int 
 }
 
 // Geometry shared by the policies built on 16 x 16 MFMA tiles: A fragment fr
-// (16 rows x one k-step) of a 16-row block, and the position of accumulator
-// element i of lane ln in fragment (mb, j) of a wave's tile.
+// (16 rows x one k-step) of a 16-row block, and the position (row_of, col_of)
+// of accumulator element i of lane ln in fragment (mb, j) of a wave's tile.
 struct Tile16 {
   template <int kFrag>
   __device__ static uint32_t a_voff16(int fr, int lane, int rows, size_t arow) {
@@ -96,7 +96,7 @@ struct Tile16 {
     return (uint32_t)((size_t)min(rb * 16 + (lane & 15), rows - 1) * arow + 64 * f + 16 * (lane >> 4));
   }
   __device__ static int row_of(int mb, int, int i, int ln) { return mb * 16 + 4 * (ln >> 4) + i; }
-  __device__ static int col_of(int, int j, int ln) { return j * 16 + (ln & 15); }
+  __device__ static int col_of(int, int j, int, int ln) { return j * 16 + (ln & 15); }
 };
 
 // LDS layout of a launch: [scales | extra | A rings (KP x 3 slots)]; the
@@ -183,12 +183,13 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
 
-  // ---- prologue. Weights run kWD groups ahead in a register ring of kWD + 1
-  // stages, activations two groups ahead in a 3-slot LDS ring. (A deeper weight
-  // ring was measured slower on MI355X: the extra registers cost occupancy.)
+  // ---- prologue. Weights run kWD = F::kWeightDepth groups ahead (2 or 5) in a
+  // register ring of kWD + 1 stages, activations two groups ahead in a 3-slot
+  // LDS ring. (For the 16-byte-per-lane formats a deeper weight ring was
+  // measured slower on MI355X: the extra registers cost occupancy.)
   // The first loads go out before the scale staging.
-  constexpr int kWD = 2, kWS = kWD + 1, kAS = 3;
-  static_assert(kWS % kAS == 0, "the unrolled body must return both rings to slot 0");
+  constexpr int kWD = F::kWeightDepth, kWS = kWD + 1, kAS = 3;
+  static_assert(kWD >= 2 && kWS % kAS == 0, "the unrolled body must return both rings to slot 0");
   auto wl = [&](int g) { return min(g, nload - 1); };
   Stage st[kWS];
 #pragma unroll
@@ -253,7 +254,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
       const int i = e & 3, ln = (e >> 2) & 63, fj = e >> 8;      // fj = (nw*MB + mb)*NBW + j
       const int j = fj % NBW, mb = (fj / NBW) % MB, w = fj / (NBW * MB);
       const int row = ti.row0 + F::row_of(mb, j, i, ln);
-      const int col = (ti.b0 + w * NBW) * 16 + F::col_of(mb, j, ln);
+      const int col = (ti.b0 + w * NBW) * 16 + F::col_of(mb, j, i, ln);
       if (row < ti.row0 + ti.rows) F::store(p, row, col, s);
     }
     return;
@@ -293,9 +294,9 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
     }
     const int ln = e4 & 63, fj = e4 >> 6;
     const int j = fj % NBW, mb = (fj / NBW) % MB, w = fj / (NBW * MB);
-    const int col = (ti.b0 + w * NBW) * 16 + F::col_of(mb, j, ln);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int col = (ti.b0 + w * NBW) * 16 + F::col_of(mb, j, i, ln);
       const int row = ti.row0 + F::row_of(mb, j, i, ln);
       if (row < ti.row0 + ti.rows) F::store(p, row, col, s[i]);
     }

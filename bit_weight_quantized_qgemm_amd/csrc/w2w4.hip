@@ -27,6 +27,7 @@ struct PolicyW2W4 : Tile16 {
   static constexpr int kFrag = 4;
   static constexpr int kAElem = 2;
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
+  static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
     return a_voff16<kFrag>(fr, lane, rows, arow);
   }

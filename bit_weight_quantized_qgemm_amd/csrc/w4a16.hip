@@ -20,6 +20,7 @@ struct PolicyW4A16 : Tile16 {
   static constexpr int kFrag = 4;           // A fragments (16 rows x 32 k) per group
   static constexpr int kAElem = 2;          // bytes per activation
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
+  static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
     return a_voff16<kFrag>(fr, lane, rows, arow);
   }
@@ -124,6 +125,7 @@ struct PolicyW4A16M32 {
   // Each lane loads its own column's group scale with the weights: staging all
   // of a tall tile's scales in LDS would cost occupancy on long K ranges.
   static constexpr bool kStageScales = false;
+  static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
 
   typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -131,7 +133,7 @@ struct PolicyW4A16M32 {
     return (uint32_t)((size_t)min(lane & 31, rows - 1) * arow + 32 * fr + 16 * (lane >> 5));
   }
   __device__ static int row_of(int mb, int j, int i, int ln) { return 8 * (mb * 2 + j) + 4 * (ln >> 5) + i; }
-  __device__ static int col_of(int, int, int ln) { return ln & 31; }
+  __device__ static int col_of(int, int, int, int ln) { return ln & 31; }
 
   using Consts = PolicyW4A16::Consts;
 

@@ -25,6 +25,7 @@ struct PolicyW4A8 : Tile16 {
   static constexpr int kFrag = 2;           // A fragments (16 rows x 64 k) per group
   static constexpr int kAElem = 1;
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
+  static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
     return a_voff16<kFrag>(fr, lane, rows, arow);
   }

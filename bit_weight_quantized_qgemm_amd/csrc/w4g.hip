@@ -41,6 +41,7 @@ struct PolicyW4G : Tile16 {
   static constexpr int kFrag = 4;           // A fragments (16 rows x 32 k) per chunk
   static constexpr int kAElem = 2;
   static constexpr bool kStageScales = false;
+  static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   static constexpr uint32_t kEntry = kZ ? 4u : 2u;   // bytes per grid entry
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
     return a_voff16<kFrag>(fr, lane, rows, arow);

@@ -21,6 +21,12 @@
  *          stored with memory alignment in mind): per group of 128 k of one
  *          column either 4-bit codes (zero 8) or 2-bit codes (zero 2), one fp16
  *          scale per group, a host bitmap marking the 4-bit groups.
+ *   W4A16_SP24  W4A16 with 2:4 structured sparsity along K (the MARLIN
+ *          abstract's sparse extension): in every run of 4 consecutive k
+ *          (k = 4j .. 4j+3) of a column at most two codes differ from the zero
+ *          point 8; the blob keeps only those two codes and their positions
+ *          (3 bits per weight with the metadata) and the GEMM runs on the gfx950
+ *          sparse matrix instruction.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers unless the name ends in _host.
@@ -68,7 +74,8 @@ typedef enum qgemm_fmt {
   QGEMM_FMT_W4A16 = 1,
   QGEMM_FMT_W4A8 = 2,
   QGEMM_FMT_W2W4 = 3,
-  QGEMM_FMT_W4G = 4   /* general grid: only through the qgemm_w4g_* entry points */
+  QGEMM_FMT_W4G = 4,  /* general grid: only through the qgemm_w4g_* entry points */
+  QGEMM_FMT_W4A16_SP24 = 5
 } qgemm_fmt;
 
 /* Activation (and scale, output) type of the general-grid 4-bit GEMM. */
@@ -127,10 +134,15 @@ int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* byte
  *                       are ignored)
  *          group_scales fp16[K/128][N]
  *          bitmap_host  HOST uint32[K/128][ceil(N/32)] (see qgemm_packed_bytes)
+ *   W4A16_SP24: codes    uint32[K/8][N] dense, as W4A16, pruned weights holding
+ *                        code 8; a run of 4 consecutive k with more than two
+ *                        other codes is QGEMM_ERR_RANGE (the repack then
+ *                        synchronizes `stream` once to read its check)
+ *          group_scales fp16[K/128][N]
  *
  * packed must hold exactly qgemm_packed_bytes() bytes (QGEMM_ERR_SIZE
  * otherwise) and must not overlap the inputs. W4A16 and W4A8 repacks are fully
- * asynchronous. The W2W4 repack uploads a small per-tile offset table computed
+ * asynchronous (W4A16_SP24: see above). The W2W4 repack uploads a small per-tile offset table computed
  * on the host from bitmap_host and synchronizes `stream` once before returning.
  */
 int qgemm_repack(int fmt, int64_t K, int64_t N, const void* codes, const void* group_scales,
@@ -158,6 +170,15 @@ int qgemm_w4a16(const void* A, int64_t lda, const void* packed, void* C, int64_t
 int qgemm_w4a8(const void* A, int64_t lda, const void* a_scale, const void* packed, void* C,
                int64_t ldc, int32_t* acc_out, int64_t M, int64_t K, int64_t N,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * 2:4 sparse W4A16 GEMM: like qgemm_w4a16 but packed is a QGEMM_FMT_W4A16_SP24
+ * blob; the result equals qgemm_w4a16's on the dense codes (pruned weights
+ * are exactly zero).
+ */
+int qgemm_w4a16_sp24(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc,
+                     int64_t M, int64_t K, int64_t N, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * Mixed 2/4-bit GEMM: like qgemm_w4a16 but packed is a QGEMM_FMT_W2W4 blob; each

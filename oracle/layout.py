@@ -61,16 +61,16 @@ activations and scales)
 
 W4A16 2:4 sparse (format 5: at most two nonzero weights, i.e. codes other
 than 8, in every 4 consecutive k of a column)
-  codes   G*NB chunks of 512 B, chunk (b, g) at (g*NB + b)*512. Lane l owns
-          8 B at +8*l: words s = 0, 1 (64-k steps). Word s covers
+  chunks  G*NB chunks of 768 B, chunk (b, g) at (g*NB + b)*768. Lane l owns
+          12 B at +12*l: code words s = 0, 1 (64-k steps), then its position
+          word. Code word s covers
           k = 128*g + 64*s + 16*h + 4*j + p (quads j = 0..3, positions p = 0..3)
           of column n = 16*b + c; each quad keeps two positions p0 < p1 (the
           positions of its codes other than 8, completed with the lowest other
           positions); kept value v = 2*j + i (i = 0 for p0, 1 for p1) sits in
           nibble sigma(v) (the W4A16 nibble order).
-  meta    G*NB chunks of 256 B, chunk (b, g) at (g*NB + b)*256; lane l owns the
-          u32 at +4*l: bits 16*s + 2*v .. +1 = the position p of kept value v
-          of word s.
+          The position word's bits 16*s + 2*v .. +1 hold the position p of
+          kept value v of code word s.
   scales  as W4A16.
   status  256 B; u32 at +0 = number of quads that break the 2:4 structure
           (0 for a valid blob), the rest zero.
@@ -166,7 +166,7 @@ def packed_bytes(fmt: int, K: int, N: int, n4: int = 0) -> int:
         return (_align256(NB * G * 512) + _align256(NB * G * 8) + _align256(NB * G8 * 256)
                 + _align256(32 * n4))
     if fmt == FMT_SP24:
-        return _align256(NB * G * 512) + _align256(NB * G * 256) + _align256(NB * G8 * 256) + 256
+        return _align256(NB * G * 768) + _align256(NB * G8 * 256) + 256
     raise ValueError("unknown format")
 
 
@@ -223,11 +223,11 @@ def blob_sp24(qw: np.ndarray, scales: np.ndarray) -> bytes:
         words |= vals[..., v].astype(np.uint32) << np.uint32(4 * _sigma(v))
         for st in range(2):
             meta |= pos[..., st, v].astype(np.uint32) << np.uint32(16 * st + 2 * v)
-    codes = _pad_to(words.reshape(G, NB, 64, 2).astype("<u4").tobytes(), _align256(NB * G * 512))
-    metab = _pad_to(meta.reshape(G, NB, 64).astype("<u4").tobytes(), _align256(NB * G * 256))
+    rec = np.concatenate([words.reshape(G, NB, 64, 2), meta.reshape(G, NB, 64, 1)], axis=3)
+    chunks = _pad_to(rec.astype("<u4").tobytes(), _align256(NB * G * 768))
     sc = _pad_to(_scale_region(np.asarray(scales, dtype=np.float16), G, N, np.float16),
                  _align256(NB * ((G + 7) // 8) * 256))
-    out = codes + metab + sc + bytes(256)
+    out = chunks + sc + bytes(256)
     assert len(out) == packed_bytes(FMT_SP24, K, N)
     return out
 

@@ -288,3 +288,34 @@ def test_w4g_plan_covers_every_unit_once(K, N, M):
     p = qg.plan(qg.FMT_W4G, M, K, N)
     assert p["kernel"] == 1
     _check_plan(p, M, K, N, ws=qg.workspace_bytes_w4g(M, K, N))
+
+
+# --------------------------------------------------------------------------- 2:4 sparse
+@pytest.mark.parametrize("K,N", CONFIG_SHAPES + [(128, 64), (1152, 320)])
+def test_sp24_packed_bytes_match_independent_layout(K, N):
+    assert qg.packed_bytes(qg.FMT_W4A16_SP24, K, N) == layout.packed_bytes(layout.FMT_SP24, K, N)
+
+
+def test_sp24_validation_without_gpu(L):
+    A, P, C, W = _fake(0x10000000), _fake(0x20000000), _fake(0x30000000), _fake(0x40000000)
+    M, K, N = 16, 4096, 4096
+    ws = qg.workspace_bytes(qg.FMT_W4A16_SP24, M, K, N)
+    assert L.qgemm_w4a16_sp24(None, K, None, None, N, 0, K, N, None, 0, None) == OK
+    assert L.qgemm_w4a16_sp24(None, K, P, C, N, M, K, N, W, ws, None) == ERR_NULL
+    assert L.qgemm_w4a16_sp24(A, K, P, C, N, M, 1000, N, W, ws, None) == ERR_SHAPE
+    assert L.qgemm_w4a16_sp24(A, K + 4, P, C, N, M, K, N, W, ws, None) == ERR_ALIGN
+    assert L.qgemm_w4a16_sp24(A, K, P, _fake(0x10000000 + 256), N, M, K, N, W, ws, None) == ERR_ALIAS
+    nb = qg.packed_bytes(qg.FMT_W4A16_SP24, K, N)
+    assert L.qgemm_repack(5, K, N, _fake(0x10000000), _fake(0x20000000), None, None, _fake(0x30000000),
+                          nb - 256, None) == ERR_SIZE
+    st = L.qgemm_w4a16_sp24(A, K, P, C, N, M, K, N, W, ws, None)
+    if st != OK:
+        assert st in (ERR_HIP, ERR_DEV)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 11008), (8192, 28672), (28672, 8192), (1024, 1024)])
+@pytest.mark.parametrize("M", [1, 16, 33, 128])
+def test_sp24_plan_covers_every_unit_once(K, N, M):
+    p = qg.plan(qg.FMT_W4A16_SP24, M, K, N)
+    assert p["kernel"] == 1
+    _check_plan(p, M, K, N, ws=qg.workspace_bytes(qg.FMT_W4A16_SP24, M, K, N))

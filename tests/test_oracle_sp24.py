@@ -43,10 +43,8 @@ def test_generator_structure_and_spread():
 def _blob_words(blob, K, N):
     G, NB = K // 128, N // 16
     raw = np.frombuffer(blob, dtype=np.uint8)
-    words = raw[:NB * G * 512].view("<u4").reshape(G, NB, 64, 2)
-    m0 = (NB * G * 512 + 255) // 256 * 256
-    meta = raw[m0:m0 + NB * G * 256].view("<u4").reshape(G, NB, 64)
-    return words, meta
+    rec = raw[:NB * G * 768].view("<u4").reshape(G, NB, 64, 3)   # 12 bytes per lane
+    return rec[..., :2], rec[..., 2]
 
 
 def test_blob_hand_positions():
@@ -106,7 +104,7 @@ def test_blob_round_trip():
     assert np.array_equal(_decode(blob, K, N), ref.unpack_u4(p["codes"]))
     # scales region equals the W4A16 one
     d = layout.blob_w4a16(p["codes"], p["scales"])
-    s_sp = blob[K * N // 4 + K * N // 8:][:(N // 16) * 256]
+    s_sp = blob[3 * K * N // 8:][:(N // 16) * 256]
     s_w4 = d[K * N // 2:][:(N // 16) * 256]
     assert s_sp == s_w4
 
