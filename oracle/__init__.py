@@ -13,7 +13,9 @@ fails loudly if its HIP build is missing.
                         (group length 64 .. K, stored zero points, fp16 or bf16
                         activations); the 2:4 structure check of sparse
                         W4A16 (whose GEMM is the W4A16 definition on the
-                        dense codes); plus the per-token dynamic int8
+                        dense codes); the bit-plane W_b A8 GEMM on
+                        bipolar-INT weights (b = 1..8); plus the per-token
+                        dynamic int8
                         activation quantization that feeds W4A8.
 * ``oracle.layout``  -- an independent implementation of the repacked weight
                         blob byte layout, for byte-exact checks of the GPU repack.

@@ -74,6 +74,13 @@ than 8, in every 4 consecutive k of a column)
   scales  as W4A16.
   status  256 B; u32 at +0 = number of quads that break the 2:4 structure
           (0 for a valid blob), the rest zero.
+
+Bit-plane W_b A8 (format 6, b = 1..8 bits of a bipolar-INT code U)
+  chunks  G*NB chunks of 256*b B, chunk (b_, g) at (g*NB + b_)*256*b. Lane l
+          owns 4*b B at +4*b*l: plane words i = 0..b-1; bit 16*u + j of plane
+          word i is bit i of U at k = 128*g + 64*u + 16*h + j (u = 0, 1;
+          j = 0..15), column n = 16*b_ + c.
+  cscales fp16[N] = s_c[n].
 """
 
 from __future__ import annotations
@@ -87,6 +94,7 @@ FMT_W4A8 = 2
 FMT_W2W4 = 3
 FMT_W4G = 4
 FMT_SP24 = 5
+FMT_BP = 6
 
 
 def _align256(x: int) -> int:
@@ -229,6 +237,33 @@ def blob_sp24(qw: np.ndarray, scales: np.ndarray) -> bytes:
                  _align256(NB * ((G + 7) // 8) * 256))
     out = chunks + sc + bytes(256)
     assert len(out) == packed_bytes(FMT_SP24, K, N)
+    return out
+
+
+# --------------------------------------------------------------------------- bit planes
+def packed_bytes_bitplane(K: int, N: int, bits: int) -> int:
+    _check_shape(K, N)
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be 1..8")
+    G, NB = K // GROUP, N // 16
+    return _align256(NB * G * 256 * bits) + _align256(2 * N)
+
+
+def blob_bitplane(codes_u8: np.ndarray, bits: int, chan_scales: np.ndarray) -> bytes:
+    U = np.asarray(codes_u8).astype(np.uint32) & np.uint32(2 ** bits - 1)
+    K, N = U.shape
+    _check_shape(K, N)
+    G, NB = K // GROUP, N // 16
+    x = U.reshape(G, 2, 4, 16, NB, 16)                   # g, u, h, j, b, c
+    x = x.transpose(0, 4, 2, 5, 1, 3).reshape(G, NB, 64, 32)   # g, b, lane, 16u + j
+    words = np.zeros((G, NB, 64, bits), dtype=np.uint32)
+    for i in range(bits):
+        for t in range(32):
+            words[..., i] |= ((x[..., t] >> np.uint32(i)) & np.uint32(1)) << np.uint32(t)
+    chunks = _pad_to(words.astype("<u4").tobytes(), _align256(NB * G * 256 * bits))
+    cs = _pad_to(np.asarray(chan_scales, dtype=np.float16).tobytes(), _align256(2 * N))
+    out = chunks + cs
+    assert len(out) == packed_bytes_bitplane(K, N, bits)
     return out
 
 

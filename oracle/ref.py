@@ -103,6 +103,39 @@ def sparse24_violations(qw: np.ndarray, zero: int = 8) -> int:
     return int((nz > 2).sum())
 
 
+# --------------------------------------------------------------------------- bit-plane W_b A8
+def bipolar_value(u: np.ndarray, bits: int) -> np.ndarray:
+    """Value of a b-bit bipolar integer with stored bits u_i (0/1): every bit
+    plane i contributes +2^i or -2^i, so w = sum_i 2^i (2 u_i - 1) =
+    2 U - (2^b - 1) with U the bits read as an unsigned integer: the odd
+    integers -(2^b - 1) .. 2^b - 1, symmetric about zero (the bipolar-INT format
+    of the arbitrary-precision Tensor Core page's abstract)."""
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be 1..8")
+    return 2 * np.asarray(u).astype(np.int64) - (2 ** bits - 1)
+
+
+def gemm_bitplane_a8(A_i8: np.ndarray, codes_u8: np.ndarray, bits: int, a_scale: np.ndarray,
+                     chan_scales: np.ndarray, cols: np.ndarray | None = None):
+    """W_b A8 GEMM on bipolar-INT weights with a per-column fp16 scale and
+    int8 activations with a per-row fp16 scale:
+
+        acc[m, n] = sum_k A[m, k] * (2 U[k, n] - (2^b - 1))   (exact, int64)
+        C[m, n]   = acc[m, n] * a_scale[m] * s_c[n]           (fp64)
+
+    ``codes_u8`` holds U (only its low ``bits`` bits). Every product and partial
+    sum is an integer below 2^53 in magnitude, so the fp64 matmul is exact."""
+    U = np.asarray(codes_u8).astype(np.int64) & (2 ** bits - 1)
+    sc = np.asarray(chan_scales).astype(np.float64)
+    if cols is not None:
+        U = U[:, cols]
+        sc = sc[cols]
+    W = bipolar_value(U, bits).astype(np.float64)
+    acc = (np.asarray(A_i8).astype(np.float64) @ W).astype(np.int64)
+    C = acc.astype(np.float64) * np.asarray(a_scale).astype(np.float64)[:, None] * sc[None, :]
+    return acc, C
+
+
 # --------------------------------------------------------------------------- W4 general grid
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     """bfloat16 values given as their 16-bit patterns -> fp64 (exact).

@@ -32,6 +32,7 @@ _KIND_W4A8 = 2
 _KIND_W2W4 = 3
 _KIND_W4G = 4
 _KIND_SP24 = 5
+_KIND_BP = 6
 
 
 def rng_for(seed: int, *tags: int) -> np.random.Generator:
@@ -226,3 +227,20 @@ def w4a16_sp24_problem(M: int, K: int, N: int, seed: int = 0, weights: bool = Tr
         out["codes"] = pack_nibbles_u32(q)
         out["scales"] = _fp16_uniform(rng_for(seed, _KIND_SP24, 2, K, N), 0.005, 0.02, (K // GROUP, N))
     return out
+
+
+def bitplane_problem(M: int, K: int, N: int, bits: int, seed: int = 0) -> dict:
+    """W_b A8 workload on bipolar-INT weights: int8 A uniform in [-127, 127] with
+    a per-row fp16 scale uniform in [0.01, 0.03]; b-bit codes U uniform in
+    0 .. 2^b - 1 (value 2U - (2^b - 1)); a per-column fp16 scale uniform in
+    [0.05, 0.1] / (2^b - 1), so every weight lies within +-0.1."""
+    if not 1 <= bits <= 8:
+        raise ValueError("bits must be 1..8")
+    return {
+        "M": M, "K": K, "N": N, "bits": bits,
+        "A": rng_for(seed, _KIND_BP, bits, 0, M, K).integers(-127, 128, size=(M, K), dtype=np.int8),
+        "a_scale": _fp16_uniform(rng_for(seed, _KIND_BP, bits, 1, M, K), 0.01, 0.03, (M,)),
+        "codes": rng_for(seed, _KIND_BP, bits, 2, K, N).integers(0, 2 ** bits, size=(K, N), dtype=np.uint8),
+        "chan_scales": (rng_for(seed, _KIND_BP, bits, 3, K, N).uniform(0.05, 0.1, size=(N,))
+                        / (2 ** bits - 1)).astype(np.float16),
+    }
