@@ -179,6 +179,7 @@ SECONDARY = (
     + [("per-token int8 quantization", 4, 4096, 0, M) for M in (16, 64, 128)]
     + [("w4a8 from fp16 (quantize + GEMM)", 5, 4096, 11008, M) for M in (16, 64, 128)]
     + [("w4a16 2:4 sparse", 7, K, N, M) for (K, N) in [(8192, 28672), (4096, 11008)] for M in (1, 16, 64)]
+    + [(f"bit-plane w{b}a8", 8, 4096, 11008, M) for b in (1, 2, 3, 4, 8) for M in (1, 16)]
     + [(name, 6, 4096, 11008, M) for name in ("w4g g64 fp16", "w4g g128 zeros fp16", "w4g per-channel fp16",
                                               "w4g g128 bf16", "w4g g128 zeros bf16") for M in (1, 16)]
 )
@@ -188,9 +189,12 @@ W4G_VARIANTS = {"w4g g64 fp16": (64, False, "fp16"), "w4g g128 zeros fp16": (128
                 "w4g g128 zeros bf16": (128, True, "bf16")}
 
 
-def secondary_bytes_ops(fmt, K, N, M, n4=0, gs=128, zeros=False):
+def secondary_bytes_ops(fmt, K, N, M, n4=0, gs=128, zeros=False, name_bits=4):
     """Algorithmic bytes and ops of one launch (codes, scales, A, C)."""
     G = K // 128
+    if fmt == 8:   # b bit planes, channel scales, int8 A + row scales, fp16 C
+        b = int(name_bits)
+        return K * N * b // 8 + 2 * N + M * K + 2 * M + 2 * M * N, alg_flops(M, K, N)
     if fmt == 7:   # kept codes (half the weights x 4 bits) + 2-bit positions + scales, A, C
         return K * N // 4 + K * N // 8 + G * N * 2 + 2 * M * K + 2 * M * N, alg_flops(M, K, N)
     if fmt == 6:   # codes, one 2-byte scale (4 with a zero point) per group, A, C
@@ -218,9 +222,16 @@ def secondary(torch, qg, dev, rotate_mb):
     rows = []
     built = {}
     for (name, fmt, K, N, M) in SECONDARY:
-        key = (fmt, K, N, name if fmt == 6 else "")
+        key = (fmt, K, N, name if fmt in (6, 8) else "")
         if key not in built:
-            if fmt == 7:
+            if fmt == 8:
+                bits = int(name.split("w")[1].split("a")[0])
+                p = gen.bitplane_problem(128, K, N, bits, seed=0)
+                blob = qg.repack_bitplane(torch.from_numpy(p["codes"]).to(dev),
+                                          torch.from_numpy(p["chan_scales"]).to(dev), bits)
+                A = torch.from_numpy(p["A"]).to(dev)
+                extra = {"a_scale": torch.from_numpy(p["a_scale"]).to(dev), "bits": bits}
+            elif fmt == 7:
                 p = gen.w4a16_sp24_problem(128, K, N, seed=0)
                 blob = qg.repack_sp24(torch.from_numpy(p["codes"].view(np.int32)).to(dev),
                                       torch.from_numpy(p["scales"]).to(dev))
@@ -269,7 +280,10 @@ def secondary(torch, qg, dev, rotate_mb):
         A = A_all[:M].contiguous()
         C = torch.empty((M, max(N, 1)), dtype=A.dtype if fmt == 6 else torch.float16, device=dev)
         ws = qg.Workspace()
-        if fmt == 7:
+        if fmt == 8:
+            a_s = extra["a_scale"][:M].contiguous()
+            run = lambda b: qg.bitplane_a8(A, a_s, b, K, N, extra["bits"], out=C, workspace=ws)
+        elif fmt == 7:
             run = lambda b: qg.w4a16_sp24(A, b, K, N, out=C, workspace=ws)
         elif fmt == 6:
             run = lambda b: qg.w4g(A, b, K, N, extra["gs"], extra["zeros"], out=C, workspace=ws)
@@ -309,12 +323,12 @@ def secondary(torch, qg, dev, rotate_mb):
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (5 * n)
         byt, ops = secondary_bytes_ops(fmt, K, N, M, extra.get("n4", 0), extra.get("gs", 128),
-                                       extra.get("zeros", False))
-        peak = INT8_PEAK_TOPS if fmt in (2, 5) else FP16_PEAK_TFLOPS
+                                       extra.get("zeros", False), extra.get("bits", 4))
+        peak = INT8_PEAK_TOPS if fmt in (2, 5, 8) else FP16_PEAK_TFLOPS
         gbs = byt / (us * 1e-6) / 1e9
         tops = ops / (us * 1e-6) / 1e12
         roof_us = max(byt / (HBM_PEAK_GBS * 1e9), ops / (peak * 1e12)) * 1e6
-        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4", "quant_a8", "w4a8_fp16", "w4g", "w4a16_sp24"][fmt],
+        rows.append({"workload": name, "fmt": ["", "w4a16", "w4a8", "w2w4", "quant_a8", "w4a8_fp16", "w4g", "w4a16_sp24", "bitplane_a8"][fmt],
                      "K": K, "N": N, "M": M,
                      "us": round(us, 2), "tops": round(tops, 2), "gbs": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline_frac": round(roof_us / us, 4),

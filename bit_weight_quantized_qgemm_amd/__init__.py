@@ -17,7 +17,8 @@ __all__ = [
     "workspace_bytes", "plan", "set_plan_override", "repack", "repack_w4a16", "repack_w4a8",
     "repack_w2w4", "w4a16", "w4a8", "w2w4_mixed", "Workspace", "EXPORTED_SYMBOLS", "quantize_a8",
     "w4a8_fp16", "FMT_W4G", "DT_F16", "DT_BF16", "packed_bytes_w4g", "workspace_bytes_w4g",
-    "repack_w4g", "w4g", "FMT_W4A16_SP24", "repack_sp24", "w4a16_sp24",
+    "repack_w4g", "w4g", "FMT_W4A16_SP24", "repack_sp24", "w4a16_sp24", "FMT_BITPLANE",
+    "packed_bytes_bitplane", "workspace_bytes_bitplane", "repack_bitplane", "bitplane_a8",
 ]
 
 FMT_W4A16 = 1
@@ -25,6 +26,7 @@ FMT_W4A8 = 2
 FMT_W2W4 = 3
 FMT_W4G = 4
 FMT_W4A16_SP24 = 5
+FMT_BITPLANE = 6
 DT_F16 = 1
 DT_BF16 = 2
 
@@ -37,6 +39,8 @@ EXPORTED_SYMBOLS = (
     "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16", "qgemm_w4a8", "qgemm_w2w4_mixed",
     "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8", "qgemm_w4g_packed_bytes",
     "qgemm_w4g_workspace_bytes", "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24",
+    "qgemm_bitplane_packed_bytes", "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack",
+    "qgemm_bitplane_a8",
 )
 
 
@@ -78,10 +82,15 @@ def lib() -> ctypes.CDLL:
         L.qgemm_w4g_workspace_bytes.argtypes = [i64, i64, i64, u64p]
         L.qgemm_w4g_repack.argtypes = [i64, i64, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.qgemm_w4g.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, ctypes.c_size_t, vp]
+        L.qgemm_bitplane_packed_bytes.argtypes = [i64, i64, i32, u64p]
+        L.qgemm_bitplane_workspace_bytes.argtypes = [i64, i64, i64, i32, u64p]
+        L.qgemm_bitplane_repack.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.qgemm_bitplane_a8.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
                      "qgemm_quantize_a8", "qgemm_w4g_packed_bytes", "qgemm_w4g_workspace_bytes",
-                     "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24"):
+                     "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24", "qgemm_bitplane_packed_bytes",
+                     "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack", "qgemm_bitplane_a8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -344,4 +353,43 @@ def w4g(A, blob, K: int, N: int, group_size: int, has_zeros: bool, out=None,
     ws, wsb = (workspace or _default_ws).get(workspace_bytes_w4g(M, K, N), A.device)
     _check(lib().qgemm_w4g(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K, N, group_size,
                            int(bool(has_zeros)), dt, _ptr(ws), wsb, _stream_ptr(A.device)), "qgemm_w4g")
+    return out
+
+
+# ----------------------------------------------------------------------------- bit planes
+def packed_bytes_bitplane(K: int, N: int, bits: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qgemm_bitplane_packed_bytes(K, N, bits, ctypes.byref(out)), "qgemm_bitplane_packed_bytes")
+    return out.value
+
+
+def workspace_bytes_bitplane(M: int, K: int, N: int, bits: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().qgemm_bitplane_workspace_bytes(M, K, N, bits, ctypes.byref(out)),
+           "qgemm_bitplane_workspace_bytes")
+    return out.value
+
+
+def repack_bitplane(codes_u8, chan_scales, bits: int):
+    """codes_u8: uint8 [K][N] holding U (low `bits` bits); chan_scales: fp16 [N]."""
+    torch = _torch()
+    _require_cuda(codes_u8, chan_scales)
+    K, N = codes_u8.shape
+    nbytes = packed_bytes_bitplane(K, N, bits)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=codes_u8.device)
+    _check(lib().qgemm_bitplane_repack(K, N, bits, _ptr(codes_u8), _ptr(chan_scales), _ptr(out), nbytes,
+                                       _stream_ptr(codes_u8.device)), "qgemm_bitplane_repack")
+    return out
+
+
+def bitplane_a8(A_i8, a_scale, blob, K: int, N: int, bits: int, out=None, acc_out=None,
+                workspace: Workspace | None = None):
+    """Bit-plane W_b A8 GEMM; returns C (fp16) and fills acc_out (int32 [M][N]) when given."""
+    _require_cuda(A_i8, a_scale, blob, acc_out)
+    M = A_i8.shape[0]
+    out = _gemm_out(M, N, A_i8.device, out)
+    ws, wsb = (workspace or _default_ws).get(workspace_bytes_bitplane(M, K, N, bits), A_i8.device)
+    _check(lib().qgemm_bitplane_a8(_ptr(A_i8), A_i8.stride(0), _ptr(a_scale), _ptr(blob), _ptr(out),
+                                   out.stride(0), _ptr(acc_out), M, K, N, bits, _ptr(ws), wsb,
+                                   _stream_ptr(A_i8.device)), "qgemm_bitplane_a8")
     return out

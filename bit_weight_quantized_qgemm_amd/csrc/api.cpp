@@ -27,6 +27,7 @@ constexpr int64_t kMaxM = 65535;
 constexpr int64_t kMaxKN = int64_t(1) << 20;
 constexpr int64_t kMaxKW4A8 = 16384;
 constexpr int64_t kMaxWeights = int64_t(1) << 32;   // K*N: at most 2 GiB of 4-bit codes
+constexpr int64_t kMaxKBitplane = 65536;            // K*127*255 < 2^31: exact int32
 
 int hip_fail(hipError_t e, const char* what) {
   g_last_error = std::string(what) + ": " + hipGetErrorString(e);
@@ -49,6 +50,7 @@ int check_kn(int fmt, int64_t K, int64_t N) {
   if (K <= 0 || K % qg::kGroup != 0 || K > kMaxKN) return QGEMM_ERR_SHAPE;
   if (N <= 0 || N % 64 != 0 || N > kMaxKN) return QGEMM_ERR_SHAPE;
   if (fmt == QGEMM_FMT_W4A8 && K > kMaxKW4A8) return QGEMM_ERR_SHAPE;
+  if (fmt == QGEMM_FMT_BITPLANE && K > kMaxKBitplane) return QGEMM_ERR_SHAPE;
   if (K * N > kMaxWeights) return QGEMM_ERR_SHAPE;   // 32-bit buffer offsets into the blob
   return QGEMM_OK;
 }
@@ -146,6 +148,19 @@ BlobLayout blob_layout_w4g(int64_t K, int64_t N, int gs, bool zeros) {
   return L;
 }
 
+BlobLayout blob_layout_bitplane(int64_t K, int64_t N, int bits) {
+  BlobLayout L;
+  L.K = K;
+  L.N = N;
+  L.G = K / kGroup;
+  L.NB = N / 16;
+  L.G8 = (L.G + 7) / 8;
+  L.codes = 0;
+  L.aux = align256((size_t)(L.NB * L.G) * 256 * bits);
+  L.total = L.aux + align256((size_t)N * 2);
+  return L;
+}
+
 // Large-M W4A16 plan: 8-wave workgroups own 16*mb x 256 tiles. K is split across
 // workgroups until about one workgroup per CU is busy: measured on MI355X, a
 // second resident workgroup per CU does not pay for the extra partial-sum
@@ -180,7 +195,7 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   return pl;
 }
 
-Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits) {
   const int force_kernel = g_force_kernel.load();
   const bool wide_ok = fmt == QGEMM_FMT_W4A16 && N % kWideCols == 0;
   if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM))) {
@@ -212,7 +227,8 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
   const int force_nb = g_force_nb.load();
   const int force_wpt = g_force_wpt.load();
   const int force_splits = g_force_splits.load();
-  const double chunk = fmt == QGEMM_FMT_W2W4 ? 560.0 : fmt == QGEMM_FMT_W4A16_SP24 ? 768.0 : 1024.0;   // streamed bytes per 16 x 128 chunk
+  const double chunk = fmt == QGEMM_FMT_W2W4 ? 560.0 : fmt == QGEMM_FMT_W4A16_SP24 ? 768.0
+                       : fmt == QGEMM_FMT_BITPLANE ? 256.0 * bits : 1024.0;   // streamed bytes per 16 x 128 chunk
   const double blob = (double)G * (double)(N / 16) * chunk;
   const double inflight_target = std::min(8.0 * 1048576.0, blob / 2);
   const int pref_nb = M > 4 ? 2 : 1;
@@ -239,7 +255,11 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
       if (kp > G) continue;
       // 1024-thread workgroups leave 128 VGPRs per wave: these tiles would spill
       if (kp == 4 && !force_wpt && nb == 2 &&
-          (fmt == QGEMM_FMT_W2W4 || ((fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W4G) && pl.mb == 2)))
+          (fmt == QGEMM_FMT_W2W4 || ((fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W4G) && pl.mb == 2) ||
+           (fmt == QGEMM_FMT_BITPLANE && pl.mb == 2 && bits >= 6)))
+        continue;
+      // and these (8 planes, 32-row tiles) spill even with one column block
+      if (kp == 4 && !force_wpt && fmt == QGEMM_FMT_BITPLANE && pl.mb == 2 && bits == 8)
         continue;
       const int smax = tiles > kMaxCounters ? 1 : std::min(G, 64);
       for (int s0 = 1; s0 <= smax; ++s0) {
@@ -255,7 +275,8 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N) {
         const size_t lds = fmt == QGEMM_FMT_W4A16 ? lds_bytes_w4a16(c, G)
                            : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G)
                            : fmt == QGEMM_FMT_W4G  ? lds_bytes_w4g(c, G)
-                           : fmt == QGEMM_FMT_W4A16_SP24 ? lds_bytes_sp24(c, G) : lds_bytes_w2w4(c, G);
+                           : fmt == QGEMM_FMT_W4A16_SP24 ? lds_bytes_sp24(c, G)
+                           : fmt == QGEMM_FMT_BITPLANE ? lds_bytes_bitplane(c, G) : lds_bytes_w2w4(c, G);
         if (lds > 160 * 1024) continue;
         const int64_t wgs = tiles * s;
         const int64_t waves = wgs * 4 * kp;
@@ -480,31 +501,34 @@ struct GemmCall {
   int gs = qg::kGroup;    // general grid only
   bool zeros = false;
   bool bf16 = false;
+  int bits = 4;           // bit-plane format only
 };
 
 int run_gemm(const GemmCall& g) {
-  if (!valid_fmt(g.fmt) && g.fmt != QGEMM_FMT_W4G) return QGEMM_ERR_FORMAT;
+  if (!valid_fmt(g.fmt) && g.fmt != QGEMM_FMT_W4G && g.fmt != QGEMM_FMT_BITPLANE) return QGEMM_ERR_FORMAT;
+  const bool int8_act = g.fmt == QGEMM_FMT_W4A8 || g.fmt == QGEMM_FMT_BITPLANE;
   int st = check_kn(g.fmt, g.K, g.N);
   if (st) return st;
   if (g.M < 0 || g.M > kMaxM) return QGEMM_ERR_SHAPE;
   if (g.M == 0) return QGEMM_OK;
   if (!g.A || !g.packed || !g.C) return QGEMM_ERR_NULL;
-  if (g.fmt == QGEMM_FMT_W4A8 && !g.a_scale) return QGEMM_ERR_NULL;
-  const int64_t aelt = g.fmt == QGEMM_FMT_W4A8 ? 1 : 2;
+  if (int8_act && !g.a_scale) return QGEMM_ERR_NULL;
+  const int64_t aelt = int8_act ? 1 : 2;
   if (!aligned(g.A, 16) || !aligned(g.packed, 16) || !aligned(g.C, 16)) return QGEMM_ERR_ALIGN;
   if (g.lda < g.K || (g.lda * aelt) % 16 != 0) return QGEMM_ERR_ALIGN;
   if (g.ldc < g.N || g.ldc % 8 != 0) return QGEMM_ERR_ALIGN;
   if (g.a_scale && !aligned(g.a_scale, 2)) return QGEMM_ERR_ALIGN;
   if (g.acc_out && !aligned(g.acc_out, 4)) return QGEMM_ERR_ALIGN;
-  const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N);
+  const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N, g.bits);
   if (pl.ws_bytes > 0) {
     if (!g.ws) return QGEMM_ERR_NULL;
     if (g.ws_bytes < pl.ws_bytes) return QGEMM_ERR_WORKSPACE;
     if (!aligned(g.ws, 16)) return QGEMM_ERR_ALIGN;
   }
   // the fixed-size part of the blob (everything before a mixed blob's high plane)
-  const qg::BlobLayout L = g.fmt == QGEMM_FMT_W4G ? qg::blob_layout_w4g(g.K, g.N, g.gs, g.zeros)
-                                                   : qg::blob_layout(g.fmt, g.K, g.N, 0);
+  const qg::BlobLayout L = g.fmt == QGEMM_FMT_W4G       ? qg::blob_layout_w4g(g.K, g.N, g.gs, g.zeros)
+                           : g.fmt == QGEMM_FMT_BITPLANE ? qg::blob_layout_bitplane(g.K, g.N, g.bits)
+                                                         : qg::blob_layout(g.fmt, g.K, g.N, 0);
   const size_t blob_fixed = g.fmt == QGEMM_FMT_W2W4 ? L.high : L.total;
   const size_t c_bytes = (size_t)((g.M - 1) * g.ldc + g.N) * 2;
   const size_t a_bytes = (size_t)((g.M - 1) * g.lda + g.K) * aelt;
@@ -542,6 +566,7 @@ int run_gemm(const GemmCall& g) {
   a.mt = pl.mt;
   a.nt = pl.nt;
   a.gs = g.gs;
+  a.bits = g.bits;
   if (pl.ws_bytes) {
     a.counters = static_cast<uint32_t*>(g.ws);
     a.partial = static_cast<char*>(g.ws) + pl.counter_bytes;
@@ -552,6 +577,8 @@ int run_gemm(const GemmCall& g) {
   else if (g.fmt == QGEMM_FMT_W4A8) e = qg::launch_w4a8(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4G) e = qg::launch_w4g(pl, a, g.bf16, g.zeros, s);
   else if (g.fmt == QGEMM_FMT_W4A16_SP24) e = qg::launch_sp24(pl, a, s);
+  else if (g.fmt == QGEMM_FMT_BITPLANE)
+    e = g.bits <= 4 ? qg::launch_bitplane_lo(pl, a, g.bits, s) : qg::launch_bitplane_hi(pl, a, g.bits, s);
   else e = qg::launch_w2w4(pl, a, s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return QGEMM_OK;
@@ -641,6 +668,56 @@ int qgemm_w4g(const void* A, int64_t lda, const void* packed, void* C, int64_t l
   g.gs = group_size;
   g.zeros = has_zeros != 0;
   g.bf16 = act_dtype == QGEMM_DT_BF16;
+  return run_gemm(g);
+}
+
+int qgemm_bitplane_packed_bytes(int64_t K, int64_t N, int32_t bits, size_t* bytes) {
+  if (!bytes) return QGEMM_ERR_NULL;
+  int st = check_kn(QGEMM_FMT_BITPLANE, K, N);
+  if (st) return st;
+  if (bits < 1 || bits > 8) return QGEMM_ERR_RANGE;
+  *bytes = qg::blob_layout_bitplane(K, N, bits).total;
+  return QGEMM_OK;
+}
+
+int qgemm_bitplane_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t bits, size_t* bytes) {
+  if (!bytes) return QGEMM_ERR_NULL;
+  int st = check_kn(QGEMM_FMT_BITPLANE, K, N);
+  if (st) return st;
+  if (bits < 1 || bits > 8) return QGEMM_ERR_RANGE;
+  if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
+  *bytes = M == 0 ? 0 : qg::make_plan(QGEMM_FMT_BITPLANE, M, K, N, bits).ws_bytes;
+  return QGEMM_OK;
+}
+
+int qgemm_bitplane_repack(int64_t K, int64_t N, int32_t bits, const void* codes, const void* chan_scales,
+                          void* packed, size_t packed_bytes, void* stream) {
+  if (!codes || !chan_scales || !packed) return QGEMM_ERR_NULL;
+  int st = check_kn(QGEMM_FMT_BITPLANE, K, N);
+  if (st) return st;
+  if (bits < 1 || bits > 8) return QGEMM_ERR_RANGE;
+  const qg::BlobLayout L = qg::blob_layout_bitplane(K, N, bits);
+  if (packed_bytes != L.total) return QGEMM_ERR_SIZE;
+  if (!aligned(packed, 16) || !aligned(chan_scales, 2)) return QGEMM_ERR_ALIGN;
+  if (overlap(packed, L.total, codes, (size_t)(K * N)) || overlap(packed, L.total, chan_scales, (size_t)N * 2))
+    return QGEMM_ERR_ALIAS;
+  st = check_device();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = qg::launch_zero_fill(packed, L.total, s);
+  if (e != hipSuccess) return hip_fail(e, "zero fill");
+  e = qg::launch_repack_bitplane(L, bits, codes, chan_scales, packed, s);
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  return QGEMM_OK;
+}
+
+int qgemm_bitplane_a8(const void* A, int64_t lda, const void* a_scale, const void* packed, void* C, int64_t ldc,
+                      int32_t* acc_out, int64_t M, int64_t K, int64_t N, int32_t bits, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (check_kn(QGEMM_FMT_BITPLANE, K, N) == QGEMM_OK && (bits < 1 || bits > 8)) return QGEMM_ERR_RANGE;
+  GemmCall g{QGEMM_FMT_BITPLANE, A, lda, a_scale, packed, C, ldc, acc_out, M, K, N, workspace,
+             workspace_bytes, stream};
+  g.bits = bits;
   return run_gemm(g);
 }
 

@@ -55,7 +55,8 @@ struct Plan {
   size_t ws_bytes = 0;   // total workspace (0 when splits == 1)
 };
 
-Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N);
+// bits: planes per weight of the bit-plane format (ignored by the others)
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits = 4);
 
 // Arguments of every GEMM kernel (passed by value).
 struct GemmArgs {
@@ -73,6 +74,7 @@ struct GemmArgs {
   int M, K, N, G, G8;
   int splits, gps, mt, nt;
   int gs;                 // general-grid format: k per quantization group
+  int bits;               // bit-plane format: planes per weight
 };
 
 size_t lds_bytes_w4a16(const Plan& pl, int G);
@@ -80,12 +82,15 @@ size_t lds_bytes_w4a8(const Plan& pl, int G);
 size_t lds_bytes_w2w4(const Plan& pl, int G);
 size_t lds_bytes_w4g(const Plan& pl, int G);
 size_t lds_bytes_sp24(const Plan& pl, int G);
+size_t lds_bytes_bitplane(const Plan& pl, int G);
 hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4g(const Plan& pl, const GemmArgs& a, bool bf16, bool zeros, hipStream_t s);
 hipError_t launch_sp24(const Plan& pl, const GemmArgs& a, hipStream_t s);
+hipError_t launch_bitplane_lo(const Plan& pl, const GemmArgs& a, int bits, hipStream_t s);   // bits 1..4
+hipError_t launch_bitplane_hi(const Plan& pl, const GemmArgs& a, int bits, hipStream_t s);   // bits 5..8
 
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* Q, int64_t ldq,
@@ -98,6 +103,10 @@ hipError_t launch_repack_w4a8(const BlobLayout& L, const void* codes, const void
 // scales region (see repack.hip); Gs = K / gs groups, P = 2 entries per 128-k
 // chunk when gs = 64, else 1.
 BlobLayout blob_layout_w4g(int64_t K, int64_t N, int gs, bool zeros);
+// Bit-plane W_b A8: chunks of 256*bits bytes (codes), then fp16 channel scales (aux).
+BlobLayout blob_layout_bitplane(int64_t K, int64_t N, int bits);
+hipError_t launch_repack_bitplane(const BlobLayout& L, int bits, const void* codes, const void* cscales,
+                                  void* packed, hipStream_t s);
 // 2:4 sparse W4A16: 768-byte chunks of kept codes and positions, scales, status word (high).
 hipError_t launch_repack_sp24(const BlobLayout& L, const void* codes, const void* scales, void* packed,
                               hipStream_t s);

@@ -48,6 +48,10 @@
 //                The position word's bits 16s + 2v .. +1 hold the position of
 //                kept value v of code word s.
 //  SP24 status : u32 count of quads with more than two codes other than 8.
+//  BP chunks   : bit-plane W_b A8; chunk (b, g) of 256*B bytes at (g*NB + b)*256*B;
+//                lane l owns 4*B bytes = plane words i = 0..B-1; bit 16u + j of word
+//                i is bit i of the code at k = 128g + 64u + 16h + j, column 16b + c.
+//  BP cscales  : fp16 [N].
 //  W2W4 high   : per 4-bit group, 32 B at 32*(off + rank(c)), quarter h at +8h,
 //                the upper 2 code bits in the base-plane arrangement.
 #include "qgemm_device.h"
@@ -151,6 +155,27 @@ __global__ void repack_w2w4_kernel(const uint8_t* __restrict__ codes, const u32x
     const uint32_t rank = __builtin_popcount(d[1] & ((1u << c) - 1u));
     high[(size_t)(d[0] + rank) * 4 + h] = hi;
   }
+}
+
+// One thread per (chunk, lane) of the bit-plane format: 32 codes -> B plane words.
+__global__ void repack_bitplane_kernel(const uint8_t* __restrict__ codes, uint32_t* __restrict__ out, int N,
+                                       int bits, int64_t total) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= total) return;
+  const int lane = (int)(tid & 63);
+  const int64_t chunk = tid >> 6;
+  const int NB = N / 16;
+  const int g = (int)(chunk / NB), b = (int)(chunk % NB);
+  const int c = lane & 15, h = lane >> 4;
+  const int n = 16 * b + c;
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = 0; t < 32; ++t) {
+    const int k = 128 * g + 64 * (t >> 4) + 16 * h + (t & 15);
+    const uint32_t u = codes[(size_t)k * N + n];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] |= ((u >> i) & 1u) << t;
+  }
+  for (int i = 0; i < bits; ++i) out[tid * bits + i] = w[i];
 }
 
 // One thread per (chunk, lane) of the 2:4 sparse format: 16 canonical words
@@ -262,6 +287,21 @@ hipError_t launch_repack_sp24(const BlobLayout& L, const void* codes, const void
   hipLaunchKernelGGL((repack_scales<uint16_t>), dim3(grid_for(ns, 256)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(scales), reinterpret_cast<uint16_t*>(out + L.scales),
                      (int)L.G, (int)L.G8, (int)L.N, ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_bitplane(const BlobLayout& L, int bits, const void* codes, const void* cscales,
+                                  void* packed, hipStream_t s) {
+  char* out = static_cast<char*>(packed);
+  const int64_t nc = L.NB * L.G * 64;
+  hipLaunchKernelGGL(repack_bitplane_kernel, dim3(grid_for(nc, 256)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(codes), reinterpret_cast<uint32_t*>(out + L.codes), (int)L.N,
+                     bits, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(copy_halves, dim3(grid_for(L.N, 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(cscales), reinterpret_cast<uint16_t*>(out + L.aux),
+                     (int)L.N);
   return hipGetLastError();
 }
 

@@ -5,8 +5,9 @@
  * batches (M = 1..128 is the design range; larger M is accepted), the
  * mixed-precision auto-regressive linear layer of the MARLIN paper (abstract:
  * weights compressed to about 4 bits per element, batched decode with 1..128
- * parallel clients, memory-bound up to batch 16..32). Three weight formats,
- * and a general-grid 4-bit variant (qgemm_w4g, below):
+ * parallel clients, memory-bound up to batch 16..32). Four weight formats,
+ * a general-grid 4-bit variant (qgemm_w4g) and a bit-plane W_b A8 format
+ * (qgemm_bitplane_*), both below:
  *
  *   W4A16  fp16 activations; unsigned 4-bit codes q (0..15) with an implicit
  *          zero point 8 and one fp16 scale s per group of 128 consecutive k of
@@ -75,7 +76,8 @@ typedef enum qgemm_fmt {
   QGEMM_FMT_W4A8 = 2,
   QGEMM_FMT_W2W4 = 3,
   QGEMM_FMT_W4G = 4,  /* general grid: only through the qgemm_w4g_* entry points */
-  QGEMM_FMT_W4A16_SP24 = 5
+  QGEMM_FMT_W4A16_SP24 = 5,
+  QGEMM_FMT_BITPLANE = 6  /* bit-plane W_b A8: only through the qgemm_bitplane_* entry points */
 } qgemm_fmt;
 
 /* Activation (and scale, output) type of the general-grid 4-bit GEMM. */
@@ -243,6 +245,38 @@ int qgemm_w4g_repack(int64_t K, int64_t N, int32_t group_size, const void* codes
 int qgemm_w4g(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M,
               int64_t K, int64_t N, int32_t group_size, int32_t has_zeros, int32_t act_dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bit-plane W_b A8 GEMM, b = 1..8 bits per weight (the arbitrary-precision
+ * Tensor Core page's abstract: a symmetric bipolar-INT weight format whose
+ * matrices are decomposed at the bit level and recovered after the products).
+ * A weight with stored bits u_i (code U = sum_i 2^i u_i) has the value
+ *   w = sum_i 2^i (2 u_i - 1) = 2U - (2^b - 1),
+ * the odd integers -(2^b - 1) .. 2^b - 1; each output column has one fp16
+ * scale s_c[n]. Activations are int8 with a per-row fp16 scale (as
+ * qgemm_w4a8; qgemm_quantize_a8 produces them):
+ *   acc[m,n] = sum_k A[m,k] * w[k,n]   (exact int32; K <= 65536, else
+ *              QGEMM_ERR_SHAPE, keeps |acc| < 2^31 for every input)
+ *   C[m,n]   = fp16(float(acc) * a_scale[m] * s_c[n]).
+ * The blob holds the b bit planes (b/8 bytes per weight) and the channel
+ * scales. bits outside 1..8 is QGEMM_ERR_RANGE.
+ *
+ * qgemm_bitplane_packed_bytes / _workspace_bytes: sizes (workspace contract
+ *   as qgemm_workspace_bytes).
+ * qgemm_bitplane_repack: codes uint8[K][N] holding U (only the low `bits`
+ *   bits of each byte are used), chan_scales fp16[N]; packed must hold exactly
+ *   qgemm_bitplane_packed_bytes() bytes. Asynchronous on `stream`.
+ * qgemm_bitplane_a8: A int8[M][lda] (lda a multiple of 16), a_scale fp16[M],
+ *   C fp16[M][ldc], acc_out (nullable) int32[M][N] dense; `bits` must be the
+ *   value the blob was repacked with (it is not recorded in the blob).
+ */
+int qgemm_bitplane_packed_bytes(int64_t K, int64_t N, int32_t bits, size_t* bytes);
+int qgemm_bitplane_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t bits, size_t* bytes);
+int qgemm_bitplane_repack(int64_t K, int64_t N, int32_t bits, const void* codes, const void* chan_scales,
+                          void* packed, size_t packed_bytes, void* stream);
+int qgemm_bitplane_a8(const void* A, int64_t lda, const void* a_scale, const void* packed, void* C,
+                      int64_t ldc, int32_t* acc_out, int64_t M, int64_t K, int64_t N, int32_t bits,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Work decomposition used for a call of this shape (for tests and tuning).

@@ -319,3 +319,34 @@ def test_sp24_plan_covers_every_unit_once(K, N, M):
     p = qg.plan(qg.FMT_W4A16_SP24, M, K, N)
     assert p["kernel"] == 1
     _check_plan(p, M, K, N, ws=qg.workspace_bytes(qg.FMT_W4A16_SP24, M, K, N))
+
+
+# --------------------------------------------------------------------------- bit planes
+@pytest.mark.parametrize("K,N", [(1024, 1024), (4096, 11008), (11008, 4096), (128, 64)])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 8])
+def test_bitplane_packed_bytes_match_independent_layout(K, N, bits):
+    assert qg.packed_bytes_bitplane(K, N, bits) == layout.packed_bytes_bitplane(K, N, bits)
+
+
+def test_bitplane_validation_without_gpu(L):
+    out = ctypes.c_size_t(0)
+    assert L.qgemm_bitplane_packed_bytes(1024, 1024, 0, ctypes.byref(out)) == ERR_RANGE
+    assert L.qgemm_bitplane_packed_bytes(1024, 1024, 9, ctypes.byref(out)) == ERR_RANGE
+    assert L.qgemm_bitplane_packed_bytes(65536, 64, 4, ctypes.byref(out)) == OK
+    assert L.qgemm_bitplane_packed_bytes(65536 + 128, 64, 4, ctypes.byref(out)) == ERR_SHAPE
+    A, S, P, C, W = (_fake(0x10000000), _fake(0x50000000), _fake(0x20000000), _fake(0x30000000),
+                     _fake(0x40000000))
+    M, K, N = 16, 4096, 4096
+    ws = qg.workspace_bytes_bitplane(M, K, N, 3)
+    assert L.qgemm_bitplane_a8(None, K, None, None, None, N, None, 0, K, N, 3, None, 0, None) == OK
+    assert L.qgemm_bitplane_a8(A, K, None, P, C, N, None, M, K, N, 3, W, ws, None) == ERR_NULL   # a_scale
+    assert L.qgemm_bitplane_a8(A, K, S, P, C, N, None, M, K, N, 0, W, ws, None) == ERR_RANGE
+    assert L.qgemm_bitplane_a8(A, K + 8, S, P, C, N, None, M, K, N, 3, W, ws, None) == ERR_ALIGN
+    assert L.qgemm_bitplane_a8(A, K, S, P, C, N, _fake(0x30000000), M, K, N, 3, W, ws, None) == ERR_ALIAS
+    nb = qg.packed_bytes_bitplane(K, N, 3)
+    assert L.qgemm_bitplane_repack(K, N, 3, None, S, P, nb, None) == ERR_NULL
+    assert L.qgemm_bitplane_repack(K, N, 3, A, S, P, nb - 256, None) == ERR_SIZE
+    assert L.qgemm_bitplane_repack(K, N, 9, A, S, P, nb, None) == ERR_RANGE
+    st = L.qgemm_bitplane_a8(A, K, S, P, C, N, None, M, K, N, 3, W, ws, None)
+    if st != OK:
+        assert st in (ERR_HIP, ERR_DEV)
