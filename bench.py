@@ -64,14 +64,18 @@ def kernel_label(pl: dict) -> str:
     return f"skinny_gemm_kp{pl['wpt'] // 4}<{policy},{pl['mb']},{pl['nb']}>"
 
 
+# sources of the W4A16 kernels the sweep launches (and their planner)
+W4A16_SOURCES = ("api.cpp", "qgemm_device.h", "qgemm_internal.h", "skinny.h", "w4a16.hip", "wide.hip")
+
+
 def source_sha() -> str:
-    """Hash of the kernel and planner sources with comments and blank lines
-    removed: HBM byte counters taken on other code are not reported."""
+    """Hash of the W4A16 kernel and planner sources with comments and blank
+    lines removed: HBM byte counters taken on other code are not reported."""
     import hashlib
     import re
     d = os.path.join(ROOT, "bit_weight_quantized_qgemm_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
+    for f in sorted(W4A16_SOURCES):
         with open(os.path.join(d, f)) as fh:
             txt = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
         txt = re.sub(r"//[^\n]*", "", txt)
