@@ -226,6 +226,9 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
         wait_vmcnt<kAfter>();
         raw_barrier();
         issue_a(wl(i + 2), (r + 2) % kAS);
+        // the count above relies on this order (activations, then weights):
+        // keep the compiler from issuing the weight loads first
+        __builtin_amdgcn_sched_barrier(0);
         v.load_vmem(st[(r + kWD) % kWS], wl(i + kWD));
         __builtin_amdgcn_sched_barrier(0);
         v.load_lds(st[(r + kWD) % kWS], wl(i + kWD));
@@ -280,16 +283,25 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
     }
   }
   if (!workgroup_arrive_last(p.counters + tile_id, (uint32_t)p.splits, flag)) return;
+  constexpr int kBatch = 8;   // splits whose loads are in flight together
   for (int e4 = tid; e4 < kTileElems / 4; e4 += KP * 256) {
     E s[4] = {0, 0, 0, 0};
-    for (int q = 0; q < p.splits; ++q) {
-      const f32x4 x = load16_coherent(region(q), e4 * 16u);
+    for (int q0 = 0; q0 < p.splits; q0 += kBatch) {
+      f32x4 x[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // copy the lane out first: this compiler's bit_cast of a vector-element
-        // lvalue reads element 0 whatever the index
-        const float xi = x[i];
-        s[i] += __builtin_bit_cast(E, xi);
+      for (int u = 0; u < kBatch; ++u) x[u] = load16_coherent(region(min(q0 + u, p.splits - 1)), e4 * 16u);
+      // in split order; splits past the last were re-reads and add nothing
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (q0 + u < p.splits) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // copy the lane out first: this compiler's bit_cast of a vector-element
+            // lvalue reads element 0 whatever the index
+            const float xi = x[u][i];
+            s[i] += __builtin_bit_cast(E, xi);
+          }
+        }
       }
     }
     const int ln = e4 & 63, fj = e4 >> 6;

@@ -179,6 +179,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
       wait_vmcnt<kAfter>();
       raw_barrier();
       issue_a(min(i + kDepth, ng - 1), (r + kDepth) % kASlots);
+      // the count above relies on this order (activations, then weights)
+      __builtin_amdgcn_sched_barrier(0);
       issue_b(st[(r + kDepth) % kASlots], min(i + kDepth, ng - 1));
       __builtin_amdgcn_sched_barrier(0);
       if (i < ng) {
@@ -262,21 +264,33 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
     for (int jb = 0; jb < kWideJB; ++jb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rb][jb][i] = 0.f;
-  for (int q = 0; q < p.splits; ++q) {
-    const rsrc_t rq = region(q);
+  // two splits' loads in flight at a time (a split past the last re-reads the
+  // last and adds nothing); the sum stays in split order
+  for (int q = 0; q < p.splits; q += 2) {
+    const rsrc_t r0 = region(q), r1 = region(min(q + 1, p.splits - 1));
+    const bool has1 = q + 1 < p.splits;
+    f32x4 v0[R32][kWideJB][4], v1[R32][kWideJB][4];
 #pragma unroll
     for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
       for (int jb = 0; jb < kWideJB; ++jb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 v = load16_coherent(rq, voff(rb, jb, q4));
+          v0[rb][jb][q4] = load16_coherent(r0, voff(rb, jb, q4));
+          v1[rb][jb][q4] = load16_coherent(r1, voff(rb, jb, q4));
+        }
+#pragma unroll
+    for (int rb = 0; rb < R32; ++rb)
+#pragma unroll
+      for (int jb = 0; jb < kWideJB; ++jb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float ve = v[e];
-            acc[rb][jb][4 * q4 + e] += ve;
+            const float a0 = v0[rb][jb][q4][e], a1 = v1[rb][jb][q4][e];
+            acc[rb][jb][4 * q4 + e] += a0;
+            if (has1) acc[rb][jb][4 * q4 + e] += a1;
           }
-        }
   }
   store_tile();
 }
