@@ -57,6 +57,13 @@ struct Plan {
 
 // bits: planes per weight of the bit-plane format (ignored by the others)
 Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits = 4);
+struct KernelOccupancy {
+  int waves_per_simd;
+  bool spills;
+};
+// register-limited occupancy of a streaming-kernel instance (tile 16*mb x 64*nb,
+// kp waves per SIMD per workgroup)
+KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits);
 
 // Arguments of every GEMM kernel (passed by value).
 struct GemmArgs {

@@ -289,6 +289,13 @@ int qgemm_bitplane_a8(const void* A, int64_t lda, const void* a_scale, const voi
 int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 
 /*
+ * The work decomposition of a bit-plane W_b A8 call (qgemm_bitplane_a8) of
+ * this shape and bit width, in the layout of qgemm_plan. bits outside 1..8:
+ * QGEMM_ERR_RANGE; shape rules as for qgemm_bitplane_a8. Host-only; no HIP call.
+ */
+int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* out10);
+
+/*
  * Override the automatic plan for later calls of this process: kernel (1 =
  * streaming kernel for every format, 2 = wide W4A16 kernel for N a multiple of
  * 256; other cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or

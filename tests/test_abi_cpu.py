@@ -350,3 +350,23 @@ def test_bitplane_validation_without_gpu(L):
     st = L.qgemm_bitplane_a8(A, K, S, P, C, N, None, M, K, N, 3, W, ws, None)
     if st != OK:
         assert st in (ERR_HIP, ERR_DEV)
+
+
+def test_bitplane_plan_validation(L):
+    out = (ctypes.c_int64 * 10)()
+    assert L.qgemm_bitplane_plan(16, 4096, 4096, 0, out) == ERR_RANGE
+    assert L.qgemm_bitplane_plan(16, 4096, 4096, 9, out) == ERR_RANGE
+    assert L.qgemm_bitplane_plan(16, 4096, 4096, 4, None) == ERR_NULL
+    assert L.qgemm_bitplane_plan(0, 4096, 4096, 4, out) == ERR_SHAPE
+    assert L.qgemm_bitplane_plan(16, 65536 + 128, 64, 4, out) == ERR_SHAPE
+    assert L.qgemm_bitplane_plan(16, 4096, 4096 + 32, 4, out) == ERR_SHAPE
+
+
+@pytest.mark.parametrize("bits", [1, 2, 4, 6, 8])
+@pytest.mark.parametrize("K,N", [(1024, 1024), (4096, 11008), (11008, 4096), (8192, 28672), (28672, 8192)])
+@pytest.mark.parametrize("M", [1, 16, 32, 64, 128])
+def test_bitplane_plan_covers_every_unit_once(K, N, M, bits):
+    p = qg.plan(qg.FMT_BITPLANE, M, K, N, bits=bits)
+    assert p["kernel"] == 1
+    _check_plan(p, M, K, N, ws=qg.workspace_bytes_bitplane(M, K, N, bits))
+
