@@ -203,11 +203,11 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
 // general-grid entries are the minimum over its four variants (fp16 / bf16,
 // with or without zero points), the bit-plane rows are b = 1..8.
 namespace {
-const char* const kOccW4A16 = "888555677666";   // 32-row two-block tiles: the M32 policy
+const char* const kOccW4A16 = "888555666555";   // 32-row two-block tiles: the M32 policy
 const char* const kOccW4A8 = "888566666444";
-const char* const kOccW2W4 = "77744456633d";
-const char* const kOccW4G = "55544444423d";
-const char* const kOccSP24 = "777555555444";
+const char* const kOccW2W4 = "67744455533d";
+const char* const kOccW4G = "55544434423d";
+const char* const kOccSP24 = "666555555444";
 const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455344",
                                "677555444234", "56644434433d", "55544434432d", "55534423d12d"};
 }  // namespace

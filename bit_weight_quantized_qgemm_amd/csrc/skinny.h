@@ -99,6 +99,23 @@ struct Tile16 {
   __device__ static int col_of(int, int j, int, int ln) { return j * 16 + (ln & 15); }
 };
 
+// fp16 / bf16 activation slots in LDS: [rows][128 k], 256 B per row, with the
+// 16-byte chunk c (k = 8c .. 8c + 7) of row r at chunk position c ^ (r & 15).
+// Each direct-to-LDS load moves four whole rows (lane j: row 4*fr + j/16,
+// position j % 16), i.e. 1 KB in 8 full cache lines, where MFMA operand order
+// would touch 16 or 32 rows per load; the operand reads, whose lanes take 16
+// or 32 consecutive rows at one chunk, see 16 distinct positions per 16 rows,
+// so they stay free of bank conflicts.
+struct ARows16 {
+  // byte offset in A (row stride arow bytes) of this lane's 16 bytes of load fr
+  __device__ static uint32_t dma_voff(int fr, int lane, int rows, size_t arow) {
+    const int r = 4 * fr + (lane >> 4);
+    return (uint32_t)((size_t)min(r, rows - 1) * arow + (uint32_t)(((lane & 15) ^ (r & 15)) << 4));
+  }
+  // the 8 activations of row r, chunk c of a slot
+  __device__ static const char* at(const char* slot, int r, int c) { return slot + r * 256 + ((c ^ (r & 15)) << 4); }
+};
+
 // LDS layout of a launch: [scales | extra | A rings (KP x 3 slots)]; the
 // reduction buffer reuses the start of LDS after the main loop.
 struct SkinnyLds {

@@ -42,7 +42,7 @@ struct PolicySP24 {
   static constexpr bool kStageScales = true;
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
-    return Tile16::a_voff16<kFrag>(fr, lane, rows, arow);
+    return ARows16::dma_voff(fr, lane, rows, arow);
   }
   // transposed result: element i of lane ln is column 4*(ln/16) + i, row ln % 16
   __device__ static int row_of(int mb, int, int, int ln) { return mb * 16 + (ln & 15); }
@@ -111,8 +111,9 @@ struct PolicySP24 {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const f16x8 lo = *reinterpret_cast<const f16x8*>(aslot + (mb * 4 + 2 * st) * 1024 + lane * 16);
-        const f16x8 hi = *reinterpret_cast<const f16x8*>(aslot + (mb * 4 + 2 * st + 1) * 1024 + lane * 16);
+        const int r = mb * 16 + (lane & 15);
+        const f16x8 lo = *reinterpret_cast<const f16x8*>(ARows16::at(aslot, r, 8 * st + (lane >> 4)));
+        const f16x8 hi = *reinterpret_cast<const f16x8*>(ARows16::at(aslot, r, 8 * st + 4 + (lane >> 4)));
         a[mb][st] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
       }
 #pragma unroll

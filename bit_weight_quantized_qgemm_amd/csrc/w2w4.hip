@@ -29,7 +29,7 @@ struct PolicyW2W4 : Tile16 {
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
-    return a_voff16<kFrag>(fr, lane, rows, arow);
+    return ARows16::dma_voff(fr, lane, rows, arow);
   }
 
   struct Consts {
@@ -127,7 +127,8 @@ struct PolicyW2W4 : Tile16 {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[mb][t] = *reinterpret_cast<const f16x8*>(aslot + (mb * 4 + t) * 1024 + lane * 16);
+      for (int t = 0; t < 4; ++t)
+        a[mb][t] = *reinterpret_cast<const f16x8*>(ARows16::at(aslot, mb * 16 + (lane & 15), 4 * t + (lane >> 4)));
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const float sc = valid ? half_of(cur.s[j], 0) : 0.f;

@@ -3,7 +3,7 @@
 //
 // Per group and lane: one 16-byte weight load per 16-column block (the blob is in
 // v_mfma_f32_16x16x32_f16 B-operand order, one fully coalesced 1 KB wave load),
-// the four A fragments per 16-row block from the workgroup's LDS ring, and the
+// the four A operands per 16-row block from the workgroup's LDS ring, and the
 // lane's group scale from LDS. Dequantization: 9 VALU ops per 8 weights produce exact fp16 (q - 8)
 // (dequant_u4x8); the fp32 MFMA partial of the group is scaled once
 // (acc += s * partial), so the result is sum_g s[g,n] * sum_k A[m,k] (q[k,n] - 8)
@@ -22,7 +22,7 @@ struct PolicyW4A16 : Tile16 {
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
-    return a_voff16<kFrag>(fr, lane, rows, arow);
+    return ARows16::dma_voff(fr, lane, rows, arow);
   }
 
   struct Consts {
@@ -86,7 +86,8 @@ struct PolicyW4A16 : Tile16 {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[mb][t] = *reinterpret_cast<const f16x8*>(aslot + (mb * 4 + t) * 1024 + lane * 16);
+      for (int t = 0; t < 4; ++t)
+        a[mb][t] = *reinterpret_cast<const f16x8*>(ARows16::at(aslot, mb * 16 + (lane & 15), 4 * t + (lane >> 4)));
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const float sc = valid ? half_of(cur.s[j], 0) : 0.f;
@@ -130,7 +131,7 @@ struct PolicyW4A16M32 {
   typedef float f32x16 __attribute__((ext_vector_type(16)));
 
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
-    return (uint32_t)((size_t)min(lane & 31, rows - 1) * arow + 32 * fr + 16 * (lane >> 5));
+    return ARows16::dma_voff(fr, lane, rows, arow);
   }
   __device__ static int row_of(int mb, int j, int i, int ln) { return 8 * (mb * 2 + j) + 4 * (ln >> 5) + i; }
   __device__ static int col_of(int, int, int, int ln) { return ln & 31; }
@@ -186,7 +187,7 @@ struct PolicyW4A16M32 {
     for (int e = 0; e < 16; ++e) part[e] = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(aslot + u * 1024 + lane * 16);
+      const f16x8 a = *reinterpret_cast<const f16x8*>(ARows16::at(aslot, lane & 31, 2 * u + (lane >> 5)));
       const f16x8 b = dequant_u4x8((u & 1) ? cur.odd[u >> 1] : cur.even[u >> 1], k.lo_off, k.hi_off, k.magic);
       part = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, part, 0, 0, 0);
     }

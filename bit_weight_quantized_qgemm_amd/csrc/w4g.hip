@@ -44,7 +44,7 @@ struct PolicyW4G : Tile16 {
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   static constexpr uint32_t kEntry = kZ ? 4u : 2u;   // bytes per grid entry
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
-    return a_voff16<kFrag>(fr, lane, rows, arow);
+    return ARows16::dma_voff(fr, lane, rows, arow);
   }
 
   struct Consts {
@@ -125,7 +125,8 @@ struct PolicyW4G : Tile16 {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[mb][t] = *reinterpret_cast<const u32x4*>(aslot + (mb * 4 + t) * 1024 + lane * 16);
+      for (int t = 0; t < 4; ++t)
+        a[mb][t] = *reinterpret_cast<const u32x4*>(ARows16::at(aslot, mb * 16 + (lane & 15), 4 * t + (lane >> 4)));
     if constexpr (!kBF16) {
       const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
 #pragma unroll

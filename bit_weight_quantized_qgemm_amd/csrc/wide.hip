@@ -18,9 +18,10 @@
 //     so every lane fetches two 16-byte pieces per 32-column block and group
 //     (its "even" and "odd" k-steps) at lane-dependent offsets - each byte of
 //     the chunk pair is still loaded exactly once per wave;
-//   * per group of 128 k the tile's activations arrive in 32x32x16 A-operand
-//     order (1 KB per 32 rows x 16 k) by direct buffer-to-LDS loads, issued
-//     kDepth groups ahead into an LDS ring, each wave fetching an eighth; one
+//   * per group of 128 k the tile's activations arrive as whole rows (the
+//     swizzled row-major slot of ARows16, four rows per 1 KB load) by direct
+//     buffer-to-LDS loads, issued kDepth groups ahead into an LDS ring, each
+//     wave fetching an eighth; one
 //     barrier per group publishes a slot after the wave's own loads of it are
 //     counted complete (s_waitcnt on the in-order vector memory counter), and the
 //     slot written next is the one all waves finished reading before that
@@ -82,15 +83,14 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   // activations: rows of the tile from k = 128*G0; rows beyond M re-read a valid row
   const rsrc_t ra = make_rsrc(static_cast<const f16*>(p.A) + (size_t)row0 * p.lda + (size_t)G0 * kGroup,
                               (uint32_t)(((size_t)(rows - 1) * p.lda + (size_t)ng * kGroup) * 2));
-  // fragment f = rb32 * 8 + u (32 rows x 16 k); this wave fetches f = wave*kAPerWave ..
+  // load f moves rows 4f .. 4f + 3 of the group (1 KB); this wave issues f = wave*kAPerWave ..
   uint32_t avoff[kAPerWave];
   int afrag[kAPerWave];
 #pragma unroll
   for (int q = 0; q < kAPerWave; ++q) {
     const int f = wave * kAPerWave + q;
-    const int rb32 = f >> 3, u = f & 7;
     afrag[q] = f;
-    avoff[q] = (uint32_t)((size_t)min(rb32 * 32 + c32, rows - 1) * p.lda * 2 + u * 32 + hh * 16);
+    avoff[q] = ARows16::dma_voff(f, lane, rows, (size_t)p.lda * 2);
   }
   auto issue_a = [&](int rel, int slot) {
 #pragma unroll
@@ -168,7 +168,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   auto read_a = [&](const char* slot, int u, f16x8 (&a)[R32]) {
 #pragma unroll
     for (int rb = 0; rb < R32; ++rb)
-      a[rb] = *reinterpret_cast<const f16x8*>(slot + ((wr * R32 + rb) * 8 + u) * 1024 + lane * 16);
+      a[rb] = *reinterpret_cast<const f16x8*>(ARows16::at(slot, (wr * R32 + rb) * 32 + c32, 2 * u + hh));
   };
 
   for (int base = 0; base < ng; base += kASlots) {
