@@ -204,12 +204,12 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
 // with or without zero points), the bit-plane rows are b = 1..8.
 namespace {
 const char* const kOccW4A16 = "888555666555";   // 32-row two-block tiles: the M32 policy
-const char* const kOccW4A8 = "888566666444";
+const char* const kOccW4A8 = "888666666444";
 const char* const kOccW2W4 = "67744455533d";
 const char* const kOccW4G = "55544434423d";
 const char* const kOccSP24 = "666555555444";
-const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455344",
-                               "677555444234", "56644434433d", "55544434432d", "55534423d12d"};
+const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455444",
+                               "67755544433d", "56645534433d", "55544434433d", "55544423d13d"};
 }  // namespace
 
 KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits) {

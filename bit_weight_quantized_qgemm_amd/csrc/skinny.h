@@ -86,15 +86,10 @@ __device__ __forceinline__ void stage_scales(const void* scales, char* lds, int 
   }
 }
 
-// Geometry shared by the policies built on 16 x 16 MFMA tiles: A fragment fr
-// (16 rows x one k-step) of a 16-row block, and the position (row_of, col_of)
-// of accumulator element i of lane ln in fragment (mb, j) of a wave's tile.
+// Geometry shared by the policies built on 16 x 16 MFMA tiles: the position
+// (row_of, col_of) of accumulator element i of lane ln in fragment (mb, j) of
+// a wave's tile.
 struct Tile16 {
-  template <int kFrag>
-  __device__ static uint32_t a_voff16(int fr, int lane, int rows, size_t arow) {
-    const int rb = fr / kFrag, f = fr % kFrag;
-    return (uint32_t)((size_t)min(rb * 16 + (lane & 15), rows - 1) * arow + 64 * f + 16 * (lane >> 4));
-  }
   __device__ static int row_of(int mb, int, int i, int ln) { return mb * 16 + 4 * (ln >> 4) + i; }
   __device__ static int col_of(int, int j, int, int ln) { return j * 16 + (ln & 15); }
 };
@@ -114,6 +109,20 @@ struct ARows16 {
   }
   // the 8 activations of row r, chunk c of a slot
   __device__ static const char* at(const char* slot, int r, int c) { return slot + r * 256 + ((c ^ (r & 15)) << 4); }
+};
+
+// int8 activation slots: [rows][128 k], 128 B per row, chunk c at position
+// c ^ ((r >> 1) & 7); a 1 KB load moves eight whole rows (lane j: row
+// 8*fr + j/8, position j % 8), and the 16x16x64 operand reads (16 rows at one
+// chunk) cover all 64 banks once.
+struct ARows8 {
+  __device__ static uint32_t dma_voff(int fr, int lane, int rows, size_t arow) {
+    const int r = 8 * fr + (lane >> 3);
+    return (uint32_t)((size_t)min(r, rows - 1) * arow + (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4));
+  }
+  __device__ static const char* at(const char* slot, int r, int c) {
+    return slot + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+  }
 };
 
 // LDS layout of a launch: [scales | extra | A rings (KP x 3 slots)]; the

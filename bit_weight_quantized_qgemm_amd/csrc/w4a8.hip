@@ -27,7 +27,7 @@ struct PolicyW4A8 : Tile16 {
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
   __device__ static uint32_t a_voff(int fr, int lane, int rows, size_t arow) {
-    return a_voff16<kFrag>(fr, lane, rows, arow);
+    return ARows8::dma_voff(fr, lane, rows, arow);
   }
 
   struct Consts {};
@@ -82,7 +82,8 @@ struct PolicyW4A8 : Tile16 {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) a[mb][u] = *reinterpret_cast<const i32x4*>(aslot + (mb * 2 + u) * 1024 + lane * 16);
+      for (int u = 0; u < 2; ++u)
+        a[mb][u] = *reinterpret_cast<const i32x4*>(ARows8::at(aslot, mb * 16 + (lane & 15), 4 * u + (lane >> 4)));
     i32x4 rsum[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
