@@ -59,7 +59,7 @@ def alg_flops(M, K, N):
 def kernel_label(pl: dict) -> str:
     """Name of the HIP kernel a plan launches (as rocprofv3 lists it, shortened)."""
     if pl["kernel"] == 2:
-        return f"w4a16_wide_m{16 * pl['mb']}"
+        return f"w4a16_wide_m{16 * pl['mb']}" + ("_kp2" if pl["wpt"] == 16 else "")
     policy = "PolicyW4A16M32" if (pl["mb"], pl["nb"]) == (2, 2) else "PolicyW4A16"
     return f"skinny_gemm_kp{pl['wpt'] // 4}<{policy},{pl['mb']},{pl['nb']}>"
 

@@ -262,6 +262,10 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
       }
     }
   }
+  // The last iterations left loads in flight: activation DMA into the ring,
+  // then Stage::kVmem weight loads whose values are never used. The counter
+  // retires in order, so this retires every DMA write before LDS is reused.
+  wait_vmcnt<Stage::kVmem>();
   __syncthreads();   // all LDS reads done: reuse LDS for the reduction
 
   // ---- reduce the KP K-parts in K-part order; fragment (wave, mb, j) = 1 KB

@@ -54,7 +54,7 @@ struct WideStage {
 
 }  // namespace
 
-template <int MBW, int NWC>
+template <int MBW, int NWC, int KPW>
 __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* flag) {
   constexpr int NWR = kWideWaves / NWC;             // row waves
   constexpr int kWideJB = kWideCols / 32 / NWC;     // 32-column blocks per wave
@@ -66,15 +66,23 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   using Stage = WideStage<kWideJB>;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kpi = wave_all / kWideWaves;             // K-part of this wave
+  const int wave = wave_all % kWideWaves;            // wave within its K-part
   const int wc = wave % NWC, wr = wave / NWC;
   const int c32 = lane & 31, hh = lane >> 5;
   const int nt = blockIdx.x % p.nt;
   const int rest = blockIdx.x / p.nt;
   const int mt = rest % p.mt;
   const int split = rest / p.mt;
-  const int G0 = split * p.gps;
-  const int ng = min(p.G, G0 + p.gps) - G0;
+  const int G0s = split * p.gps;
+  const int ngw = min(p.G, G0s + p.gps) - G0s;
+  // this K-part's groups [G0, G0 + ng); every K-part runs `iters` iterations
+  const int iters = (ngw + KPW - 1) / KPW;
+  const int gk0 = G0s + kpi * iters;
+  const int ng = max(0, min(G0s + ngw - gk0, iters));
+  const int nload = max(ng, 1);                      // clamp target for reloads
+  const int G0 = ng > 0 ? gk0 : G0s;                 // an empty K-part re-reads the first group
   const int row0 = mt * MBW * 16;
   const int rows = min(MBW * 16, p.M - row0);
   const int bw = nt * (kWideCols / 16) + wc * 2 * kWideJB;     // first 16-column block of the wave
@@ -82,7 +90,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
 
   // activations: rows of the tile from k = 128*G0; rows beyond M re-read a valid row
   const rsrc_t ra = make_rsrc(static_cast<const f16*>(p.A) + (size_t)row0 * p.lda + (size_t)G0 * kGroup,
-                              (uint32_t)(((size_t)(rows - 1) * p.lda + (size_t)ng * kGroup) * 2));
+                              (uint32_t)(((size_t)(rows - 1) * p.lda + (size_t)nload * kGroup) * 2));
   // load f moves rows 4f .. 4f + 3 of the group (1 KB); this wave issues f = wave*kAPerWave ..
   uint32_t avoff[kAPerWave];
   int afrag[kAPerWave];
@@ -92,17 +100,18 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
     afrag[q] = f;
     avoff[q] = ARows16::dma_voff(f, lane, rows, (size_t)p.lda * 2);
   }
+  char* ring = lds + kpi * kASlots * kSlotBytes;     // this K-part's activation ring
   auto issue_a = [&](int rel, int slot) {
 #pragma unroll
     for (int q = 0; q < kAPerWave; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + slot * kSlotBytes + afrag[q] * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ring + slot * kSlotBytes + afrag[q] * 1024), 16,
                                                avoff[q], rel * 256u, 0, 0);
   };
 
   // weights and scales of this wave's 32-column blocks (group-major chunks)
   const uint32_t gstep = (uint32_t)(p.N / 16) * 1024u;
   const rsrc_t rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)G0 * (p.N / 16) + bw) * 1024,
-                              (uint32_t)(ng - 1) * gstep + 2 * kWideJB * 1024u);
+                              (uint32_t)(nload - 1) * gstep + 2 * kWideJB * 1024u);
   uint32_t cvoff[kWideJB];
 #pragma unroll
   for (int jb = 0; jb < kWideJB; ++jb)
@@ -147,9 +156,9 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   Stage st[kASlots];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
-    issue_a(min(d, ng - 1), d);
+    issue_a(min(d, nload - 1), d);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b(st[d], min(d, ng - 1));
+    issue_b(st[d], min(d, nload - 1));
     __builtin_amdgcn_sched_barrier(0);
   }
   constexpr int kAfter = kBPerGroup + (kDepth - 1) * (kAPerWave + kBPerGroup);
@@ -171,21 +180,21 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
       a[rb] = *reinterpret_cast<const f16x8*>(ARows16::at(slot, (wr * R32 + rb) * 32 + c32, 2 * u + hh));
   };
 
-  for (int base = 0; base < ng; base += kASlots) {
+  for (int base = 0; base < iters; base += kASlots) {
 #pragma unroll
     for (int r = 0; r < kASlots; ++r) {
       const int i = base + r;
       // raw_barrier(): publishes only the counted completion above (see skinny.h)
       wait_vmcnt<kAfter>();
       raw_barrier();
-      issue_a(min(i + kDepth, ng - 1), (r + kDepth) % kASlots);
+      issue_a(min(i + kDepth, nload - 1), (r + kDepth) % kASlots);
       // the count above relies on this order (activations, then weights)
       __builtin_amdgcn_sched_barrier(0);
-      issue_b(st[(r + kDepth) % kASlots], min(i + kDepth, ng - 1));
+      issue_b(st[(r + kDepth) % kASlots], min(i + kDepth, nload - 1));
       __builtin_amdgcn_sched_barrier(0);
       if (i < ng) {
         const Stage& cur = st[r];
-        const char* slot = lds + r * kSlotBytes;
+        const char* slot = ring + r * kSlotBytes;
         // software pipeline over the 8 k-steps: the fragments and dequantized
         // weights of step u+1 are fetched while the MFMAs of step u run
         f16x8 a[2][R32], bf[2][kWideJB];
@@ -207,7 +216,45 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
     }
   }
 
-  // ---- epilogue: element i of lane l is row 8*(i/4) + 4*hh + i%4 of the 32-row
+  if constexpr (KPW > 1) {
+    // The last iterations left loads in flight: activation DMA into the ring,
+    // then kBPerGroup weight and scale loads whose values are never used; the
+    // counter retires in order, so this retires every DMA write before LDS is
+    // reused. K-parts 1.. then publish their accumulators and K-part 0 adds
+    // them in K-part order.
+    wait_vmcnt<kBPerGroup>();
+    __syncthreads();
+    constexpr int kAcc4 = R32 * kWideJB * 4;         // f32x4 per lane
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    auto at = [&](int q, int e4) -> f32x4& { return red[(((q - 1) * kWideWaves + wave) * kAcc4 + e4) * 64 + lane]; };
+    if (kpi > 0) {
+#pragma unroll
+      for (int rb = 0; rb < R32; ++rb)
+#pragma unroll
+        for (int jb = 0; jb < kWideJB; ++jb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            at(kpi, (rb * kWideJB + jb) * 4 + q4) = f32x4{acc[rb][jb][4 * q4], acc[rb][jb][4 * q4 + 1],
+                                                          acc[rb][jb][4 * q4 + 2], acc[rb][jb][4 * q4 + 3]};
+    }
+    __syncthreads();
+    if (kpi == 0) {
+#pragma unroll
+      for (int q = 1; q < KPW; ++q)
+#pragma unroll
+        for (int rb = 0; rb < R32; ++rb)
+#pragma unroll
+          for (int jb = 0; jb < kWideJB; ++jb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4 v = at(q, (rb * kWideJB + jb) * 4 + q4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[rb][jb][4 * q4 + e] += v[e];
+            }
+    }
+  }
+
+  // ---- epilogue (K-part 0): element i of lane l is row 8*(i/4) + 4*hh + i%4 of the 32-row
   // block, column c32 of the 32-column block
   auto store_tile = [&]() {
     f16* C = static_cast<f16*>(p.C);
@@ -224,7 +271,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
       }
   };
   if (p.splits == 1) {
-    store_tile();
+    if (kpi == 0) store_tile();
     return;
   }
   // Cross-workgroup split: partials in accumulator order, four 1 KB pieces per
@@ -241,7 +288,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   auto voff = [&](int rb, int jb, int q4) {
     return (uint32_t)((((wave * R32 + rb) * kWideJB + jb) * 4 + q4) * 1024 + lane * 16);
   };
-  {
+  if (kpi == 0) {
     const rsrc_t mine = region(split);
 #pragma unroll
     for (int rb = 0; rb < R32; ++rb)
@@ -254,7 +301,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
           store16_coherent(v, mine, voff(rb, jb, q4));
         }
   }
-  if (!workgroup_arrive_last(p.counters + tile_id, (uint32_t)p.splits, flag)) return;
+  // every wave takes part in the arrival barriers; only K-part 0 continues
+  if (!workgroup_arrive_last(p.counters + tile_id, (uint32_t)p.splits, flag) || kpi > 0) return;
   // last arriver: sum the splits in split order (deterministic), then store fp16
   // (measured faster than prefetching the next split or reusing the own partial
   // from registers, which raise register pressure)
@@ -264,33 +312,35 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
     for (int jb = 0; jb < kWideJB; ++jb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[rb][jb][i] = 0.f;
-  // two splits' loads in flight at a time (a split past the last re-reads the
-  // last and adds nothing); the sum stays in split order
-  for (int q = 0; q < p.splits; q += 2) {
-    const rsrc_t r0 = region(q), r1 = region(min(q + 1, p.splits - 1));
-    const bool has1 = q + 1 < p.splits;
-    f32x4 v0[R32][kWideJB][4], v1[R32][kWideJB][4];
+  // kEpi splits' loads in flight at a time (a split past the last re-reads the
+  // last and adds nothing); the sum stays in split order. The 16-wave build
+  // keeps one at a time to stay within 128 registers.
+  constexpr int kEpi = KPW == 1 ? 2 : 1;
+  for (int q = 0; q < p.splits; q += kEpi) {
+    f32x4 v[kEpi][R32][kWideJB][4];
 #pragma unroll
-    for (int rb = 0; rb < R32; ++rb)
+    for (int u = 0; u < kEpi; ++u) {
+      const rsrc_t r = region(min(q + u, p.splits - 1));
 #pragma unroll
-      for (int jb = 0; jb < kWideJB; ++jb)
+      for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          v0[rb][jb][q4] = load16_coherent(r0, voff(rb, jb, q4));
-          v1[rb][jb][q4] = load16_coherent(r1, voff(rb, jb, q4));
-        }
+        for (int jb = 0; jb < kWideJB; ++jb)
 #pragma unroll
-    for (int rb = 0; rb < R32; ++rb)
+          for (int q4 = 0; q4 < 4; ++q4) v[u][rb][jb][q4] = load16_coherent(r, voff(rb, jb, q4));
+    }
 #pragma unroll
-      for (int jb = 0; jb < kWideJB; ++jb)
+    for (int u = 0; u < kEpi; ++u) {
+      const bool has = q + u < p.splits;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
+      for (int rb = 0; rb < R32; ++rb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a0 = v0[rb][jb][q4][e], a1 = v1[rb][jb][q4][e];
-            acc[rb][jb][4 * q4 + e] += a0;
-            if (has1) acc[rb][jb][4 * q4 + e] += a1;
-          }
+        for (int jb = 0; jb < kWideJB; ++jb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (has) acc[rb][jb][4 * q4 + e] += v[u][rb][jb][q4][e];
+    }
   }
   store_tile();
 }
@@ -298,32 +348,43 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
 __global__ void __launch_bounds__(512) w4a16_wide_m64(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int flag;
-  wide_body<4, 8>(p, lds, &flag);   // eight column waves of 32 columns
+  wide_body<4, 8, 1>(p, lds, &flag);   // eight column waves of 32 columns
+}
+
+// the same tile with two K-parts of eight waves (four waves per SIMD)
+__global__ void __launch_bounds__(1024) w4a16_wide_m64_kp2(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int flag;
+  wide_body<4, 8, 2>(p, lds, &flag);
 }
 
 
 
 namespace {
 
-hipError_t launch_wide_k(const void* fn, void (*kernel)(GemmArgs), int mbw, const Plan& pl,
-                         const GemmArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)kASlots * mbw * 4 * 1024;
-  // the LDS size is fixed per kernel: opt in to it (above 64 KiB) once
+// KPW K-parts of eight waves; the LDS size is fixed per kernel: opt in to it
+// (above 64 KiB) once per kernel
+template <int KPW>
+hipError_t launch_wide_k(void (*kernel)(GemmArgs), int mbw, const Plan& pl, const GemmArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)KPW * kASlots * mbw * 4 * 1024;
   static std::atomic<bool> done{false};
   if (!done.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     done.store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * kWideWaves), lds, s, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * kWideWaves * KPW), lds, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s) {
-  switch (pl.mb) {
-    case 4: return launch_wide_k(reinterpret_cast<const void*>(&w4a16_wide_m64), w4a16_wide_m64, 4, pl, a, s);
+  if (pl.mb != 4) return hipErrorInvalidValue;
+  switch (pl.wpt) {
+    case 8: return launch_wide_k<1>(w4a16_wide_m64, 4, pl, a, s);
+    case 16: return launch_wide_k<2>(w4a16_wide_m64_kp2, 4, pl, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -299,7 +299,8 @@ int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* 
  * Override the automatic plan for later calls of this process: kernel (1 =
  * streaming kernel for every format, 2 = wide W4A16 kernel for N a multiple of
  * 256; other cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or
- * 2; 4 is taken as 2), waves per workgroup of kernel 1 (4, 8 or 16) and
+ * 2; 4 is taken as 2), waves per workgroup (kernel 1: 4, 8 or 16; kernel 2:
+ * 16 runs two K-parts of 8 waves, 4 or 8 one part of 8) and
  * k-splits across workgroups (1..4096); 0 keeps the automatic choice for that
  * field. Values a shape cannot use are clamped (no more K-parts than groups).
  * For tests of the split-K reductions and for tuning sweeps; affects

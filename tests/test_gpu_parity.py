@@ -350,27 +350,34 @@ def test_workspace_shared_across_plans():
 
 
 # ----------------------------------------------------------------------------- wide W4A16 kernel
+# waves per workgroup of the wide kernel: 8, or 16 as two K-parts of 8
+WIDE_WAVES = [8, 16]
+
+
+@pytest.mark.parametrize("wpt", WIDE_WAVES)
 @pytest.mark.parametrize("M,K,N,splits", [(48, 1024, 512, 0), (128, 2048, 256, 3), (130, 1280, 512, 0),
-                                          (64, 4096, 768, 5)])
-def test_w4a16_wide_one_hot_bit_exact(M, K, N, splits):
-    _say("w4a16 wide one-hot", M, K, N, splits)
+                                          (64, 4096, 768, 5), (48, 128, 256, 0), (40, 384, 256, 0)])
+def test_w4a16_wide_one_hot_bit_exact(M, K, N, splits, wpt):
+    _say("w4a16 wide one-hot", M, K, N, splits, wpt)
     rng = np.random.default_rng(M + K + N)
     p = gen.w4a16_problem(1, K, N, seed=M * 3 + 1, activations=False)
     A, ks = _one_hot(M, K, rng)
-    qg.set_plan_override(kernel=2, k_splits=splits)
-    assert qg.plan(qg.FMT_W4A16, M, K, N)["kernel"] == 2
+    qg.set_plan_override(kernel=2, k_splits=splits, waves_per_tile=wpt)
+    pl = qg.plan(qg.FMT_W4A16, M, K, N)
+    assert pl["kernel"] == 2 and pl["wpt"] == wpt
     C = qg.w4a16(_t(A), upload_w4a16(p), K, N).cpu().numpy()
     q = ref.unpack_u4(p["codes"])
     expect = ((q[ks] - 8).astype(np.float64) * p["scales"][ks // 128].astype(np.float64)).astype(np.float16)
     assert np.array_equal(C.view(np.uint16), expect.view(np.uint16))
 
 
+@pytest.mark.parametrize("wpt", WIDE_WAVES)
 @pytest.mark.parametrize("M", [1, 17, 33, 47, 64, 65, 100, 127, 128, 129, 200])
-def test_w4a16_wide_ragged(M):
+def test_w4a16_wide_ragged(M, wpt):
     K, N = 1280, 512                      # G = 10, two 256-column tiles
-    _say("w4a16 wide ragged", M, K, N)
+    _say("w4a16 wide ragged", M, K, N, wpt)
     p = gen.w4a16_problem(M, K, N, seed=M + 5)
-    qg.set_plan_override(kernel=2)
+    qg.set_plan_override(kernel=2, waves_per_tile=wpt)
     C1 = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N)
     C2 = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N)
     torch.cuda.synchronize()
@@ -378,14 +385,15 @@ def test_w4a16_wide_ragged(M):
     _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, ("wide", M))
 
 
+@pytest.mark.parametrize("wpt", WIDE_WAVES)
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
 @pytest.mark.parametrize("M", [40, 128])
-def test_w4a16_wide_forced_splits(splits, M):
+def test_w4a16_wide_forced_splits(splits, M, wpt):
     K, N = 4096, 512
-    _say("w4a16 wide splits", splits, M)
+    _say("w4a16 wide splits", splits, M, wpt)
     p = gen.w4a16_problem(M, K, N, seed=splits)
-    qg.set_plan_override(kernel=2, k_splits=splits)
+    qg.set_plan_override(kernel=2, k_splits=splits, waves_per_tile=wpt)
     pl = qg.plan(qg.FMT_W4A16, M, K, N)
-    assert pl["kernel"] == 2 and pl["splits"] == splits
+    assert pl["kernel"] == 2 and pl["splits"] == splits and pl["wpt"] == wpt
     C = qg.w4a16(_t(p["A"]), upload_w4a16(p), K, N).cpu().numpy()
     _ok(C, ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, ("wide splits", splits, M))
