@@ -34,7 +34,8 @@
 // and finished with the coherent-store / arrival-counter fix-up.
 #include "skinny.h"
 
-#include <atomic>
+#include <mutex>
+#include <set>
 
 namespace qg {
 namespace {
@@ -363,16 +364,23 @@ __global__ void __launch_bounds__(1024) w4a16_wide_m64_kp2(GemmArgs p) {
 namespace {
 
 // KPW K-parts of eight waves; the LDS size is fixed per kernel: opt in to it
-// (above 64 KiB) once per kernel
+// (above 64 KiB) once per kernel and device
 template <int KPW>
 hipError_t launch_wide_k(void (*kernel)(GemmArgs), int mbw, const Plan& pl, const GemmArgs& a, hipStream_t s) {
   const size_t lds = (size_t)KPW * kASlots * mbw * 4 * 1024;
-  static std::atomic<bool> done{false};
-  if (!done.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    done.store(true, std::memory_order_release);
+  static std::mutex mu;
+  static std::set<int> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (!done.count(dev)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+      if (e != hipSuccess) return e;
+      done.insert(dev);
+    }
   }
   hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * kWideWaves * KPW), lds, s, a);
   return hipGetLastError();
