@@ -31,7 +31,7 @@ struct PolicyBP : Tile16 {
   using Acc = i32x4;
   using Elem = int32_t;
   static constexpr int kScaleChunk = 0;
-  static constexpr int kFrag = 2;           // A fragments (16 rows x 64 k int8) per chunk
+  static constexpr int kFrag = 2;           // 1 KB activation loads per 16 rows and chunk
   static constexpr int kAElem = 1;
   static constexpr bool kStageScales = false;
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave

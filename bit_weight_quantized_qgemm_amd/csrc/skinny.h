@@ -8,10 +8,10 @@
 //   * its 4*KP waves form KP K-parts of 4 column waves: column wave n streams
 //     16*NBW columns, K-part k the k-th contiguous share of the tile's groups;
 //   * the 4 column waves of a K-part share the activations through LDS: each
-//     group's A fragments (16 rows x 32 fp16 or x 64 int8 k per KB, already in
-//     MFMA operand order) arrive by direct buffer-to-LDS loads two groups ahead
-//     into a 3-slot ring, each column wave fetching a quarter, published by one
-//     barrier per group;
+//     group's A rows (1 KB loads of 4 fp16 or 8 int8 whole rows, chunk-swizzled,
+//     see ARows16 / ARows8) arrive by direct buffer-to-LDS loads two groups
+//     ahead into a 3-slot ring, each column wave fetching a quarter, published
+//     by one barrier per group;
 //   * weights stream per wave into a 3-stage register ring, also two groups
 //     ahead, so every wave keeps two groups of loads in flight;
 //   * at the end the KP partial tiles are summed in LDS in K-part order
@@ -21,8 +21,8 @@
 //     with device-coherent 16-byte stores and loads and one arrival counter per
 //     tile; the last workgroup to arrive adds them in split order.
 //
-// A format policy F supplies the per-group weight stage (load and math), the A
-// fragment geometry and the output conversion. Group scales of the tile are
+// A format policy F supplies the per-group weight stage (load and math), the
+// activation slot layout and the output conversion. Group scales of the tile are
 // staged in LDS once per workgroup, after the first loads are already in flight.
 #pragma once
 
@@ -152,7 +152,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
   using Stage = typename F::template Stage<NBW>;
   using View = typename F::template View<NBW>;
   constexpr int NB = 4 * NBW;
-  constexpr int kFrags = MB * F::kFrag;          // A fragments per group per K-part
+  constexpr int kFrags = MB * F::kFrag;          // 1 KB activation loads per group per K-part
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -181,16 +181,16 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
   const int nload = max(ngk, 1);                  // clamp target for reloads
   const int gk0c = ngk > 0 ? gk0 : ti.G0;         // empty K-parts re-read the first group
 
-  // ---- activations: this K-part's fragments, a quarter per column wave
+  // ---- activations: this K-part's 1 KB row loads, a quarter per column wave
   const size_t arow = (size_t)p.lda * F::kAElem;
   const rsrc_t ra = make_rsrc(static_cast<const char*>(p.A) + (size_t)ti.row0 * arow + (size_t)gk0c * 128 * F::kAElem,
                               (uint32_t)((size_t)(ti.rows - 1) * arow + (size_t)nload * 128 * F::kAElem));
-  constexpr int kAPerWave = (kFrags + 3) / 4;     // fragment loads per column wave per group
+  constexpr int kAPerWave = (kFrags + 3) / 4;     // activation loads per column wave per group
   uint32_t avoff[kAPerWave];
   int afrag[kAPerWave];
 #pragma unroll
   for (int q = 0; q < kAPerWave; ++q) {
-    const int fr = min(nw + 4 * q, kFrags - 1);   // waves past the last fragment duplicate it
+    const int fr = min(nw + 4 * q, kFrags - 1);   // waves past the last load duplicate it
     afrag[q] = fr;
     avoff[q] = F::a_voff(fr, lane, ti.rows, arow);
   }
@@ -238,7 +238,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
   for (int d = 0; d < kWD; ++d) v.load_lds(st[d], wl(d));
 
   const typename F::Consts k;
-  // Per iteration each wave issues one batch: its A fragments of group i + 2,
+  // Per iteration each wave issues one batch: its A loads of group i + 2,
   // then the weights of group i + kWD. At the wait of iteration i the weights
   // of group i + kWD - 2 and the whole batch of iteration i - 1 were issued
   // after the wave's last A(i) load (the weights of group i went out earlier

@@ -37,7 +37,7 @@ struct PolicySP24 {
   using Acc = f32x4;
   using Elem = float;
   static constexpr int kScaleChunk = 256;   // 16 columns x 8 groups x fp16 (as W4A16)
-  static constexpr int kFrag = 4;           // A fragments (16 rows x 32 k) per chunk
+  static constexpr int kFrag = 4;           // 1 KB activation loads per 16 rows and chunk
   static constexpr int kAElem = 2;
   static constexpr bool kStageScales = true;
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave

@@ -17,7 +17,7 @@ struct PolicyW4A16 : Tile16 {
   using Acc = f32x4;
   using Elem = float;
   static constexpr int kScaleChunk = 256;   // 16 columns x 8 groups x fp16
-  static constexpr int kFrag = 4;           // A fragments (16 rows x 32 k) per group
+  static constexpr int kFrag = 4;           // 1 KB activation loads per 16 rows and group
   static constexpr int kAElem = 2;          // bytes per activation
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave
@@ -113,15 +113,15 @@ struct PolicyW4A16 : Tile16 {
 // 16-k step; result element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
 // column l % 32. The blob keeps its 16-column chunks: the B operand of k-step u
 // is word u/2 of blob lane 16*(2*(u%2) + l/32) + l%16 of chunk (l%32)/16, so
-// each lane loads two 16-byte pieces per group (even and odd k-steps). A
-// fragment u of the LDS ring holds rows 0..31 x k 16u..16u+15 in operand order.
+// each lane loads two 16-byte pieces per group (even and odd k-steps). The A
+// operand of k-step u is read from the slot's whole rows (ARows16).
 // The accumulator's four quarters stand in for the (mb, j) fragments of the
 // shared driver.
 struct PolicyW4A16M32 {
   using Acc = f32x4;
   using Elem = float;
   static constexpr int kScaleChunk = 256;
-  static constexpr int kFrag = 4;           // 2 x 4 = 8 fragments of 32 rows x 16 k per group
+  static constexpr int kFrag = 4;           // 2 x 4 = 8 loads of 4 whole rows per group
   static constexpr int kAElem = 2;
   // Each lane loads its own column's group scale with the weights: staging all
   // of a tall tile's scales in LDS would cost occupancy on long K ranges.

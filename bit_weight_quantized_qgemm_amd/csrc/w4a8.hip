@@ -22,7 +22,7 @@ struct PolicyW4A8 : Tile16 {
   using Acc = i32x4;
   using Elem = int32_t;
   static constexpr int kScaleChunk = 128;   // 16 columns x 8 groups x int8
-  static constexpr int kFrag = 2;           // A fragments (16 rows x 64 k) per group
+  static constexpr int kFrag = 2;           // 1 KB activation loads per 16 rows and group
   static constexpr int kAElem = 1;
   static constexpr bool kStageScales = true;   // the tile's group scales live in LDS
   static constexpr int kWeightDepth = 2;        // weight groups in flight per wave

@@ -63,7 +63,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   constexpr int R32 = R32T / NWR;                   // 32-row blocks per wave
   static_assert(R32 >= 1 && kWideJB >= 1, "wave grid");
   constexpr int kSlotBytes = R32T * 8 * 1024;       // 32-row blocks x 8 k-steps x 1 KB
-  constexpr int kAPerWave = R32T * 8 / kWideWaves;  // fragment loads per wave per group
+  constexpr int kAPerWave = R32T * 8 / kWideWaves;  // 1 KB activation loads per wave per group
   using Stage = WideStage<kWideJB>;
 
   const int lane = threadIdx.x & 63;
@@ -150,7 +150,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   // Prologue: activations and weights of groups 0 .. kDepth-1. Each later
   // iteration issues one batch (activations, then weights and scales, of group
   // i + kDepth), so at the wait of iteration i the weights of group i and the
-  // batches of groups i+1 .. i+kDepth-1 were issued after the last fragment load
+  // batches of groups i+1 .. i+kDepth-1 were issued after the last activation load
   // of group i; the vector memory counter retires loads in order. Slots and
   // stages are static inside the unrolled body, and the iterations past the end
   // only re-issue in-bounds loads and skip the math.
@@ -196,7 +196,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
       if (i < ng) {
         const Stage& cur = st[r];
         const char* slot = ring + r * kSlotBytes;
-        // software pipeline over the 8 k-steps: the fragments and dequantized
+        // software pipeline over the 8 k-steps: the A operands and dequantized
         // weights of step u+1 are fetched while the MFMAs of step u run
         f16x8 a[2][R32], bf[2][kWideJB];
         read_a(slot, 0, a[0]);
