@@ -207,7 +207,7 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
 // general-grid entries are the minimum over its four variants (fp16 / bf16,
 // with or without zero points), the bit-plane rows are b = 1..8.
 namespace {
-const char* const kOccW4A16 = "888555666555";   // 32-row two-block tiles: the M32 policy
+const char* const kOccW4A16 = "888555777555";   // 32-row two-block tiles: the M32 policy
 const char* const kOccW4A8 = "888666666444";
 const char* const kOccW2W4 = "67744455533d";
 const char* const kOccW4G = "55544434423d";
