@@ -208,8 +208,8 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
 // with or without zero points), the bit-plane rows are b = 1..8.
 namespace {
 const char* const kOccW4A16 = "888555777555";   // 32-row two-block tiles: the M32 policy
-const char* const kOccW4A8 = "888666666444";
-const char* const kOccW2W4 = "67744455533d";
+const char* const kOccW4A8 = "888555677444";
+const char* const kOccW2W4 = "677444655444";
 const char* const kOccW4G = "55544434423d";
 const char* const kOccSP24 = "666555555444";
 const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455444",

@@ -129,17 +129,25 @@ struct PolicyW2W4 : Tile16 {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         a[mb][t] = *reinterpret_cast<const f16x8*>(ARows16::at(aslot, mb * 16 + (lane & 15), 4 * t + (lane >> 4)));
+    // the blocks' accumulation chains interleaved step by step (independent
+    // consecutive MFMAs), as in the W4A16 policy
+    f32x4 part[MB][NBW];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) part[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+          part[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bf[j][t], part[mb][j], 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const float sc = valid ? half_of(cur.s[j], 0) : 0.f;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        f32x4 part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          part = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mb][t], bf[j][t], part, 0, 0, 0);
-        acc[mb][j] += sc * part;
-      }
+      for (int mb = 0; mb < MB; ++mb) acc[mb][j] += sc * part[mb][j];
     }
   }
 

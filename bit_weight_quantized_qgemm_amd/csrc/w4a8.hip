@@ -90,24 +90,34 @@ struct PolicyW4A8 : Tile16 {
       rsum[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][0], ones, zero, 0, 0, 0);
       rsum[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][1], ones, rsum[mb], 0, 0, 0);
     }
+    i32x4 b[NBW][2];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const u32x4 w = cur.code[j];
-      const i32x4 b0 = {(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
-                        (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu)};
-      const i32x4 b1 = {(int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
-                        (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
+      b[j][0] = i32x4{(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
+                      (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu)};
+      b[j][1] = i32x4{(int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
+                      (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
+    }
+    // the blocks' two-step chains interleaved (independent consecutive MFMAs)
+    i32x4 part[MB][NBW];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+          part[mb][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][u], b[j][u], u ? part[mb][j] : zero, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
       const int sg = valid ? cur.s[j] : 0;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        i32x4 part = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][0], b0, zero, 0, 0, 0);
-        part = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb][1], b1, part, 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int corr = part[r] - 8 * rsum[mb][r];   // sum_{k in g} A * q, |.| < 2^18
+          const int corr = part[mb][j][r] - 8 * rsum[mb][r];   // sum_{k in g} A * q, |.| < 2^18
           acc[mb][j][r] += __builtin_amdgcn_sbfe(corr, 0, 24) * sg;
         }
-      }
     }
   }
 
