@@ -152,10 +152,11 @@ struct PolicyW4G : Tile16 {
         const float s1 = valid ? scale_of(cur.e[j][1]) : 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
+          // the halves' chains interleaved: consecutive MFMAs are independent
           f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
           p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][0]), bf[0], p0, 0, 0, 0);
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][1]), bf[1], p0, 0, 0, 0);
           p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][2]), bf[2], p1, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][1]), bf[1], p0, 0, 0, 0);
           p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a[mb][3]), bf[3], p1, 0, 0, 0);
           acc[mb][j] += s0 * p0 + s1 * p1;
         }
@@ -169,8 +170,8 @@ struct PolicyW4G : Tile16 {
         r0[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         r1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
         r0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][0]), ones, r0[mb], 0, 0, 0);
-        r0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][1]), ones, r0[mb], 0, 0, 0);
         r1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][2]), ones, r1[mb], 0, 0, 0);
+        r0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][1]), ones, r0[mb], 0, 0, 0);
         r1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][3]), ones, r1[mb], 0, 0, 0);
       }
 #pragma unroll
@@ -196,8 +197,8 @@ struct PolicyW4G : Tile16 {
         for (int mb = 0; mb < MB; ++mb) {
           f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
           p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][0]), bf[0], p0, 0, 0, 0);
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][1]), bf[1], p0, 0, 0, 0);
           p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][2]), bf[2], p1, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][1]), bf[1], p0, 0, 0, 0);
           p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mb][3]), bf[3], p1, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
