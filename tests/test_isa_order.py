@@ -1,10 +1,13 @@
 """The streaming and wide kernels count their outstanding vector-memory
 operations to know when a group's activations (direct-to-LDS loads) have
-landed; the count assumes that after each loop barrier a wave issues its
-activation loads before its weight loads. This test compiles kernels to gfx950
-assembly and checks that order after every barrier (a compiler that issued the
-weight loads first made the count wait too little and the kernel read
-activation slots still being filled). Needs hipcc; no GPU."""
+landed; the count assumes a fixed issue order in each loop iteration
+(streaming kernel: the weights of a later group, the wait, the barrier, the
+activation loads; wide kernel: the wait, the barrier, the activation loads,
+the weights), so after each loop barrier the first vector-memory load a wave
+issues is an activation load. This test compiles kernels to gfx950 assembly and checks that
+after every barrier (a compiler that issued weight loads first made the count
+wait too little and the kernel read activation slots still being filled).
+Needs hipcc; no GPU."""
 
 import os
 import re
