@@ -148,12 +148,14 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   const uint32_t magic = 0x64006400u;
 
   // Prologue: activations and weights of groups 0 .. kDepth-1. Each later
-  // iteration issues one batch (activations, then weights and scales, of group
-  // i + kDepth), so at the wait of iteration i the weights of group i and the
-  // batches of groups i+1 .. i+kDepth-1 were issued after the last activation load
-  // of group i; the vector memory counter retires loads in order. Slots and
-  // stages are static inside the unrolled body, and the iterations past the end
-  // only re-issue in-bounds loads and skip the math.
+  // iteration issues the weights and scales of group i + kDepth, waits, passes
+  // the barrier and issues the activations of group i + kDepth, so at the wait
+  // of iteration i >= kDepth exactly kAfter loads (the batches of groups
+  // i+1 .. i+kDepth-1 and the weights of group i + kDepth) were issued after
+  // the last activation load of group i, and earlier iterations wait for more;
+  // the vector memory counter retires loads in order. Slots and stages are
+  // static inside the unrolled body, and the iterations past the end only
+  // re-issue in-bounds loads and skip the math.
   Stage st[kASlots];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
@@ -185,13 +187,15 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
 #pragma unroll
     for (int r = 0; r < kASlots; ++r) {
       const int i = base + r;
-      // raw_barrier(): publishes only the counted completion above (see skinny.h)
+      // weights first (their stage held group i - 1, already consumed), so
+      // they are in flight during the wait; raw_barrier() publishes only the
+      // counted completion (see skinny.h)
+      issue_b(st[(r + kDepth) % kASlots], min(i + kDepth, nload - 1));
+      // the count relies on this order: no load moves across the wait
+      __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<kAfter>();
       raw_barrier();
       issue_a(min(i + kDepth, nload - 1), (r + kDepth) % kASlots);
-      // the count above relies on this order (activations, then weights)
-      __builtin_amdgcn_sched_barrier(0);
-      issue_b(st[(r + kDepth) % kASlots], min(i + kDepth, nload - 1));
       __builtin_amdgcn_sched_barrier(0);
       if (i < ng) {
         const Stage& cur = st[r];
@@ -218,12 +222,10 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   }
 
   if constexpr (KPW > 1) {
-    // The last iterations left loads in flight: activation DMA into the ring,
-    // then kBPerGroup weight and scale loads whose values are never used; the
-    // counter retires in order, so this retires every DMA write before LDS is
-    // reused. K-parts 1.. then publish their accumulators and K-part 0 adds
-    // them in K-part order.
-    wait_vmcnt<kBPerGroup>();
+    // The last iterations left loads in flight, the last of them activation
+    // DMA into the ring: retire everything before LDS is reused. K-parts 1..
+    // then publish their accumulators and K-part 0 adds them in K-part order.
+    wait_vmcnt<0>();
     __syncthreads();
     constexpr int kAcc4 = R32 * kWideJB * 4;         // f32x4 per lane
     f32x4* red = reinterpret_cast<f32x4*>(lds);
