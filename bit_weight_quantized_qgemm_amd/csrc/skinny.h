@@ -140,7 +140,7 @@ __host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_
   const int extra = F::extra_lds(NB, ng_max);
   L.ring_off = (L.extra_off + extra + 255) / 256 * 256;
   L.slot_bytes = MB * F::kFrag * 1024;
-  const int rings = L.ring_off + KP * 3 * L.slot_bytes;
+  const int rings = L.ring_off + KP * (F::kWeightDepth + 1) * L.slot_bytes;
   const int red = KP * 4 * MB * NBW * 1024;   // one 1 KB fragment of floats per (wave, block)
   L.total = rings > red ? rings : red;
   return L;
@@ -194,7 +194,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
     afrag[q] = fr;
     avoff[q] = F::a_voff(fr, lane, ti.rows, arow);
   }
-  char* ring = lds + L.ring_off + kp * 3 * L.slot_bytes;
+  char* ring = lds + L.ring_off + kp * (F::kWeightDepth + 1) * L.slot_bytes;
   auto issue_a = [&](int rel, int slot) {
 #pragma unroll
     for (int q = 0; q < kAPerWave; ++q)
@@ -209,28 +209,22 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
 
-  // ---- prologue. Weights run kWD = F::kWeightDepth groups ahead (2 or 5) in a
-  // register ring of kWD + 1 stages, activations two groups ahead in a 3-slot
-  // LDS ring. (For the 16-byte-per-lane formats a deeper weight ring was
+  // ---- prologue. Weights and activations both run kWD = F::kWeightDepth
+  // groups ahead, in a register ring of kWD + 1 stages and an LDS ring of
+  // kWD + 1 slots. (For the 16-byte-per-lane formats a deeper weight ring was
   // measured slower on MI355X: the extra registers cost occupancy.)
   // The first loads go out before the scale staging.
-  constexpr int kWD = F::kWeightDepth, kWS = kWD + 1, kAS = 3;
-  static_assert(kWD >= 2 && kWS % kAS == 0, "the unrolled body must return both rings to slot 0");
+  constexpr int kWD = F::kWeightDepth, kWS = kWD + 1, kAS = kWD + 1;
+  static_assert(kWD >= 2, "at least two groups in flight");
   auto wl = [&](int g) { return min(g, nload - 1); };
   Stage st[kWS];
 #pragma unroll
-  for (int d = 0; d < kWD - 2; ++d) {
+  for (int d = 0; d < kWD; ++d) {
+    issue_a(wl(d), d);
+    __builtin_amdgcn_sched_barrier(0);
     v.load_vmem(st[d], wl(d));
     __builtin_amdgcn_sched_barrier(0);
   }
-  issue_a(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  v.load_vmem(st[kWD - 2], wl(kWD - 2));
-  __builtin_amdgcn_sched_barrier(0);
-  issue_a(wl(1), 1);
-  __builtin_amdgcn_sched_barrier(0);
-  v.load_vmem(st[kWD - 1], wl(kWD - 1));
-  __builtin_amdgcn_sched_barrier(0);
   if (F::kStageScales) stage_scales(p.scales, lds, NB, p.G8, ti.b0, ti.c8, ti.n8, F::kScaleChunk);
   F::stage_extra(p, lds + L.extra_off, ti, NB);
   __syncthreads();
@@ -240,14 +234,15 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
   const typename F::Consts k;
   // Per iteration each wave first issues the weights of group i + kWD (their
   // register stage held group i - 1, already consumed), waits, passes the
-  // barrier, then issues its A loads of group i + 2 (their slot held group
+  // barrier, then issues its A loads of group i + kWD (their slot held group
   // i - 1, which the barrier shows every wave has finished reading). At the
-  // wait of iteration i >= 2 exactly the weights of iterations i - 1 and i and
-  // the A loads of iteration i - 1 were issued after the wave's last A(i) load
-  // (earlier iterations wait for more), and the counter retires loads in
-  // order. Issuing the weights before the wait keeps them in flight while the
-  // wave waits at the barrier (measured on MI355X: 5-9 % at M = 8-32).
-  constexpr int kAfter = kAPerWave + 2 * Stage::kVmem;
+  // wait of iteration i >= kWD exactly the batches of iterations i - kWD + 1 ..
+  // i - 1 and the weights of iteration i were issued after the wave's last
+  // A(i) load (earlier iterations have more loads after it, so they wait for
+  // more), and the counter retires loads in order. Issuing the weights before
+  // the wait keeps them in flight while the wave waits at the barrier
+  // (measured on MI355X: 3-6 % at M = 4-32 on the down projection).
+  constexpr int kAfter = Stage::kVmem + (kWD - 1) * (kAPerWave + Stage::kVmem);
   for (int base = 0; base < iters; base += kWS) {
 #pragma unroll
     for (int r = 0; r < kWS; ++r) {
@@ -259,7 +254,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<kAfter>();
         raw_barrier();
-        issue_a(wl(i + 2), (r + 2) % kAS);
+        issue_a(wl(i + kWD), (r + kWD) % kAS);
         __builtin_amdgcn_sched_barrier(0);
         v.load_lds(st[(r + kWD) % kWS], wl(i + kWD));
         F::template compute<MB, NBW>(st[r], ring + (r % kAS) * L.slot_bytes, acc, i < ngk, k, lane);
