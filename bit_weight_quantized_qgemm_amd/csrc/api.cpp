@@ -272,7 +272,9 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits) {
   const double blob = (double)G * (double)(N / 16) * chunk;
   const double big_blob = 32.0 * 1048576.0;
   const double inflight_target = std::min(8.0 * 1048576.0, blob / 2);
-  const int pref_nb = (M > 4 && blob >= big_blob) ? 2 : 1;
+  // the bit-plane kernel is bound by its plane unpacking: one-block tiles (twice
+  // the waves) measured faster on every layer and batch
+  const int pref_nb = (fmt != QGEMM_FMT_BITPLANE && M > 4 && blob >= big_blob) ? 2 : 1;
   struct Score {
     int violations, nb_pen, cost, splits;
     int64_t neg_waves;
