@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8", "qgemm_w4g_packed_bytes",
     "qgemm_w4g_workspace_bytes", "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24",
     "qgemm_bitplane_packed_bytes", "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack",
-    "qgemm_bitplane_a8", "qgemm_bitplane_plan",
+    "qgemm_bitplane_a8", "qgemm_bitplane_plan", "qgemm_w4g_plan",
 )
 
 
@@ -87,12 +87,13 @@ def lib() -> ctypes.CDLL:
         L.qgemm_bitplane_repack.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.qgemm_bitplane_a8.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
         L.qgemm_bitplane_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.qgemm_w4g_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_int64)]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
                      "qgemm_quantize_a8", "qgemm_w4g_packed_bytes", "qgemm_w4g_workspace_bytes",
                      "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24", "qgemm_bitplane_packed_bytes",
                      "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack", "qgemm_bitplane_a8",
-                     "qgemm_bitplane_plan"):
+                     "qgemm_bitplane_plan", "qgemm_w4g_plan"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,12 +138,14 @@ def workspace_bytes(fmt: int, M: int, K: int, N: int) -> int:
 _PLAN_KEYS = ("kernel", "mb", "nb", "wpt", "splits", "gps", "mt", "nt", "workgroups", "waves")
 
 
-def plan(fmt: int, M: int, K: int, N: int, bits: int = 4) -> dict:
+def plan(fmt: int, M: int, K: int, N: int, bits: int = 4, group_size: int = 128, zeros: bool = True) -> dict:
     """Work decomposition of a call of this shape (bits: bit-plane width, used
-    only for FMT_BITPLANE)."""
+    only for FMT_BITPLANE; group_size / zeros: the grid, used only for FMT_W4G)."""
     arr = (ctypes.c_int64 * 10)()
     if fmt == FMT_BITPLANE:
         _check(lib().qgemm_bitplane_plan(M, K, N, bits, arr), "qgemm_bitplane_plan")
+    elif fmt == FMT_W4G:
+        _check(lib().qgemm_w4g_plan(M, K, N, group_size, int(zeros), arr), "qgemm_w4g_plan")
     else:
         _check(lib().qgemm_plan(fmt, M, K, N, arr), "qgemm_plan")
     return dict(zip(_PLAN_KEYS, list(arr)))

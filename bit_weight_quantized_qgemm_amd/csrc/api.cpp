@@ -210,17 +210,18 @@ namespace {
 const char* const kOccW4A16 = "888555777555";   // 32-row two-block tiles: the M32 policy
 const char* const kOccW4A8 = "888555677444";
 const char* const kOccW2W4 = "677444655444";
-const char* const kOccW4G = "55544434423d";
+const char* const kOccW4G = "55544434423d";    // grid entries staged in LDS
+const char* const kOccW4GL = "55544434423d";   // grid entries loaded per lane
 const char* const kOccSP24 = "666555555444";
 const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455444",
                                "67755544433d", "56645534433d", "55544434433d", "55544423d13d"};
 }  // namespace
 
-KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits) {
+KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int kernel) {
   const char* row = fmt == QGEMM_FMT_W4A16 ? kOccW4A16
                     : fmt == QGEMM_FMT_W4A8 ? kOccW4A8
                     : fmt == QGEMM_FMT_W2W4 ? kOccW2W4
-                    : fmt == QGEMM_FMT_W4G ? kOccW4G
+                    : fmt == QGEMM_FMT_W4G ? (kernel == 3 ? kOccW4GL : kOccW4G)
                     : fmt == QGEMM_FMT_W4A16_SP24 ? kOccSP24
                     : kOccBP[std::min(std::max(bits, 1), 8) - 1];
   const char ch = row[((mb - 1) * 2 + (nb - 1)) * 3 + (kp == 1 ? 0 : kp == 2 ? 1 : 2)];
@@ -230,7 +231,7 @@ KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits) {
   return o;
 }
 
-Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits) {
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool zeros) {
   const int force_kernel = g_force_kernel.load();
   const bool wide_ok = fmt == QGEMM_FMT_W4A16 && N % kWideCols == 0;
   if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM))) {
@@ -286,55 +287,72 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits) {
       return neg_waves < o.neg_waves;
     }
   };
+  // General-grid kernel: 1 stages the grid entries in LDS, 3 (only on request)
+  // loads them per lane. Measured on MI355X over 1k x 4k to 57k x 8k layers at
+  // M = 1..128, staging is faster in all but a few cases at M >= 32 with group
+  // length 64 and zero points (8-byte entries per column and chunk), and 10%
+  // faster in total; a plan whose staged entries alone cut a launch of more
+  // workgroups than CUs down to one workgroup per CU counts a violation.
+  const bool w4g = fmt == QGEMM_FMT_W4G;
+  const int var = w4g && force_kernel == 3 ? 3 : 1;
   bool have = false;
   Score best{};
   int best_nb = 1, best_kp = 1, best_s = 1;
-  for (int nb = 1; nb <= 2; ++nb) {
-    if (force_nb && nb != std::min(force_nb, 2)) continue;
-    if (N % (64 * nb) != 0) continue;
-    const int64_t tiles = (int64_t)pl.mt * (N / (64 * nb));
-    for (int kp = 1; kp <= 4; kp *= 2) {
-      if (force_wpt && kp != std::max(1, force_wpt / 4)) continue;
-      if (kp > G) continue;
-      const KernelOccupancy occ = skinny_occupancy(fmt, pl.mb, nb, kp, bits);
-      if (occ.spills && !force_wpt) continue;
-      const int smax = tiles > kMaxCounters ? 1 : std::min(G, 64);
-      for (int s0 = 1; s0 <= smax; ++s0) {
-        if (force_splits && s0 != std::min(force_splits, G)) continue;
-        const int gps = (G + s0 - 1) / s0;
-        const int s = (G + gps - 1) / gps;
-        if (s != s0) continue;                       // the same plan as a smaller s0
-        if (kp > gps) continue;                      // every K-part gets a group
-        Plan c = pl;
-        c.nb = nb;
-        c.wpt = 4 * kp;
-        c.gps = gps;
-        const size_t lds = fmt == QGEMM_FMT_W4A16 ? lds_bytes_w4a16(c, G)
-                           : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G)
-                           : fmt == QGEMM_FMT_W4G  ? lds_bytes_w4g(c, G)
-                           : fmt == QGEMM_FMT_W4A16_SP24 ? lds_bytes_sp24(c, G)
-                           : fmt == QGEMM_FMT_BITPLANE ? lds_bytes_bitplane(c, G) : lds_bytes_w2w4(c, G);
-        if (lds > 160 * 1024) continue;
-        const int64_t wgs = tiles * s;
-        const int64_t waves = wgs * 4 * kp;
-        // resident workgroups per CU: LDS, and registers (a workgroup puts kp
-        // waves on each of the 4 SIMDs)
-        const int64_t cap = std::max<int64_t>(
-            1, std::min<int64_t>((160 * 1024) / std::max<size_t>(lds, 1), occ.waves_per_simd / kp));
-        Score sc;
-        // too few loads in flight costs more than workgroups in a second round
-        sc.violations = (wgs * 4 < 3 * kCUs) + 2 * (waves * nb * 2.0 * chunk < inflight_target) +
-                        (wgs > cap * kCUs);
-        sc.cost = s * kp + s;   // fronts + k-splits
-        sc.splits = s;
-        sc.nb_pen = nb == pref_nb ? 0 : 1;
-        sc.neg_waves = -waves;
-        if (!have || sc < best) {
-          have = true;
-          best = sc;
-          best_nb = nb;
-          best_kp = kp;
-          best_s = s;
+  {
+    for (int nb = 1; nb <= 2; ++nb) {
+      if (force_nb && nb != std::min(force_nb, 2)) continue;
+      if (N % (64 * nb) != 0) continue;
+      const int64_t tiles = (int64_t)pl.mt * (N / (64 * nb));
+      for (int kp = 1; kp <= 4; kp *= 2) {
+        if (force_wpt && kp != std::max(1, force_wpt / 4)) continue;
+        if (kp > G) continue;
+        const KernelOccupancy occ = skinny_occupancy(fmt, pl.mb, nb, kp, bits, var);
+        if (occ.spills && !force_wpt) continue;
+        const int smax = tiles > kMaxCounters ? 1 : std::min(G, 64);
+        for (int s0 = 1; s0 <= smax; ++s0) {
+          if (force_splits && s0 != std::min(force_splits, G)) continue;
+          const int gps = (G + s0 - 1) / s0;
+          const int s = (G + gps - 1) / gps;
+          if (s != s0) continue;                       // the same plan as a smaller s0
+          if (kp > gps) continue;                      // every K-part gets a group
+          Plan c = pl;
+          c.kernel = var;
+          c.nb = nb;
+          c.wpt = 4 * kp;
+          c.gps = gps;
+          const size_t lds = fmt == QGEMM_FMT_W4A16 ? lds_bytes_w4a16(c, G)
+                             : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G)
+                             : fmt == QGEMM_FMT_W4G  ? lds_bytes_w4g(c, G, gs, zeros)
+                             : fmt == QGEMM_FMT_W4A16_SP24 ? lds_bytes_sp24(c, G)
+                             : fmt == QGEMM_FMT_BITPLANE ? lds_bytes_bitplane(c, G) : lds_bytes_w2w4(c, G);
+          if (lds > kSkinnyLdsBudget) continue;
+          const int64_t wgs = tiles * s;
+          const int64_t waves = wgs * 4 * kp;
+          // resident workgroups per CU: LDS, and registers (a workgroup puts kp
+          // waves on each of the 4 SIMDs)
+          const int64_t lds_cap = std::max<int64_t>(1, kLdsPerWorkgroup / std::max<size_t>(lds, 1));
+          const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(lds_cap, occ.waves_per_simd / kp));
+          Score sc;
+          // too few loads in flight costs more than workgroups in a second round
+          bool staged_pen = false;
+          if (w4g && var == 1 && wgs > kCUs && kLdsPerWorkgroup / (lds + 16) < 2) {
+            Plan c3 = c;
+            c3.kernel = 3;
+            staged_pen = kLdsPerWorkgroup / (lds_bytes_w4g(c3, G, gs, zeros) + 16) >= 2;
+          }
+          sc.violations = (wgs * 4 < 3 * kCUs) + 2 * (waves * nb * 2.0 * chunk < inflight_target) +
+                          (wgs > cap * kCUs) + staged_pen;
+          sc.cost = s * kp + s;   // fronts + k-splits
+          sc.splits = s;
+          sc.nb_pen = nb == pref_nb ? 0 : 1;
+          sc.neg_waves = -waves;
+          if (!have || sc < best) {
+            have = true;
+            best = sc;
+            best_nb = nb;
+            best_kp = kp;
+            best_s = s;
+          }
         }
       }
     }
@@ -351,6 +369,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits) {
   splits = (G + gps - 1) / gps;
   int kp = best_kp;
   while (kp > 1 && kp > gps) kp /= 2;       // every K-part gets at least one group
+  pl.kernel = var;
   pl.nb = best_nb;
   pl.nt = (int)(N / (64 * best_nb));
   pl.wpt = 4 * kp;
@@ -444,7 +463,7 @@ int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* 
 }
 
 int qgemm_set_plan_override(int kernel, int nb_per_tile, int waves_per_tile, int k_splits) {
-  if (kernel < 0 || kernel > 2) return QGEMM_ERR_RANGE;
+  if (kernel < 0 || kernel > 3) return QGEMM_ERR_RANGE;
   if (!(nb_per_tile == 0 || nb_per_tile == 1 || nb_per_tile == 2 || nb_per_tile == 4))
     return QGEMM_ERR_RANGE;
   if (!(waves_per_tile == 0 || waves_per_tile == 4 || waves_per_tile == 8 || waves_per_tile == 16))
@@ -569,7 +588,7 @@ int run_gemm(const GemmCall& g) {
   if (g.ldc < g.N || g.ldc % 8 != 0) return QGEMM_ERR_ALIGN;
   if (g.a_scale && !aligned(g.a_scale, 2)) return QGEMM_ERR_ALIGN;
   if (g.acc_out && !aligned(g.acc_out, 4)) return QGEMM_ERR_ALIGN;
-  const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N, g.bits);
+  const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N, g.bits, g.gs, g.zeros);
   if (pl.ws_bytes > 0) {
     if (!g.ws) return QGEMM_ERR_NULL;
     if (g.ws_bytes < pl.ws_bytes) return QGEMM_ERR_WORKSPACE;
@@ -679,7 +698,24 @@ int qgemm_w4g_workspace_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
   int st = check_kn(QGEMM_FMT_W4G, K, N);
   if (st) return st;
   if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
-  *bytes = M == 0 ? 0 : qg::make_plan(QGEMM_FMT_W4G, M, K, N).ws_bytes;
+  // the plan depends on the grid; size for every grid
+  size_t ws = 0;
+  for (int gs : {64, 128})
+    for (bool z : {false, true}) ws = std::max(ws, M == 0 ? 0 : qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, gs, z).ws_bytes);
+  *bytes = ws;
+  return QGEMM_OK;
+}
+
+int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zeros, int64_t* out10) {
+  if (!out10) return QGEMM_ERR_NULL;
+  int st = check_kn(QGEMM_FMT_W4G, K, N);
+  if (st) return st;
+  if (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1)) return QGEMM_ERR_RANGE;
+  if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
+  const qg::Plan pl = qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, group_size, has_zeros != 0);
+  const int64_t v[10] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps,
+                         pl.mt, pl.nt, pl.workgroups, pl.waves};
+  std::memcpy(out10, v, sizeof(v));
   return QGEMM_OK;
 }
 

@@ -48,7 +48,7 @@ struct PolicyBP : Tile16 {
     uint32_t w[NBW][B];
   };
 
-  __host__ __device__ static int extra_lds(int, int) { return 0; }
+  __host__ __device__ static int extra_lds(int, int, int) { return 0; }
   __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
 
   // 4*n bytes at (voff, soff) into w[0..n-1], n = 1..4

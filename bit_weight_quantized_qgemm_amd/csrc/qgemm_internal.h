@@ -13,6 +13,11 @@ constexpr int kWavesPerBlock = 4;    // one wave per SIMD of a CU
 constexpr int kCUs = 256;            // MI355X compute units (8 XCDs x 32)
 constexpr int kTargetWaves = kCUs * 8;
 constexpr int kMaxWavesPerTile = 16;
+// LDS of one workgroup on gfx950, and the dynamic part the streaming kernels
+// may request: their static LDS (the arrival flag, 16 bytes) comes on top,
+// and a launch whose total exceeds the limit aborts the queue.
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+constexpr size_t kSkinnyLdsBudget = kLdsPerWorkgroup - 256;
 constexpr int kWideCols = 256;        // columns per tile of the wide kernel
 constexpr int kWideMinM = 33;         // batches from which the wide kernel is used
 // Split-K arrival counters live in a fixed region at the start of every
@@ -56,14 +61,16 @@ struct Plan {
 };
 
 // bits: planes per weight of the bit-plane format (ignored by the others)
-Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits = 4);
+// gs / zeros: the general-grid format's group length and zero points (its
+// staged grid entries size the LDS); ignored by the other formats
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits = 4, int gs = 128, bool zeros = true);
 struct KernelOccupancy {
   int waves_per_simd;
   bool spills;
 };
 // register-limited occupancy of a streaming-kernel instance (tile 16*mb x 64*nb,
 // kp waves per SIMD per workgroup)
-KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits);
+KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int kernel);
 
 // Arguments of every GEMM kernel (passed by value).
 struct GemmArgs {
@@ -87,7 +94,7 @@ struct GemmArgs {
 size_t lds_bytes_w4a16(const Plan& pl, int G);
 size_t lds_bytes_w4a8(const Plan& pl, int G);
 size_t lds_bytes_w2w4(const Plan& pl, int G);
-size_t lds_bytes_w4g(const Plan& pl, int G);
+size_t lds_bytes_w4g(const Plan& pl, int G, int gs, bool zeros);
 size_t lds_bytes_sp24(const Plan& pl, int G);
 size_t lds_bytes_bitplane(const Plan& pl, int G);
 hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);

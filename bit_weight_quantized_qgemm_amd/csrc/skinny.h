@@ -132,12 +132,12 @@ struct SkinnyLds {
 };
 
 template <class F>
-__host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_max, int ng_max) {
+__host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_max, int ng_max, int gs) {
   SkinnyLds L;
   const int NB = 4 * NBW;
   L.scale_bytes = F::kStageScales ? NB * n8_max * F::kScaleChunk : 0;
   L.extra_off = L.scale_bytes;
-  const int extra = F::extra_lds(NB, ng_max);
+  const int extra = F::extra_lds(NB, ng_max, gs);
   L.ring_off = (L.extra_off + extra + 255) / 256 * 256;
   L.slot_bytes = MB * F::kFrag * 1024;
   const int rings = L.ring_off + KP * (F::kWeightDepth + 1) * L.slot_bytes;
@@ -172,7 +172,7 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
   ti.c8 = ti.G0 >> 3;
   ti.n8 = ((ti.G1 - 1) >> 3) - ti.c8 + 1;
   const int ngw = ti.G1 - ti.G0;
-  const SkinnyLds L = skinny_lds<F>(MB, NBW, KP, (min(p.G, p.gps) + 7) / 8 + 1, min(p.G, p.gps));
+  const SkinnyLds L = skinny_lds<F>(MB, NBW, KP, (min(p.G, p.gps) + 7) / 8 + 1, min(p.G, p.gps), p.gs);
 
   // this K-part's groups [gk0, gk0 + ngk); every K-part runs `iters` iterations
   const int iters = (ngw + KP - 1) / KP;
@@ -359,14 +359,15 @@ QG_SKINNY_KERNEL(4, 1024)
 
 // LDS bytes of a launch (the largest split range bounds the staged chunks)
 template <class F>
-inline size_t skinny_lds_bytes(const Plan& pl, int G) {
+inline size_t skinny_lds_bytes(const Plan& pl, int G, int gs = 0) {
   const int ng_max = std::min(G, pl.gps);
-  return (size_t)skinny_lds<F>(pl.mb, pl.nb, pl.wpt / 4, (ng_max + 7) / 8 + 1, ng_max).total;
+  return (size_t)skinny_lds<F>(pl.mb, pl.nb, pl.wpt / 4, (ng_max + 7) / 8 + 1, ng_max, gs).total;
 }
 
 template <class F, int MB, int NBW>
 hipError_t dispatch_kp(const Plan& pl, const GemmArgs& a, hipStream_t s) {
-  const size_t lds = skinny_lds_bytes<F>(pl, a.G);   // <= 160 KiB, the gfx950 per-workgroup LDS
+  const size_t lds = skinny_lds_bytes<F>(pl, a.G, a.gs);
+  if (lds > kSkinnyLdsBudget) return hipErrorInvalidValue;   // the planner keeps plans within it
   const dim3 grid((unsigned)pl.workgroups);
   switch (pl.wpt / 4) {
     case 1: hipLaunchKernelGGL((skinny_gemm_kp1<F, MB, NBW>), grid, dim3(256), lds, s, a); break;

@@ -61,7 +61,7 @@ struct PolicySP24 {
     uint32_t s[NBW][2];                     // fp16 scales of columns 4h .. 4h+3 (pairs)
   };
 
-  __host__ __device__ static int extra_lds(int, int) { return 0; }
+  __host__ __device__ static int extra_lds(int, int, int) { return 0; }
   __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
 
   template <int NBW>

@@ -48,7 +48,7 @@ struct PolicyW2W4 : Tile16 {
   };
 
   // descriptors of the workgroup's chunks, [NB][groups of the split]
-  __host__ __device__ static int extra_lds(int NB, int ng) { return NB * ng * 8; }
+  __host__ __device__ static int extra_lds(int NB, int ng, int) { return NB * ng * 8; }
   __device__ static void stage_extra(const GemmArgs& p, char* dst_, const TileInfo& ti, int NB) {
     u32x2* dst = reinterpret_cast<u32x2*>(dst_);
     const u32x2* src = static_cast<const u32x2*>(p.aux);

@@ -38,7 +38,7 @@ struct PolicyW4A16 : Tile16 {
     uint32_t s[NBW];                    // fp16 scale bits in the low half
   };
 
-  __host__ __device__ static int extra_lds(int, int) { return 0; }
+  __host__ __device__ static int extra_lds(int, int, int) { return 0; }
   __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
 
   template <int NBW>
@@ -155,7 +155,7 @@ struct PolicyW4A16M32 {
     uint32_t s;
   };
 
-  __host__ __device__ static int extra_lds(int, int) { return 0; }
+  __host__ __device__ static int extra_lds(int, int, int) { return 0; }
   __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
 
   template <int NBW>

@@ -39,7 +39,7 @@ struct PolicyW4A8 : Tile16 {
     int32_t s[NBW];
   };
 
-  __host__ __device__ static int extra_lds(int, int) { return 0; }
+  __host__ __device__ static int extra_lds(int, int, int) { return 0; }
   __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
 
   template <int NBW>

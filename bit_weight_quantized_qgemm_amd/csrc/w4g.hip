@@ -7,9 +7,16 @@
 // without fixing the group length; asymmetric grids store a zero point per
 // group.
 //
-// The codes are the W4A16 blob's 128-k chunks; each lane loads, with its 16 B
-// of codes, the grid entries of its column for the chunk: the two 64-k groups
-// of the chunk when gs = 64, else the one group that contains it. Every chunk
+// The codes are the W4A16 blob's 128-k chunks. Each lane needs, per chunk, the
+// grid entries of its column: the two 64-k groups of the chunk when gs = 64,
+// else the one group that contains it. Two variants fetch them:
+//   staged:   the workgroup copies the entries of its columns and k-split into
+//             LDS once, up front, and lanes read them from there (per-lane
+//             loads of a few bytes next to the 16-byte code loads cost about a
+//             third of the run time at small batches on MI355X);
+//   per lane: each lane loads them with its codes. Needs no LDS, which keeps
+//             more workgroups resident when a k-split spans many groups.
+// Every chunk
 // is treated as two 64-k halves (k-steps 0-1 and 2-3 of the 16x16x32 MFMA),
 // each with its own partial sum and grid entry; for gs >= 128 both halves use
 // the same entry. Applying a group's scale per chunk is exact regrouping of
@@ -33,7 +40,7 @@ namespace fmt {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-template <bool kBF16, bool kZ>
+template <bool kBF16, bool kZ, bool kStaged>
 struct PolicyW4G : Tile16 {
   using Acc = f32x4;
   using Elem = float;
@@ -53,63 +60,121 @@ struct PolicyW4G : Tile16 {
 
   template <int NBW>
   struct Stage {
-    static constexpr int kVmem = 2 * NBW;   // codes + grid entries per column block
+    static constexpr int kVmem = kStaged ? NBW : 2 * NBW;   // codes (+ entries when not staged)
     u32x4 code[NBW];
-    u32x2 e[NBW];                           // entries of the chunk's two 64-k halves
+    u32x2 e[NBW];                                           // entries of the chunk's two 64-k halves
   };
 
-  __host__ __device__ static int extra_lds(int, int) { return 0; }
-  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
+  // Staged variant: the workgroup's grid entries in LDS, one row per chunk of
+  // its split: [chunk - G0][NB * 16 columns][per] entries, per = 2 (the
+  // chunk's two 64-k groups) when gs = 64, else 1 (the group that holds the
+  // chunk, repeated for each of its chunks).
+  __host__ __device__ static int extra_lds(int NB, int ng, int gs) {
+    return kStaged ? ng * NB * 16 * (gs == 64 ? 2 : 1) * (int)kEntry : 0;
+  }
+  __device__ static void stage_extra(const GemmArgs& p, char* dst, const TileInfo& ti, int NB) {
+    if constexpr (kStaged) {
+      const int cpg = p.gs == 64 ? 0 : p.gs / 128;
+      const int per = cpg ? 1 : 2;
+      const int rowb = NB * 16 * per * (int)kEntry;   // bytes of a staged row (a multiple of 16)
+      const int pieces = rowb / 16;
+      const size_t srow = (size_t)p.N * per * kEntry;
+      const char* src = static_cast<const char*>(p.scales) + (size_t)ti.b0 * 16 * per * kEntry;
+      const int ng = ti.G1 - ti.G0;
+      for (int t = threadIdx.x; t < ng * pieces; t += blockDim.x) {
+        const int r = t / pieces, o = t % pieces;
+        const int g = ti.G0 + r;
+        const size_t row = cpg ? (size_t)(g / cpg) : (size_t)g;
+        *reinterpret_cast<u32x4*>(dst + r * rowb + o * 16) =
+            *reinterpret_cast<const u32x4*>(src + row * srow + o * 16);
+      }
+    }
+  }
 
   template <int NBW>
   struct View {
     rsrc_t rc, re;
-    uint32_t cvoff, gstep, evoff, rowb;
-    int gw0, cpg;     // chunks per group (0 for gs = 64)
+    uint32_t cvoff, gstep;
+    uint32_t evoff, rowb;   // per-lane variant: entry offset, bytes per entry row
+    const char* el;         // staged variant: this lane's column of its first block
+    int gw0, G0, cpg, srowb;
+    bool g64;
 
-    __device__ View(const GemmArgs& p, const char*, const SkinnyLds&, const TileInfo&, int bw,
+    __device__ View(const GemmArgs& p, const char* lds, const SkinnyLds& L, const TileInfo& ti, int bw,
                     int gw0_, int nload, int lane)
-        : gw0(gw0_) {
+        : gw0(gw0_), G0(ti.G0) {
       const uint32_t nbt = (uint32_t)(p.N / 16);
       gstep = nbt * 1024u;
       cvoff = lane * 16u;
       rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)gw0 * nbt + bw) * 1024,
                      (uint32_t)(nload - 1) * gstep + NBW * 1024u);
-      cpg = p.gs == 64 ? 0 : p.gs / 128;
-      const uint32_t per = cpg ? 1u : 2u;                 // entries per (row, column)
-      rowb = (uint32_t)p.N * per * kEntry;                // bytes per entry row
-      evoff = (uint32_t)(bw * 16 + (lane & 15)) * per * kEntry;
-      re = make_rsrc(p.scales, (uint32_t)(p.K / (cpg ? p.gs : 64)) * (uint32_t)p.N * kEntry);
+      g64 = p.gs == 64;
+      cpg = g64 ? 0 : p.gs / 128;
+      const int per = g64 ? 2 : 1;
+      if constexpr (kStaged) {
+        srowb = 4 * NBW * 16 * per * (int)kEntry;
+        el = lds + L.extra_off + ((bw - ti.b0) * 16 + (lane & 15)) * per * (int)kEntry;
+      } else {
+        rowb = (uint32_t)p.N * per * kEntry;
+        evoff = (uint32_t)(bw * 16 + (lane & 15)) * per * kEntry;
+        re = make_rsrc(p.scales, (uint32_t)(p.K / (cpg ? p.gs : 64)) * (uint32_t)p.N * kEntry);
+      }
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
-      const int g = gw0 + rel;
 #pragma unroll
       for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * 1024u + rel * gstep);
-      // wave-uniform: one load per block either way
-      if (cpg == 0) {
-        const uint32_t soff = (uint32_t)g * rowb;
+      if constexpr (!kStaged) {
+        const int g = gw0 + rel;
+        // wave-uniform: one load per block either way
+        if (g64) {
+          const uint32_t soff = (uint32_t)g * rowb;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const uint32_t vo = evoff + j * 16u * 2u * kEntry;
-          if (kZ) {
-            st.e[j] = load8(re, vo, soff);
-          } else {
-            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(re, vo, soff, 0);
-            st.e[j] = u32x2{w & 0xFFFFu, w >> 16};
+          for (int j = 0; j < NBW; ++j) {
+            const uint32_t vo = evoff + j * 16u * 2u * kEntry;
+            if (kZ) {
+              st.e[j] = load8(re, vo, soff);
+            } else {
+              const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(re, vo, soff, 0);
+              st.e[j] = u32x2{w & 0xFFFFu, w >> 16};
+            }
           }
-        }
-      } else {
-        const uint32_t soff = (uint32_t)(g / cpg) * rowb;
+        } else {
+          const uint32_t soff = (uint32_t)(g / cpg) * rowb;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const uint32_t vo = evoff + j * 16u * kEntry;
-          const uint32_t w = kZ ? __builtin_amdgcn_raw_buffer_load_b32(re, vo, soff, 0)
-                                : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(re, vo, soff, 0);
-          st.e[j] = u32x2{w, w};
+          for (int j = 0; j < NBW; ++j) {
+            const uint32_t vo = evoff + j * 16u * kEntry;
+            const uint32_t w = kZ ? __builtin_amdgcn_raw_buffer_load_b32(re, vo, soff, 0)
+                                  : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(re, vo, soff, 0);
+            st.e[j] = u32x2{w, w};
+          }
         }
       }
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>&, int) const {}
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
+      if constexpr (kStaged) {
+        const char* row = el + (gw0 + rel - G0) * srowb;
+        // wave-uniform branch
+        if (g64) {
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const char* q = row + j * 16 * 2 * (int)kEntry;
+            if (kZ) {
+              st.e[j] = *reinterpret_cast<const u32x2*>(q);
+            } else {
+              const uint32_t w = *reinterpret_cast<const uint32_t*>(q);
+              st.e[j] = u32x2{w & 0xFFFFu, w >> 16};
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const char* q = row + j * 16 * (int)kEntry;
+            const uint32_t w = kZ ? *reinterpret_cast<const uint32_t*>(q) : (uint32_t)*reinterpret_cast<const uint16_t*>(q);
+            st.e[j] = u32x2{w, w};
+          }
+        }
+      }
+    }
   };
 
   __device__ static float scale_of(uint32_t e) {
@@ -222,16 +287,25 @@ struct PolicyW4G : Tile16 {
 
 using namespace fmt;
 
-size_t lds_bytes_w4g(const Plan& pl, int G) {
-  // the LDS layout does not depend on the grid variant
-  return skinny_lds_bytes<PolicyW4G<false, false>>(pl, G);
+size_t lds_bytes_w4g(const Plan& pl, int G, int gs, bool zeros) {
+  // the layout does not depend on the activation type
+  if (pl.kernel == 3) return skinny_lds_bytes<PolicyW4G<false, true, false>>(pl, G, gs);
+  return zeros ? skinny_lds_bytes<PolicyW4G<false, true, true>>(pl, G, gs)
+               : skinny_lds_bytes<PolicyW4G<false, false, true>>(pl, G, gs);
+}
+
+template <bool kStaged>
+static hipError_t launch_w4g_v(const Plan& pl, const GemmArgs& a, bool bf16, bool zeros, hipStream_t s) {
+  if (bf16) {
+    return zeros ? dispatch_skinny<PolicyW4G<true, true, kStaged>>(pl, a, s)
+                 : dispatch_skinny<PolicyW4G<true, false, kStaged>>(pl, a, s);
+  }
+  return zeros ? dispatch_skinny<PolicyW4G<false, true, kStaged>>(pl, a, s)
+               : dispatch_skinny<PolicyW4G<false, false, kStaged>>(pl, a, s);
 }
 
 hipError_t launch_w4g(const Plan& pl, const GemmArgs& a, bool bf16, bool zeros, hipStream_t s) {
-  if (bf16) {
-    return zeros ? dispatch_skinny<PolicyW4G<true, true>>(pl, a, s) : dispatch_skinny<PolicyW4G<true, false>>(pl, a, s);
-  }
-  return zeros ? dispatch_skinny<PolicyW4G<false, true>>(pl, a, s) : dispatch_skinny<PolicyW4G<false, false>>(pl, a, s);
+  return pl.kernel == 3 ? launch_w4g_v<false>(pl, a, bf16, zeros, s) : launch_w4g_v<true>(pl, a, bf16, zeros, s);
 }
 
 }  // namespace qg

@@ -225,8 +225,8 @@ int qgemm_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* A_
  * qgemm_w4a16; an invalid group_size or act_dtype is QGEMM_ERR_RANGE.
  *
  * qgemm_w4g_packed_bytes: blob size (has_zeros 0 or 1).
- * qgemm_w4g_workspace_bytes: workspace for a call of this shape (same
- *   contract as qgemm_workspace_bytes).
+ * qgemm_w4g_workspace_bytes: workspace for a call of this shape with any grid
+ *   (otherwise the contract of qgemm_workspace_bytes).
  * qgemm_w4g_repack: codes uint32[K/8][N] (as W4A16), scales 16-bit
  *   [K/group_size][N] in the activation type (copied bit for bit), zeros
  *   uint8[K/group_size][N] or NULL (implicit 8; only the low 4 bits of each
@@ -280,11 +280,13 @@ int qgemm_bitplane_a8(const void* A, int64_t lda, const void* a_scale, const voi
 
 /*
  * Work decomposition used for a call of this shape (for tests and tuning).
- * Fills out10[0..9] = {kernel id (1 streaming, 2 wide), 16-row blocks per tile
+ * Fills out10[0..9] = {kernel id (1 streaming, 2 wide, 3 streaming general-grid
+ * kernel with per-lane grid entries; 1 there stages them in LDS), 16-row blocks per tile
  * (per wave for kernel 2), 16-column blocks per wave, waves per workgroup,
  * k-splits across workgroups, groups per k-split, m-tiles, n-tiles,
- * workgroups, waves}. fmt may also be QGEMM_FMT_W4G (the plan does not depend
- * on its grid). Host-only; no HIP call.
+ * workgroups, waves}. fmt may also be QGEMM_FMT_W4G: the plan for group length
+ * 128 with zero points (qgemm_w4g_plan gives it for any grid). Host-only; no
+ * HIP call.
  */
 int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 
@@ -296,9 +298,20 @@ int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* out10);
 
 /*
+ * The work decomposition of a general-grid call (qgemm_w4g) of this shape and
+ * grid, in the layout of qgemm_plan; the grid sets the size of the grid
+ * entries that the kernel can stage in LDS, so it enters the choice. An
+ * invalid group_size or has_zeros: QGEMM_ERR_RANGE; shape rules as for
+ * qgemm_w4g. Host-only; no HIP call.
+ */
+int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zeros,
+                   int64_t* out10);
+
+/*
  * Override the automatic plan for later calls of this process: kernel (1 =
  * streaming kernel for every format, 2 = wide W4A16 kernel for N a multiple of
- * 256; other cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or
+ * 256, 3 = general-grid streaming kernel with per-lane grid entries; other
+ * cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or
  * 2; 4 is taken as 2), waves per workgroup (kernel 1: 4, 8 or 16; kernel 2:
  * 16 runs two K-parts of 8 waves, 4 or 8 one part of 8) and
  * k-splits across workgroups (1..4096); 0 keeps the automatic choice for that

@@ -151,7 +151,7 @@ def test_repack_validation_without_gpu(L):
     assert L.qgemm_repack(1, K, N, codes, sc, None, None, _fake(0x10000000 + 4096), nb, None) == ERR_ALIAS
 
 
-def _check_plan(p, M, K, N, ws=None):
+def _check_plan(p, M, K, N, ws=None, exact_ws=True):
     G = K // 128
     if p["kernel"] == 2:
         assert p["mb"] == 4 and p["nb"] == 4 and p["wpt"] in (8, 16)
@@ -164,7 +164,7 @@ def _check_plan(p, M, K, N, ws=None):
             cover[G0:G1] += 1
         assert np.all(cover == 1)
         return
-    assert p["kernel"] == 1 and p["nb"] in (1, 2) and p["mb"] in (1, 2)
+    assert p["kernel"] in (1, 3) and p["nb"] in (1, 2) and p["mb"] in (1, 2)
     assert p["nt"] * p["nb"] * 64 == N
     assert p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
     assert p["wpt"] in (4, 8, 16) and p["wpt"] // 4 <= p["gps"]
@@ -186,7 +186,7 @@ def _check_plan(p, M, K, N, ws=None):
     if ws is None:
         ws = qg.workspace_bytes(qg.FMT_W4A16, M, K, N)
     if p["splits"] == 1:
-        assert ws == 0
+        assert ws == 0 or not exact_ws
     else:
         assert ws >= p["splits"] * p["mt"] * p["mb"] * 16 * N * 4 + 65536
         assert p["mt"] * p["nt"] <= 16384
@@ -214,7 +214,7 @@ def test_plan_override(L):
         assert L.qgemm_set_plan_override(0, 3, 0, 0) == ERR_RANGE
         assert L.qgemm_set_plan_override(0, 1, 9, 0) == ERR_RANGE
         assert L.qgemm_set_plan_override(0, 1, 0, -1) == ERR_RANGE
-        assert L.qgemm_set_plan_override(3, 0, 0, 0) == ERR_RANGE
+        assert L.qgemm_set_plan_override(4, 0, 0, 0) == ERR_RANGE
         qg.set_plan_override(2, 8, 4)
         p = qg.plan(qg.FMT_W4A16, 16, 4096, 4096)
         assert (p["nb"], p["wpt"], p["splits"], p["gps"]) == (2, 8, 4, 8)
@@ -231,6 +231,10 @@ def test_plan_override(L):
     try:
         qg.set_plan_override(kernel=1)
         assert qg.plan(qg.FMT_W4A16, 128, 8192, 28672)["kernel"] == 1
+        assert qg.plan(qg.FMT_W4G, 128, 8192, 28672)["kernel"] == 1
+        qg.set_plan_override(kernel=3)   # the general-grid kernel with per-lane entries; 1 elsewhere
+        assert qg.plan(qg.FMT_W4A16, 128, 8192, 28672)["kernel"] == 1
+        assert qg.plan(qg.FMT_W4G, 1, 4096, 4096)["kernel"] == 3
         qg.set_plan_override(kernel=2, k_splits=3)
         p = qg.plan(qg.FMT_W4A16, 8, 8192, 28672)
         assert p["kernel"] == 2 and p["splits"] == 3
@@ -284,10 +288,48 @@ def test_w4g_validation_without_gpu(L):
 
 @pytest.mark.parametrize("K,N", [(4096, 11008), (11008, 4096), (1024, 1024), (8192, 28672)])
 @pytest.mark.parametrize("M", [1, 16, 32, 64, 128])
-def test_w4g_plan_covers_every_unit_once(K, N, M):
-    p = qg.plan(qg.FMT_W4G, M, K, N)
-    assert p["kernel"] == 1
-    _check_plan(p, M, K, N, ws=qg.workspace_bytes_w4g(M, K, N))
+@pytest.mark.parametrize("gs,zeros", [(128, True), (64, True), (64, False), (None, False)])
+def test_w4g_plan_covers_every_unit_once(K, N, M, gs, zeros):
+    gs = gs or K   # None: one group per column
+    p = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
+    assert p["kernel"] in (1, 3)   # grid entries staged in LDS / loaded per lane
+    # the workspace query covers every grid, so it may exceed this plan's need
+    _check_plan(p, M, K, N, ws=qg.workspace_bytes_w4g(M, K, N), exact_ws=False)
+    if (gs, zeros) == (128, True):
+        assert p == qg.plan(qg.FMT_W4G, M, K, N)   # the grid qgemm_plan reports
+
+
+def test_w4g_plan_validation(L):
+    out = (ctypes.c_int64 * 10)()
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 128, 1, None) == ERR_NULL
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 96, 1, out) == ERR_RANGE
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 128, 2, out) == ERR_RANGE
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 8192, 0, out) == ERR_RANGE   # does not divide K
+    assert L.qgemm_w4g_plan(0, 4096, 4096, 128, 1, out) == ERR_SHAPE
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 4096, 0, out) == OK
+
+
+def _w4g_lds_bytes(p, K, gs, zeros):
+    """Dynamic LDS of a general-grid streaming launch, written from the kernel's
+    layout: staged grid entries (kernel 1: per column and chunk of the split,
+    two entries for group length 64, else one; 4 bytes with zero points, else
+    2), then K-parts x 3 activation slots of 4 KB per 16 rows; the reduction
+    buffer reuses the start."""
+    ng = min(K // 128, p["gps"])
+    nb_blocks, kp = 4 * p["nb"], p["wpt"] // 4
+    extra = ng * nb_blocks * 16 * (2 if gs == 64 else 1) * (4 if zeros else 2) if p["kernel"] == 1 else 0
+    rings = (extra + 255) // 256 * 256 + kp * 3 * p["mb"] * 4 * 1024
+    return max(rings, kp * 4 * p["mb"] * p["nb"] * 1024)
+
+
+@pytest.mark.parametrize("K,N", [(28672, 8192), (8192, 28672), (11008, 4096), (57344, 8192)])
+def test_w4g_plans_leave_room_for_static_lds(K, N):
+    # A launch's LDS is this dynamic part plus the kernel's 16-byte arrival flag;
+    # a dynamic part of the full 160 KB made the queue abort (28672 x 8192, M = 64).
+    for gs, zeros in [(64, True), (64, False), (128, True), (128, False)]:
+        for M in range(1, 129, 7):
+            p = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
+            assert _w4g_lds_bytes(p, K, gs, zeros) <= 160 * 1024 - 256, (M, gs, zeros, p)
 
 
 # --------------------------------------------------------------------------- 2:4 sparse

@@ -156,6 +156,21 @@ def test_w4g_forced_splits(act, force):
 
 
 @pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("kernel", [1, 3])   # grid entries staged in LDS / loaded per lane
+@pytest.mark.parametrize("gs,zeros,M,force", [(64, True, 1, (1, 16, 1)), (64, False, 40, (2, 8, 3)),
+                                             (128, True, 17, (2, 4, 2)), (512, False, 7, (1, 8, 5)),
+                                             (2048, True, 64, (0, 0, 0))])
+def test_w4g_entry_variants(act, kernel, gs, zeros, M, force):
+    K, N = 2048, 512
+    _say("w4g variant", act, kernel, gs, zeros, M, force)
+    p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=M * 3 + gs + kernel)
+    qg.set_plan_override(*force, kernel=kernel)
+    assert qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)["kernel"] == kernel
+    C = _run(p)
+    _ok(C, ref.gemm_w4g(p["A"], p["codes"], p["scales"], p["zeros"], gs, act), K, act, (kernel, gs, zeros, M))
+
+
+@pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("gs,zeros", [(128, True), (64, False), (11008, True)])
 def test_w4g_7b_layer(act, gs, zeros):
     K, N, M = 11008, 4096, 16
@@ -163,6 +178,23 @@ def test_w4g_7b_layer(act, gs, zeros):
     p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=21)
     C = _run(p)
     _ok(C, ref.gemm_w4g(p["A"], p["codes"], p["scales"], p["zeros"], gs, act), K, act, (gs, zeros))
+
+
+@pytest.mark.parametrize("kernel", [0, 1, 3])
+def test_w4g_70b_up_projection_sampled(kernel):
+    # 8192 x 28672 at M = 64 in the automatic plan and in both entry variants;
+    # the oracle computes 512 sampled columns (a whole staged 128-column tile
+    # among them)
+    K, N, M, gs, act = 8192, 28672, 64, 64, "fp16"
+    _say("w4g 70b sampled", kernel)
+    p = gen.w4g_problem(M, K, N, gs, True, act, seed=77)
+    qg.set_plan_override(kernel=kernel)
+    C = _run(p)
+    rng = np.random.default_rng(7)
+    cols = np.sort(np.concatenate([np.arange(5 * 128, 6 * 128), rng.choice(N, 384, replace=False)]))
+    cols = np.unique(cols)
+    ref_cols = ref.gemm_w4g(p["A"], p["codes"][:, cols], p["scales"][:, cols], p["zeros"][:, cols], gs, act)
+    _ok(C[:, cols], ref_cols, K, act, ("70b", kernel))
 
 
 def test_w4g_matches_w4a16_on_its_grid():

@@ -67,9 +67,10 @@ def test_occupancy_table_matches_compiler():
                 kp, pol, mb, nb = int(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4))
                 kernels.setdefault(pol, {})[(mb, nb, kp)] = rep[mangled]
     policies = {"W4A16": ["PolicyW4A16"], "W4A8": ["PolicyW4A8"], "W2W4": ["PolicyW2W4"], "SP24": ["PolicySP24"],
-                "W4G": [p for p in kernels if p.startswith("PolicyW4G<")]}
+                "W4G": [p for p in kernels if p.startswith("PolicyW4G<") and p.endswith("true>")],
+                "W4GL": [p for p in kernels if p.startswith("PolicyW4G<") and p.endswith("false>")]}
     policies.update({f"BP{b}": [f"PolicyBP<{b}>"] for b in range(1, 9)})
-    assert len(policies["W4G"]) == 4
+    assert len(policies["W4G"]) == 4 and len(policies["W4GL"]) == 4
     table = _table()
     assert set(table) == set(policies)
     for row, pols in policies.items():
@@ -90,14 +91,17 @@ def test_automatic_plans_avoid_spilling_kernels(row):
     fmt = {"W4A16": qg.FMT_W4A16, "W4A8": qg.FMT_W4A8, "W2W4": qg.FMT_W2W4, "W4G": qg.FMT_W4G,
            "SP24": qg.FMT_W4A16_SP24}.get(row, qg.FMT_BITPLANE)
     bits = int(row[2:]) if row.startswith("BP") else 4
-    occ = _table()[row]
     for K, N in [(1024, 1024), (4096, 11008), (11008, 4096), (8192, 28672), (28672, 8192)]:
         if fmt == qg.FMT_W4A8 and K > 16384:
             continue
         for M in (1, 8, 16, 17, 32, 64, 100, 128):
             p = qg.plan(fmt, M, K, N, bits=bits)
-            if p["kernel"] != 1:
+            if p["kernel"] == 2:
                 continue
+            if row == "W4G" and p["kernel"] == 3:
+                occ = _table()["W4GL"]   # the per-lane entry variant
+            else:
+                occ = _table()[row]
             kp = p["wpt"] // 4
             ch = occ[SHAPES.index((p["mb"], p["nb"])) * 3 + (0 if kp == 1 else 1 if kp == 2 else 2)]
             assert ch.isdigit(), (row, K, N, M, p)
