@@ -175,11 +175,13 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   // 128 x 8192 x 28672 in 78 us as 2 x 64 rows vs 93 us as one 128-row tile)
   pl.mb = 4;
   pl.nb = 4;
-  // 8 waves (two per SIMD), or 16 as two K-parts of 8: at M > 96 (two full row
-  // tiles) the extra waves hide more of the weight stream (measured on MI355X,
-  // 70B layer at M = 128: 77 vs 86 us; at M = 64-80 they were slower)
+  // 8 waves (two per SIMD), or 16 as two K-parts of 8: on layers of at least
+  // 2^27 weights at M > 64 (two row tiles) the extra waves hide more of the
+  // weight stream (measured on MI355X, 70B layers: 48.3 vs 52.1 us at M = 96,
+  // 48.8 vs 52.2 us at M = 128; at M = 48-64, and on 7B-class layers at every
+  // M, 8 waves were faster: 21.7 vs 23.3 us at 128 x 4096 x 11008)
   const int fw = g_force_wpt.load();
-  pl.wpt = fw == 16 ? 16 : fw != 0 ? 8 : (M > 96 ? 16 : 8);
+  pl.wpt = fw == 16 ? 16 : fw != 0 ? 8 : (M > 64 && K * N >= (int64_t(1) << 27) ? 16 : 8);
   pl.mt = (int)((M + 16 * pl.mb - 1) / (16 * pl.mb));
   pl.nt = (int)(N / kWideCols);
   const int64_t tiles = (int64_t)pl.mt * pl.nt;
