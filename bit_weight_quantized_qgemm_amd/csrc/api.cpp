@@ -252,12 +252,13 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   // through the blob. Measured on MI355X, the fewer such fronts the better,
   // provided that (a) at least ~3/4 of the CUs get a workgroup, (b) enough
   // weight loads are in flight (each wave keeps two groups of nb chunks in
-  // flight; about 8 MB in total covers HBM latency at full bandwidth, half the
+  // flight; about 7-8 MB in total covers HBM latency at full bandwidth, half the
   // blob on smaller layers), and (c) every workgroup is resident at once, by LDS and by the
   // register-limited occupancy of its kernel. Among plans meeting these, the
-  // search prefers nb = 2 when M > 4 and the blob is at least 32 MB (half the
-  // activation traffic per weight; on smaller blobs one-block tiles give twice
-  // the workgroups at fewer k-splits, which measured faster) and nb = 1
+  // search prefers nb = 2 when M > 4 (W4A16 on blobs of 64 MB: any M) and the
+  // blob is at least 32 MB (half the activation traffic per weight; on smaller
+  // blobs one-block tiles give twice the workgroups at fewer k-splits, which
+  // measured faster) and nb = 1
   // otherwise, then the lowest fronts + k-splits (a k-split also costs
   // partial-sum traffic and a second reduction), then fewer k-splits. Over
   // 1k x 1k to 8k x 28k layers of every format at M = 1..128 this lands
@@ -274,10 +275,16 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
                        : fmt == QGEMM_FMT_BITPLANE ? 256.0 * bits : 1024.0;   // streamed bytes per 16 x 128 chunk
   const double blob = (double)G * (double)(N / 16) * chunk;
   const double big_blob = 32.0 * 1048576.0;
-  const double inflight_target = std::min(8.0 * 1048576.0, blob / 2);
+  // W4A16: 7 MB (the 70B up projection's 8-wave two-block tiles keep 7.3 MB in
+  // flight; measured on MI355X they beat 16-wave tiles by 5-8 % at M <= 32, and
+  // 8192 x 10240 by 17-24 %); the other formats keep the 8 MB of their sweep
+  const double inflight_target = std::min((fmt == QGEMM_FMT_W4A16 ? 7.0 : 8.0) * 1048576.0, blob / 2);
   // the bit-plane kernel is bound by its plane unpacking: one-block tiles (twice
   // the waves) measured faster on every layer and batch
-  const int pref_nb = (fmt != QGEMM_FMT_BITPLANE && M > 4 && blob >= big_blob) ? 2 : 1;
+  // (W4A16 also at M <= 4 once the blob reaches 64 MB: 21.7 vs 22.5 us on the 70B
+  // up projection at M = 1-4)
+  const bool w4a16_big = fmt == QGEMM_FMT_W4A16 && blob >= 64.0 * 1048576.0;
+  const int pref_nb = (fmt != QGEMM_FMT_BITPLANE && (M > 4 || w4a16_big) && blob >= big_blob) ? 2 : 1;
   struct Score {
     int violations, nb_pen, cost, splits;
     int64_t neg_waves;
