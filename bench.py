@@ -122,11 +122,26 @@ def parse():
     return ap.parse_args()
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(target_s: float) -> dict:
     """The NumPy oracle as it stands, on a bounded sample of the step's work:
     the full M sweep on both shapes restricted to the first n_cols output
-    columns of each shape (n_cols grown until the sample takes about target_s
-    seconds; at the full width of a shape the sweep is repeated)."""
+    columns of each shape (n_cols chosen from a short calibration pass so that
+    one pass takes about target_s / 6 seconds). Inputs are generated before
+    any timing. The oracle call is timed three times (median reported as
+    ``value``); its two steps, the explicit dequantization and the fp64 matmul,
+    are timed separately the same way."""
     from oracle import ref
     from synth import gen
 
@@ -136,39 +151,65 @@ def cpu_baseline(target_s: float) -> dict:
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
 
-    def sweep(n_cols):
-        flops = 0
+    def inputs(n_cols):
+        out = []
         for (K, N) in SHAPES:
             n = min(n_cols, N)
             p = gen.w4a16_problem(128, K, n, seed=0)
-            for M in MS:
-                ref.gemm_w4a16(p["A"][:M], p["codes"], p["scales"])
-                flops += alg_flops(M, K, n)
-        return flops
+            out.append((K, n, p["A"], p["codes"], p["scales"]))
+        return out
 
-    n_cols = 512
-    while True:
+    def flops_of(data):
+        return sum(alg_flops(M, K, n) for (K, n, *_r) in data for M in MS)
+
+    def oracle_pass(data):
         t0 = time.perf_counter()
-        flops = sweep(n_cols)
-        dt = time.perf_counter() - t0
-        if dt >= target_s / 2 or n_cols >= max(N for _, N in SHAPES):
-            break
-        n_cols = min(n_cols * 2, max(N for _, N in SHAPES))
-    reps = 1
-    while dt < target_s * 0.75 and reps < 8:    # full width reached: repeat the sweep
+        for (K, n, A, codes, scales) in data:
+            for M in MS:
+                ref.gemm_w4a16(A[:M], codes, scales)
+        return time.perf_counter() - t0
+
+    def dequant_pass(data):
+        # the oracle's dequantization step alone, once per launch of the sweep
         t0 = time.perf_counter()
-        flops_r = sweep(n_cols)
-        dt += time.perf_counter() - t0
-        flops += flops_r
-        reps += 1
+        for (K, n, A, codes, scales) in data:
+            for M in MS:
+                ref.dequant_w4a16(codes, scales)
+        return time.perf_counter() - t0
+
+    def matmul_pass(data, W):
+        t0 = time.perf_counter()
+        for (K, n, A, codes, scales), Wi in zip(data, W):
+            for M in MS:
+                A[:M].astype(np.float64) @ Wi
+        return time.perf_counter() - t0
+
+    cal = inputs(256)
+    dt_cal = oracle_pass(cal)
+    n_cols = int(256 * (target_s / 6.0) / max(dt_cal, 1e-3))
+    n_cols = max(64, min(max(N for _, N in SHAPES), n_cols // 64 * 64))
+    data = inputs(n_cols)
+    flops = flops_of(data)
+    t_total = sorted(oracle_pass(data) for _ in range(3))
+    t_deq = sorted(dequant_pass(data) for _ in range(3))
+    W = [ref.dequant_w4a16(codes, scales) for (_K, _n, _A, codes, scales) in data]
+    t_mm = sorted(matmul_pass(data, W) for _ in range(3))
+    del W
+    med = t_total[1]
     return {
-        "value": flops / dt / 1e12,
+        "value": flops / med / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 dequantize+matmul of the M sweep {MS} on both shapes, first {n_cols} output "
-                  f"columns of each ({reps} pass(es), {flops / 1e9:.2f} GFLOP, {dt:.2f} s; includes input "
-                  f"generation)",
+        "cpu_model": _cpu_model(),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "seconds_median_of_3": round(med, 3),
+        "dequant_seconds_median_of_3": round(t_deq[1], 3),
+        "matmul_seconds_median_of_3": round(t_mm[1], 3),
+        "sample": f"fp64 dequantize+matmul (oracle.ref.gemm_w4a16) of the M sweep {MS} on both shapes, "
+                  f"first {n_cols} output columns of each ({flops / 1e9:.2f} GFLOP per pass); median of 3 "
+                  f"timed passes, inputs generated before timing; dequant and matmul steps timed apart "
+                  f"(median of 3 each)",
     }
 
 

@@ -18,7 +18,7 @@ __all__ = [
     "repack_w2w4", "w4a16", "w4a8", "w2w4_mixed", "Workspace", "EXPORTED_SYMBOLS", "quantize_a8",
     "w4a8_fp16", "FMT_W4G", "DT_F16", "DT_BF16", "packed_bytes_w4g", "workspace_bytes_w4g",
     "repack_w4g", "w4g", "FMT_W4A16_SP24", "repack_sp24", "w4a16_sp24", "FMT_BITPLANE",
-    "packed_bytes_bitplane", "workspace_bytes_bitplane", "repack_bitplane", "bitplane_a8",
+    "packed_bytes_bitplane", "workspace_bytes_bitplane", "repack_bitplane", "bitplane_a8", "plan_info",
 ]
 
 FMT_W4A16 = 1
@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8", "qgemm_w4g_packed_bytes",
     "qgemm_w4g_workspace_bytes", "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24",
     "qgemm_bitplane_packed_bytes", "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack",
-    "qgemm_bitplane_a8", "qgemm_bitplane_plan", "qgemm_w4g_plan",
+    "qgemm_bitplane_a8", "qgemm_bitplane_plan", "qgemm_w4g_plan", "qgemm_plan_info",
 )
 
 
@@ -88,12 +88,13 @@ def lib() -> ctypes.CDLL:
         L.qgemm_bitplane_a8.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
         L.qgemm_bitplane_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int64)]
         L.qgemm_w4g_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.qgemm_plan_info.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
                      "qgemm_quantize_a8", "qgemm_w4g_packed_bytes", "qgemm_w4g_workspace_bytes",
                      "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24", "qgemm_bitplane_packed_bytes",
                      "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack", "qgemm_bitplane_a8",
-                     "qgemm_bitplane_plan", "qgemm_w4g_plan"):
+                     "qgemm_bitplane_plan", "qgemm_w4g_plan", "qgemm_plan_info"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -151,6 +152,15 @@ def plan(fmt: int, M: int, K: int, N: int, bits: int = 4, group_size: int = 128,
     return dict(zip(_PLAN_KEYS, list(arr)))
 
 
+def plan_info(fmt: int, M: int, K: int, N: int, bits: int = 4, group_size: int = 128,
+              zeros: bool = True) -> dict:
+    """The plan of ``plan()`` plus the call's workspace bytes and the dynamic LDS
+    bytes per workgroup its launch requests."""
+    arr = (ctypes.c_int64 * 12)()
+    _check(lib().qgemm_plan_info(fmt, M, K, N, bits, group_size, int(zeros), arr), "qgemm_plan_info")
+    return dict(zip(_PLAN_KEYS + ("ws_bytes", "lds_bytes"), list(arr)))
+
+
 def set_plan_override(nb_per_tile: int = 0, waves_per_tile: int = 0, k_splits: int = 0,
                       kernel: int = 0):
     """Force parts of the work decomposition (0 = automatic); see include/qgemm.h."""
@@ -182,10 +192,14 @@ def _require_cuda(*tensors):
 
 
 class Workspace:
-    """Zero-initialised split-K workspace, grown on demand, one per device.
+    """Zero-initialised split-K workspace, grown on demand, one buffer per
+    (device, stream).
 
     The kernels leave the counter region zero after each completed call, so the
-    buffer is cleared only when it is (re)allocated.
+    buffer is cleared only when it is (re)allocated. Calls that share one
+    workspace buffer must run in order, so each stream gets its own buffer
+    (allocated while that stream is current: the caching allocator then reuses
+    a grown-out buffer's memory only in that stream's order).
     """
 
     def __init__(self):
@@ -193,7 +207,8 @@ class Workspace:
 
     def get(self, nbytes: int, device):
         torch = _torch()
-        key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+        idx = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+        key = (idx, torch.cuda.current_stream(idx).cuda_stream)
         buf = self._bufs.get(key)
         if nbytes == 0:
             return None, 0

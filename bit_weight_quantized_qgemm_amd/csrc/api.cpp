@@ -85,6 +85,11 @@ int check_device() {
   return st;
 }
 
+int no_plan() {
+  g_last_error = "no launch shape of this call fits the 160 KB of LDS of a workgroup";
+  return QGEMM_ERR_SHAPE;
+}
+
 int64_t count_bits(const uint32_t* bitmap, int64_t G, int64_t N, bool* stray) {
   const int64_t W = (N + 31) / 32;
   int64_t n = 0;
@@ -186,16 +191,16 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   pl.nt = (int)(N / kWideCols);
   const int64_t tiles = (int64_t)pl.mt * pl.nt;
   const int force_splits = g_force_splits.load();
-  const int best = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, G / 2), kCUs / tiles));
-  int splits = force_splits ? std::min(force_splits, G) : best;
-  if (tiles > kMaxCounters) splits = 1;
+  const int best = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, G / 2), device_cu_count() / tiles));
+  const int splits = force_splits ? std::min(force_splits, G) : best;
   pl.gps = (G + splits - 1) / splits;
   pl.splits = (G + pl.gps - 1) / pl.gps;
   pl.workgroups = tiles * pl.splits;
   pl.waves = pl.workgroups * pl.wpt;
+  pl.lds_bytes = wide_lds_bytes(pl);
   if (pl.splits > 1) {
     // partial tiles are kept whole (rows padded to the tile) in fragment order
-    pl.counter_bytes = kCounterBytes;
+    pl.counter_bytes = counter_region_bytes(tiles);
     pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * pl.mt * 16 * pl.mb * N * 4);
   }
   return pl;
@@ -233,8 +238,44 @@ KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int 
   return o;
 }
 
+namespace {
+// dynamic LDS of a streaming-kernel launch of plan c
+size_t plan_lds(int fmt, const Plan& c, int G, int bits, int gs, bool zeros) {
+  (void)bits;
+  return fmt == QGEMM_FMT_W4A16         ? lds_bytes_w4a16(c, G)
+         : fmt == QGEMM_FMT_W4A8        ? lds_bytes_w4a8(c, G)
+         : fmt == QGEMM_FMT_W4G         ? lds_bytes_w4g(c, G, gs, zeros)
+         : fmt == QGEMM_FMT_W4A16_SP24  ? lds_bytes_sp24(c, G)
+         : fmt == QGEMM_FMT_BITPLANE    ? lds_bytes_bitplane(c, G)
+                                        : lds_bytes_w2w4(c, G);
+}
+}  // namespace
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  static bool no_device = false;
+  std::lock_guard<std::mutex> lk(mu);
+  if (no_device) return kDefaultCUs;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    no_device = true;
+    return kDefaultCUs;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kDefaultCUs;
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = kDefaultCUs;
+  cache[dev] = cus;
+  return cus;
+}
+
 Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool zeros) {
   const int force_kernel = g_force_kernel.load();
+  const int cus = device_cu_count();
   const bool wide_ok = fmt == QGEMM_FMT_W4A16 && N % kWideCols == 0;
   if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM))) {
     // The wide tile (256 columns, all rows of the batch) needs many k-splits on
@@ -317,7 +358,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
         if (kp > G) continue;
         const KernelOccupancy occ = skinny_occupancy(fmt, pl.mb, nb, kp, bits, var);
         if (occ.spills && !force_wpt) continue;
-        const int smax = tiles > kMaxCounters ? 1 : std::min(G, 64);
+        const int smax = std::min(G, 64);
         for (int s0 = 1; s0 <= smax; ++s0) {
           if (force_splits && s0 != std::min(force_splits, G)) continue;
           const int gps = (G + s0 - 1) / s0;
@@ -329,11 +370,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
           c.nb = nb;
           c.wpt = 4 * kp;
           c.gps = gps;
-          const size_t lds = fmt == QGEMM_FMT_W4A16 ? lds_bytes_w4a16(c, G)
-                             : fmt == QGEMM_FMT_W4A8 ? lds_bytes_w4a8(c, G)
-                             : fmt == QGEMM_FMT_W4G  ? lds_bytes_w4g(c, G, gs, zeros)
-                             : fmt == QGEMM_FMT_W4A16_SP24 ? lds_bytes_sp24(c, G)
-                             : fmt == QGEMM_FMT_BITPLANE ? lds_bytes_bitplane(c, G) : lds_bytes_w2w4(c, G);
+          const size_t lds = plan_lds(fmt, c, G, bits, gs, zeros);
           if (lds > kSkinnyLdsBudget) continue;
           const int64_t wgs = tiles * s;
           const int64_t waves = wgs * 4 * kp;
@@ -344,13 +381,13 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
           Score sc;
           // too few loads in flight costs more than workgroups in a second round
           bool staged_pen = false;
-          if (w4g && var == 1 && wgs > kCUs && kLdsPerWorkgroup / (lds + 16) < 2) {
+          if (w4g && var == 1 && wgs > cus && kLdsPerWorkgroup / (lds + 16) < 2) {
             Plan c3 = c;
             c3.kernel = 3;
             staged_pen = kLdsPerWorkgroup / (lds_bytes_w4g(c3, G, gs, zeros) + 16) >= 2;
           }
-          sc.violations = (wgs * 4 < 3 * kCUs) + 2 * (waves * nb * 2.0 * chunk < inflight_target) +
-                          (wgs > cap * kCUs) + staged_pen;
+          sc.violations = (wgs * 4 < 3 * cus) + 2 * (waves * nb * 2.0 * chunk < inflight_target) +
+                          (wgs > cap * cus) + staged_pen;
           sc.cost = s * kp + s;   // fronts + k-splits
           sc.splits = s;
           sc.nb_pen = nb == pref_nb ? 0 : 1;
@@ -373,7 +410,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
     if (best_kp == 3) best_kp = 2;
   }
   const int64_t tiles = (int64_t)pl.mt * (N / (64 * best_nb));
-  int splits = tiles > kMaxCounters ? 1 : best_s;
+  int splits = best_s;
   const int gps = (G + splits - 1) / splits;
   splits = (G + gps - 1) / gps;
   int kp = best_kp;
@@ -386,9 +423,13 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   pl.gps = gps;
   pl.workgroups = tiles * splits;
   pl.waves = pl.workgroups * pl.wpt;
+  pl.lds_bytes = plan_lds(fmt, pl, G, bits, gs, zeros);
+  // no shape of the search fits (or a forced shape does not): refuse the call
+  // rather than launch more LDS than a workgroup can hold
+  if ((!have && !(force_nb || force_wpt || force_splits)) || pl.lds_bytes > kSkinnyLdsBudget) pl.kernel = 0;
   if (pl.splits > 1) {
     // partial tiles are kept whole (rows padded to the tile) in fragment order
-    pl.counter_bytes = kCounterBytes;
+    pl.counter_bytes = counter_region_bytes(tiles);
     pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * pl.mt * 16 * pl.mb * N * 4);
   }
   return pl;
@@ -441,7 +482,13 @@ int qgemm_workspace_bytes(int fmt, int64_t M, int64_t K, int64_t N, size_t* byte
   int st = check_kn(fmt, K, N);
   if (st) return st;
   if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
-  *bytes = M == 0 ? 0 : qg::make_plan(fmt, M, K, N).ws_bytes;
+  if (M == 0) {
+    *bytes = 0;
+    return QGEMM_OK;
+  }
+  const qg::Plan pl = qg::make_plan(fmt, M, K, N);
+  if (pl.kernel == 0) return no_plan();
+  *bytes = pl.ws_bytes;
   return QGEMM_OK;
 }
 
@@ -452,6 +499,7 @@ int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10) {
   if (st) return st;
   if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
   const qg::Plan pl = qg::make_plan(fmt, M, K, N);
+  if (pl.kernel == 0) return no_plan();
   const int64_t v[10] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps,
                          pl.mt, pl.nt, pl.workgroups, pl.waves};
   std::memcpy(out10, v, sizeof(v));
@@ -465,9 +513,29 @@ int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* 
   if (st) return st;
   if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
   const qg::Plan pl = qg::make_plan(QGEMM_FMT_BITPLANE, M, K, N, bits);
+  if (pl.kernel == 0) return no_plan();
   const int64_t v[10] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps,
                          pl.mt, pl.nt, pl.workgroups, pl.waves};
   std::memcpy(out10, v, sizeof(v));
+  return QGEMM_OK;
+}
+
+int qgemm_plan_info(int fmt, int64_t M, int64_t K, int64_t N, int32_t bits, int32_t group_size,
+                    int32_t has_zeros, int64_t* out12) {
+  if (!valid_fmt(fmt) && fmt != QGEMM_FMT_W4G && fmt != QGEMM_FMT_BITPLANE) return QGEMM_ERR_FORMAT;
+  if (!out12) return QGEMM_ERR_NULL;
+  int st = check_kn(fmt, K, N);
+  if (st) return st;
+  if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
+  if (fmt == QGEMM_FMT_BITPLANE && (bits < 1 || bits > 8)) return QGEMM_ERR_RANGE;
+  if (fmt == QGEMM_FMT_W4G && (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1)))
+    return QGEMM_ERR_RANGE;
+  const qg::Plan pl = qg::make_plan(fmt, M, K, N, fmt == QGEMM_FMT_BITPLANE ? bits : 4,
+                                    fmt == QGEMM_FMT_W4G ? group_size : qg::kGroup, has_zeros != 0);
+  if (pl.kernel == 0) return no_plan();
+  const int64_t v[12] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps, pl.mt, pl.nt,
+                         pl.workgroups, pl.waves, (int64_t)pl.ws_bytes, (int64_t)pl.lds_bytes};
+  std::memcpy(out12, v, sizeof(v));
   return QGEMM_OK;
 }
 
@@ -598,6 +666,7 @@ int run_gemm(const GemmCall& g) {
   if (g.a_scale && !aligned(g.a_scale, 2)) return QGEMM_ERR_ALIGN;
   if (g.acc_out && !aligned(g.acc_out, 4)) return QGEMM_ERR_ALIGN;
   const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N, g.bits, g.gs, g.zeros);
+  if (pl.kernel == 0) return no_plan();
   if (pl.ws_bytes > 0) {
     if (!g.ws) return QGEMM_ERR_NULL;
     if (g.ws_bytes < pl.ws_bytes) return QGEMM_ERR_WORKSPACE;
@@ -651,6 +720,11 @@ int run_gemm(const GemmCall& g) {
   }
   hipStream_t s = static_cast<hipStream_t>(g.stream);
   hipError_t e;
+  if (pl.ws_bytes && pl.counter_bytes > qg::kCounterBytes) {
+    // a counter region beyond the fixed one may hold other plans' partial sums
+    e = qg::launch_zero_fill(g.ws, pl.counter_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "counter clear");
+  }
   if (g.fmt == QGEMM_FMT_W4A16) e = pl.kernel == 2 ? qg::launch_w4a16_wide(pl, a, s) : qg::launch_w4a16(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4A8) e = qg::launch_w4a8(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4G) e = qg::launch_w4g(pl, a, g.bf16, g.zeros, s);
@@ -707,7 +781,8 @@ int qgemm_w4g_workspace_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
   int st = check_kn(QGEMM_FMT_W4G, K, N);
   if (st) return st;
   if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
-  // the plan depends on the grid; size for every grid
+  // the plan depends on the grid; size for every grid (a grid with no plan
+  // that fits is refused by the GEMM call itself)
   size_t ws = 0;
   for (int gs : {64, 128})
     for (bool z : {false, true}) ws = std::max(ws, M == 0 ? 0 : qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, gs, z).ws_bytes);
@@ -722,6 +797,7 @@ int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t 
   if (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1)) return QGEMM_ERR_RANGE;
   if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
   const qg::Plan pl = qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, group_size, has_zeros != 0);
+  if (pl.kernel == 0) return no_plan();
   const int64_t v[10] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps,
                          pl.mt, pl.nt, pl.workgroups, pl.waves};
   std::memcpy(out10, v, sizeof(v));
@@ -781,7 +857,13 @@ int qgemm_bitplane_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t bits
   if (st) return st;
   if (bits < 1 || bits > 8) return QGEMM_ERR_RANGE;
   if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
-  *bytes = M == 0 ? 0 : qg::make_plan(QGEMM_FMT_BITPLANE, M, K, N, bits).ws_bytes;
+  if (M == 0) {
+    *bytes = 0;
+    return QGEMM_OK;
+  }
+  const qg::Plan pl = qg::make_plan(QGEMM_FMT_BITPLANE, M, K, N, bits);
+  if (pl.kernel == 0) return no_plan();
+  *bytes = pl.ws_bytes;
   return QGEMM_OK;
 }
 

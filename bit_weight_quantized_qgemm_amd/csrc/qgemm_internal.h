@@ -10,8 +10,10 @@ namespace qg {
 constexpr int kGroup = 128;          // k per quantization group
 constexpr int kWave = 64;            // lanes per wavefront (CDNA)
 constexpr int kWavesPerBlock = 4;    // one wave per SIMD of a CU
-constexpr int kCUs = 256;            // MI355X compute units (8 XCDs x 32)
-constexpr int kTargetWaves = kCUs * 8;
+constexpr int kDefaultCUs = 256;     // MI355X compute units (8 XCDs x 32)
+// Compute units of the current device, queried once per device and cached;
+// kDefaultCUs when no device is visible (host-only queries).
+int device_cu_count();
 constexpr int kMaxWavesPerTile = 16;
 // LDS of one workgroup on gfx950, and the dynamic part the streaming kernels
 // may request: their static LDS (the arrival flag, 16 bytes) comes on top,
@@ -19,12 +21,18 @@ constexpr int kMaxWavesPerTile = 16;
 constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 constexpr size_t kSkinnyLdsBudget = kLdsPerWorkgroup - 256;
 constexpr int kWideCols = 256;        // columns per tile of the wide kernel
+constexpr int kWideSlots = 4;         // activation LDS slots per K-part of the wide kernel
 constexpr int kWideMinM = 33;         // batches from which the wide kernel is used
 // Split-K arrival counters live in a fixed region at the start of every
 // workspace, so that calls with different plans sharing one workspace never see
-// another plan's partial sums in place of zero counters.
+// another plan's partial sums in place of zero counters. A plan with more tiles
+// than that region holds gets a larger counter region, which its call clears
+// first (the fixed region's calls may have left partial sums beyond it).
 constexpr size_t kCounterBytes = 65536;
 constexpr int64_t kMaxCounters = kCounterBytes / 4;
+inline size_t counter_region_bytes(int64_t tiles) {
+  return tiles > kMaxCounters ? (size_t)((tiles * 4 + 255) / 256 * 256) : kCounterBytes;
+}
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -46,7 +54,10 @@ BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4);
 // kernel 2: 4-wave workgroups own 16*mb x 256 tiles. `splits` > 1 additionally
 // splits K across workgroups.
 struct Plan {
-  int kernel = 1;        // 1 = streaming skinny kernel, 2 = wide (large-M) W4A16 kernel
+  // 1 = streaming skinny kernel, 2 = wide (large-M) W4A16 kernel, 3 = streaming
+  // general-grid kernel with per-lane grid entries; 0 = no launch shape fits
+  // the workgroup's LDS (the call is refused with QGEMM_ERR_SHAPE)
+  int kernel = 1;
   int mb = 1;            // 16-row blocks per tile (per wave for kernel 2)
   int nb = 1;            // 16-column blocks per wave
   int wpt = 1;           // waves per tile (workgroup size / 64)
@@ -58,7 +69,12 @@ struct Plan {
   int64_t waves = 0;
   size_t counter_bytes = 0;
   size_t ws_bytes = 0;   // total workspace (0 when splits == 1)
+  size_t lds_bytes = 0;  // dynamic LDS the launch requests
 };
+
+// dynamic LDS of a wide-kernel launch: per K-part of 8 waves, kWideSlots slots
+// of 16*mb rows x 128 k fp16
+inline size_t wide_lds_bytes(const Plan& pl) { return (size_t)(pl.wpt / 8) * kWideSlots * pl.mb * 4 * 1024; }
 
 // bits: planes per weight of the bit-plane format (ignored by the others)
 // gs / zeros: the general-grid format's group length and zero points (its

@@ -369,7 +369,9 @@ namespace {
 // (above 64 KiB) once per kernel and device
 template <int KPW>
 hipError_t launch_wide_k(void (*kernel)(GemmArgs), int mbw, const Plan& pl, const GemmArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)KPW * kASlots * mbw * 4 * 1024;
+  static_assert(kASlots == kWideSlots, "the planner sizes the LDS ring");
+  const size_t lds = wide_lds_bytes(pl);
+  if (lds != (size_t)KPW * kASlots * mbw * 4 * 1024) return hipErrorInvalidValue;
   static std::mutex mu;
   static std::set<int> done;
   int dev = 0;

@@ -43,7 +43,14 @@
  *     nothing and writes nothing. No C++ exception crosses this boundary.
  *   - Shapes: K > 0 a multiple of 128, N > 0 a multiple of 64, K and N at most
  *     2^20, K*N at most 2^32 (2 GiB of 4-bit codes), 0 <= M <= 65535 (M == 0
- *     returns QGEMM_OK without launching anything).
+ *     returns QGEMM_OK without launching anything). A shape for which no launch
+ *     configuration fits the 160 KB of LDS of a workgroup is refused with
+ *     QGEMM_ERR_SHAPE (the planner finds one for every shape above; the check
+ *     guards forced plans and future formats).
+ *   - Plans are sized for the current device's compute-unit count (queried
+ *     once per device and cached; 256, the MI355X count, when no device is
+ *     visible), so query workspace sizes and plans with the device current
+ *     that will run the call.
  *   - Pointers: 16-byte aligned; lda, ldc multiples of 8 (fp16) or 16 (int8).
  *   - Concurrent calls that share one workspace race; give each stream its own.
  */
@@ -285,15 +292,28 @@ int qgemm_bitplane_a8(const void* A, int64_t lda, const void* a_scale, const voi
  * (per wave for kernel 2), 16-column blocks per wave, waves per workgroup,
  * k-splits across workgroups, groups per k-split, m-tiles, n-tiles,
  * workgroups, waves}. fmt may also be QGEMM_FMT_W4G: the plan for group length
- * 128 with zero points (qgemm_w4g_plan gives it for any grid). Host-only; no
- * HIP call.
+ * 128 with zero points (qgemm_w4g_plan gives it for any grid). Host-only: its
+ * only HIP calls are the cached device-property queries.
  */
 int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 
 /*
+ * The work decomposition of a call of any format (fmt QGEMM_FMT_BITPLANE uses
+ * `bits`, QGEMM_FMT_W4G uses `group_size` and `has_zeros`; the others ignore
+ * them) with the launch's resources: out12[0..9] as qgemm_plan, out12[10] =
+ * workspace bytes the call needs, out12[11] = dynamic LDS bytes per workgroup
+ * the launch requests (at most 160 KB - 256). QGEMM_ERR_SHAPE when no launch
+ * shape fits; argument rules as for the format's GEMM entry point. Host-only:
+ * its only HIP calls are the cached device-property queries.
+ */
+int qgemm_plan_info(int fmt, int64_t M, int64_t K, int64_t N, int32_t bits, int32_t group_size,
+                    int32_t has_zeros, int64_t* out12);
+
+/*
  * The work decomposition of a bit-plane W_b A8 call (qgemm_bitplane_a8) of
  * this shape and bit width, in the layout of qgemm_plan. bits outside 1..8:
- * QGEMM_ERR_RANGE; shape rules as for qgemm_bitplane_a8. Host-only; no HIP call.
+ * QGEMM_ERR_RANGE; shape rules as for qgemm_bitplane_a8. Host-only (cached
+ * device-property queries only).
  */
 int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* out10);
 
@@ -302,7 +322,7 @@ int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* 
  * grid, in the layout of qgemm_plan; the grid sets the size of the grid
  * entries that the kernel can stage in LDS, so it enters the choice. An
  * invalid group_size or has_zeros: QGEMM_ERR_RANGE; shape rules as for
- * qgemm_w4g. Host-only; no HIP call.
+ * qgemm_w4g. Host-only (cached device-property queries only).
  */
 int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zeros,
                    int64_t* out10);

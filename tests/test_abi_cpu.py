@@ -412,3 +412,42 @@ def test_bitplane_plan_covers_every_unit_once(K, N, M, bits):
     assert p["kernel"] == 1
     _check_plan(p, M, K, N, ws=qg.workspace_bytes_bitplane(M, K, N, bits))
 
+
+
+_LDS_BUDGET = 160 * 1024 - 256
+_FORMATS = [(qg.FMT_W4A16, {}), (qg.FMT_W4A8, {}), (qg.FMT_W2W4, {}), (qg.FMT_W4A16_SP24, {}),
+            (qg.FMT_W4G, {"group_size": 64, "zeros": True}), (qg.FMT_W4G, {"group_size": 128, "zeros": False}),
+            (qg.FMT_BITPLANE, {"bits": 8}), (qg.FMT_BITPLANE, {"bits": 1})]
+
+
+@pytest.mark.parametrize("fmt,kw", _FORMATS)
+@pytest.mark.parametrize("K,N", [(262144, 4160), (57344, 8192), (1048576, 64), (128, 1048576), (1024, 1024),
+                                 (28672, 8192)])
+def test_every_automatic_plan_fits_lds_and_covers_the_layer(fmt, kw, K, N):
+    # long K with many tiles (M up to 65535) once forced a single k-split whose
+    # staged scales or grid entries outgrew the LDS; every automatic plan must
+    # now fit, cover every unit once, and size its counters for its tiles
+    if fmt == qg.FMT_W4A8 and K > 16384:
+        pytest.skip("W4A8 accepts K <= 16384")
+    if fmt == qg.FMT_BITPLANE and K > 65536:
+        pytest.skip("bit-plane accepts K <= 65536")
+    for M in (1, 16, 17, 64, 128, 1000, 16384, 65535):
+        p = qg.plan_info(fmt, M, K, N, **kw)
+        assert 0 < p["lds_bytes"] <= _LDS_BUDGET, (M, p)
+        G = K // 128
+        assert p["splits"] * p["gps"] >= G and (p["splits"] - 1) * p["gps"] < G, (M, p)
+        tiles = p["mt"] * p["nt"]
+        assert p["workgroups"] == tiles * p["splits"]
+        if p["splits"] > 1:
+            assert p["ws_bytes"] >= max(65536, 4 * tiles), (M, p)
+
+
+def test_counter_region_grows_past_the_fixed_region():
+    # W4G 16384 x 57344 x 8192 with group 64 and zero points: the case that
+    # once returned a plan needing 253,952 B of staged entries
+    p = qg.plan_info(qg.FMT_W4G, 16384, 57344, 8192, group_size=64, zeros=True)
+    assert p["lds_bytes"] <= _LDS_BUDGET
+    tiles = p["mt"] * p["nt"]
+    assert tiles > 16384 and p["splits"] > 1
+    assert p["ws_bytes"] >= (tiles * 4 + 255) // 256 * 256
+    assert qg.workspace_bytes_w4g(16384, 57344, 8192) >= p["ws_bytes"]

@@ -13,6 +13,8 @@ import bit_weight_quantized_qgemm_amd as qg
 from oracle import compare, ref
 from synth import gen
 
+from sampling import block_cols
+
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
@@ -87,7 +89,7 @@ def test_quantize_then_w4a8_exact_accumulators():
     C = qg.w4a8_fp16(torch.from_numpy(A16).to(DEV), blob, K, N, acc_out=acc)
     torch.cuda.synchronize()
     q_ref, s_ref = ref.quantize_a8(A16)
-    cols = np.random.default_rng(3).choice(N, size=512, replace=False)
+    cols = block_cols(N, seed=3)
     acc_ref, c_ref = ref.gemm_w4a8(q_ref, p["codes"], p["group_scales"], s_ref, p["chan_scales"], cols=cols)
     assert np.array_equal(acc.cpu().numpy()[:, cols].astype(np.int64), acc_ref)
     r = compare.check_fp16(C.cpu().numpy()[:, cols], c_ref, K)

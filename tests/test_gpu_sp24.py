@@ -20,6 +20,8 @@ import bit_weight_quantized_qgemm_amd as qg
 from oracle import compare, layout, ref
 from synth import gen
 
+from sampling import block_cols
+
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
@@ -129,7 +131,7 @@ def test_sp24_70b_layer_sampled(K, N):
     _say("sp24 70b sampled", K, N)
     p = gen.w4a16_sp24_problem(128, K, N, seed=0)
     blob = _upload(p)
-    cols = np.sort(np.random.default_rng(1).choice(N, size=96, replace=False))
+    cols = block_cols(N, seed=1)
     for M in (1, 16, 128):
         A = p["A"][:M]
         C = qg.w4a16_sp24(_t(A), blob, K, N).cpu().numpy()

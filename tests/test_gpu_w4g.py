@@ -21,6 +21,8 @@ import bit_weight_quantized_qgemm_amd as qg
 from oracle import compare, layout, ref
 from synth import gen
 
+from sampling import block_cols
+
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
@@ -183,18 +185,34 @@ def test_w4g_7b_layer(act, gs, zeros):
 @pytest.mark.parametrize("kernel", [0, 1, 3])
 def test_w4g_70b_up_projection_sampled(kernel):
     # 8192 x 28672 at M = 64 in the automatic plan and in both entry variants;
-    # the oracle computes 512 sampled columns (a whole staged 128-column tile
-    # among them)
+    # the oracle computes one column of every 16-column block plus a whole
+    # staged 128-column tile
     K, N, M, gs, act = 8192, 28672, 64, 64, "fp16"
     _say("w4g 70b sampled", kernel)
     p = gen.w4g_problem(M, K, N, gs, True, act, seed=77)
     qg.set_plan_override(kernel=kernel)
     C = _run(p)
-    rng = np.random.default_rng(7)
-    cols = np.sort(np.concatenate([np.arange(5 * 128, 6 * 128), rng.choice(N, 384, replace=False)]))
-    cols = np.unique(cols)
+    cols = np.unique(np.concatenate([np.arange(5 * 128, 6 * 128), block_cols(N, seed=7)]))
     ref_cols = ref.gemm_w4g(p["A"], p["codes"][:, cols], p["scales"][:, cols], p["zeros"][:, cols], gs, act)
     _ok(C[:, cols], ref_cols, K, act, ("70b", kernel))
+
+
+@pytest.mark.parametrize("gs,zeros,act", [(64, True, "fp16"), (128, True, "bf16"), (128, False, "fp16")])
+def test_w4g_70b_down_projection_m64_automatic_plan(gs, zeros, act):
+    # 28672 x 8192 at M = 64 in the automatic plan: the shape whose launch once
+    # asked for all 160 KB of LDS as dynamic memory (leaving none for the
+    # kernel's static arrival flag) and aborted the queue; plans now keep 256
+    # bytes of headroom. Compared on one column of every 16-column block plus
+    # a whole 128-column tile.
+    K, N, M = 28672, 8192, 64
+    pl = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
+    _say("w4g 70b down m64", gs, zeros, act, pl)
+    p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=78)
+    C = _run(p)
+    cols = np.unique(np.concatenate([np.arange(3 * 128, 4 * 128), block_cols(N, seed=8)]))
+    z = None if p["zeros"] is None else p["zeros"][:, cols]
+    ref_cols = ref.gemm_w4g(p["A"], p["codes"][:, cols], p["scales"][:, cols], z, gs, act)
+    _ok(C[:, cols], ref_cols, K, act, ("70b down", gs, zeros))
 
 
 def test_w4g_matches_w4a16_on_its_grid():

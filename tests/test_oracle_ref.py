@@ -269,3 +269,118 @@ def test_bits_per_weight_mixed():
     bm = gen.bitmap_from_mask(mask.reshape(K // 128, N))
     bpw = ref.bits_per_weight_w2w4(bm, K, N)
     assert abs(bpw - (2 + 2 * n4 * 128 / (K * N) + 17 / 128)) < 1e-12
+
+
+# --------------------------------------------------------------------------- K-slab accumulation
+# The oracle adds the product slab by slab (2048 k per slab by default) once K
+# exceeds one slab, as every 7B- and 70B-class comparison does. These pins run
+# that branch with scales that differ in every (group, column), so a slab whose
+# scale slice started at the wrong group, a dropped or repeated slab, or a
+# ragged last slab handled wrongly changes at least one exact value.
+_SLAB_KS = (0, 127, 128, 2047, 2048, 2049, 4095, 4096, 6143, 6144, 8191)
+
+
+def _distinct_scales(G, N):
+    # 1 + j/1024 for j = g*N + n: exactly representable fp16 values, all distinct
+    j = np.arange(G * N).reshape(G, N)
+    assert G * N <= 1024
+    return (1.0 + j / 1024.0).astype(np.float16)
+
+
+def _slab_one_hot_case():
+    K, N = 8192, 16
+    q = np.random.default_rng(31).integers(0, 16, size=(K, N), dtype=np.uint8)
+    s = _distinct_scales(K // 128, N)
+    A = np.zeros((len(_SLAB_KS), K), dtype=np.float16)
+    A[np.arange(len(_SLAB_KS)), list(_SLAB_KS)] = 1
+    expect = np.array([[(int(q[k, n]) - 8) * float(s[k // 128, n]) for n in range(N)] for k in _SLAB_KS])
+    return A, gen.pack_nibbles_u32(q), s, expect
+
+
+def _slab_closed_form_case():
+    # constant code c and integer activations: C[m,n] = (c-8) * sum_g s[g,n] * sum_{k in g} A[m,k],
+    # evaluated with exact rationals
+    K, N, c = 8192, 8, 13
+    A = np.random.default_rng(32).integers(-4, 5, size=(2, K)).astype(np.float16)
+    s = _distinct_scales(K // 128, N)
+    qw = gen.pack_nibbles_u32(np.full((K, N), c, dtype=np.uint8))
+    expect = np.zeros((2, N))
+    for m in range(2):
+        gsum = [sum(int(A[m, k]) for k in range(128 * g, 128 * g + 128)) for g in range(K // 128)]
+        for n in range(N):
+            e = sum(Fraction(gsum[g]) * _frac(s[g, n]) for g in range(K // 128)) * (c - 8)
+            expect[m, n] = float(e)
+    return A, qw, s, expect
+
+
+def _pins_hold(gemm):
+    for case in (_slab_one_hot_case(), _slab_closed_form_case()):
+        A, qw, s, expect = case
+        if not np.array_equal(gemm(A, qw, s), expect):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("slab", [2048, 640, 128, 8192])
+def test_w4a16_k_slabs_one_hot_and_closed_form(slab):
+    # the default slab (2048) and slabs that do not divide K (640) or hold one
+    # group (128) or all of K: every value exact (each product and partial sum
+    # fits in fp64's significand)
+    assert _pins_hold(lambda A, qw, s: ref.gemm_w4a16(A, qw, s, slab=slab))
+
+
+def test_w4a16_k_slab_pins_catch_a_misaligned_scale_slice():
+    # a planted mistake in a copy of the oracle's slab loop: the scales of every
+    # slab taken from group 0 instead of group k0 // 128; the pins above must fail
+    def misaligned(A, qw, s, slab=2048):
+        K = qw.shape[0] * 8
+        C = np.zeros((A.shape[0], qw.shape[1]))
+        for k0 in range(0, K, slab):
+            k1 = min(K, k0 + slab)
+            C += A[:, k0:k1].astype(np.float64) @ ref.dequant_w4a16(qw[k0 // 8:k1 // 8], s[:(k1 - k0) // 128])
+        return C
+
+    def off_by_one(A, qw, s, slab=2048):
+        K = qw.shape[0] * 8
+        C = np.zeros((A.shape[0], qw.shape[1]))
+        for k0 in range(0, K, slab):
+            k1 = min(K, k0 + slab)
+            g0 = min(k0 // 128 + 1, K // 128 - (k1 - k0) // 128)
+            C += A[:, k0:k1].astype(np.float64) @ ref.dequant_w4a16(qw[k0 // 8:k1 // 8],
+                                                                   s[g0:g0 + (k1 - k0) // 128])
+        return C
+
+    assert _pins_hold(lambda A, qw, s: ref.gemm_w4a16(A, qw, s))
+    assert not _pins_hold(misaligned)
+    assert not _pins_hold(off_by_one)
+
+
+def test_w4a8_k_slabs_one_hot_with_varying_group_scales():
+    # one-hot int8 rows across slab boundaries with a different int8 group scale
+    # in every (group, column): acc row = q[k, :] * s_g[k // 128, :] exactly
+    K, N = 8192, 16
+    rng = np.random.default_rng(33)
+    q = rng.integers(-8, 8, size=(K, N))
+    sg = ((np.arange((K // 128) * N).reshape(K // 128, N) * 37) % 255 - 127).astype(np.int8)
+    assert len(np.unique(sg)) == 255          # no two adjacent groups of a column agree
+    qw = gen.pack_nibbles_u32((q & 0xF).astype(np.uint8))
+    A = np.zeros((len(_SLAB_KS), K), dtype=np.int8)
+    A[np.arange(len(_SLAB_KS)), list(_SLAB_KS)] = 1
+    acc = ref.w4a8_acc(A, qw, sg)
+    for i, k in enumerate(_SLAB_KS):
+        assert acc[i].tolist() == [int(q[k, n]) * int(sg[k // 128, n]) for n in range(N)], k
+
+
+def test_w4a8_bruteforce_at_k4096_with_random_group_scales():
+    # two slabs; random int8 group scales over the whole int8 range, compared
+    # with Python-int brute force on a few columns (equality)
+    K, N, M = 4096, 64, 2
+    rng = np.random.default_rng(34)
+    A = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    q = rng.integers(-8, 8, size=(K, N))
+    sg = rng.integers(-128, 128, size=(K // 128, N)).astype(np.int8)
+    qw = gen.pack_nibbles_u32((q & 0xF).astype(np.uint8))
+    cols = np.array([0, 5, 31, 63])
+    acc = ref.w4a8_acc(A, qw, sg, cols=cols)
+    exact = _bruteforce_w4a8(A, qw[:, cols], sg[:, cols])
+    assert acc.tolist() == exact.tolist()
