@@ -19,6 +19,7 @@ __all__ = [
     "w4a8_fp16", "FMT_W4G", "DT_F16", "DT_BF16", "packed_bytes_w4g", "workspace_bytes_w4g",
     "repack_w4g", "w4g", "FMT_W4A16_SP24", "repack_sp24", "w4a16_sp24", "FMT_BITPLANE",
     "packed_bytes_bitplane", "workspace_bytes_bitplane", "repack_bitplane", "bitplane_a8", "plan_info",
+    "w4a16_noalloc",
 ]
 
 FMT_W4A16 = 1
@@ -40,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "qgemm_plan", "qgemm_set_plan_override", "qgemm_quantize_a8", "qgemm_w4g_packed_bytes",
     "qgemm_w4g_workspace_bytes", "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24",
     "qgemm_bitplane_packed_bytes", "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack",
-    "qgemm_bitplane_a8", "qgemm_bitplane_plan", "qgemm_w4g_plan", "qgemm_plan_info",
+    "qgemm_bitplane_a8", "qgemm_bitplane_plan", "qgemm_w4g_plan", "qgemm_plan_info", "qgemm_w4a16_noalloc",
 )
 
 
@@ -89,12 +90,13 @@ def lib() -> ctypes.CDLL:
         L.qgemm_bitplane_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int64)]
         L.qgemm_w4g_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_int64)]
         L.qgemm_plan_info.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.qgemm_w4a16_noalloc.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
                      "qgemm_quantize_a8", "qgemm_w4g_packed_bytes", "qgemm_w4g_workspace_bytes",
                      "qgemm_w4g_repack", "qgemm_w4g", "qgemm_w4a16_sp24", "qgemm_bitplane_packed_bytes",
                      "qgemm_bitplane_workspace_bytes", "qgemm_bitplane_repack", "qgemm_bitplane_a8",
-                     "qgemm_bitplane_plan", "qgemm_w4g_plan", "qgemm_plan_info"):
+                     "qgemm_bitplane_plan", "qgemm_w4g_plan", "qgemm_plan_info", "qgemm_w4a16_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -267,6 +269,18 @@ def w4a16(A, blob, K: int, N: int, out=None, workspace: Workspace | None = None)
     ws, wsb = (workspace or _default_ws).get(workspace_bytes(FMT_W4A16, M, K, N), A.device)
     _check(lib().qgemm_w4a16(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K, N,
                              _ptr(ws), wsb, _stream_ptr(A.device)), "qgemm_w4a16")
+    return out
+
+
+def w4a16_noalloc(A, blob, K: int, N: int, out=None):
+    """qgemm_w4a16 without a workspace argument: the library's own fixed
+    split-K scratch array serves the call (nothing is allocated except `out`
+    when it is not given)."""
+    _require_cuda(A, blob)
+    M = A.shape[0]
+    out = _gemm_out(M, N, A.device, out)
+    _check(lib().qgemm_w4a16_noalloc(_ptr(A), A.stride(0), _ptr(blob), _ptr(out), out.stride(0), M, K, N,
+                                     _stream_ptr(A.device)), "qgemm_w4a16_noalloc")
     return out
 
 

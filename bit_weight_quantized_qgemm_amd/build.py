@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
 SOURCES = ["api.cpp", "repack.hip", "w4a16.hip", "w4a8.hip", "w2w4.hip", "wide.hip", "quant.hip", "w4g.hip", "sp24.hip",
-           "bitplane_lo.hip", "bitplane_hi.hip"]
+           "bitplane_lo.hip", "bitplane_hi.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -648,6 +648,7 @@ struct GemmCall {
   bool zeros = false;
   bool bf16 = false;
   int bits = 4;           // bit-plane format only
+  bool dry = false;       // validate only: no workspace checks, no launch
 };
 
 int run_gemm(const GemmCall& g) {
@@ -667,7 +668,7 @@ int run_gemm(const GemmCall& g) {
   if (g.acc_out && !aligned(g.acc_out, 4)) return QGEMM_ERR_ALIGN;
   const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N, g.bits, g.gs, g.zeros);
   if (pl.kernel == 0) return no_plan();
-  if (pl.ws_bytes > 0) {
+  if (pl.ws_bytes > 0 && !g.dry) {
     if (!g.ws) return QGEMM_ERR_NULL;
     if (g.ws_bytes < pl.ws_bytes) return QGEMM_ERR_WORKSPACE;
     if (!aligned(g.ws, 16)) return QGEMM_ERR_ALIGN;
@@ -690,6 +691,7 @@ int run_gemm(const GemmCall& g) {
     return QGEMM_ERR_ALIAS;
   st = check_device();
   if (st) return st;
+  if (g.dry) return QGEMM_OK;
 
   qg::GemmArgs a{};
   const char* blob = static_cast<const char*>(g.packed);
@@ -737,6 +739,21 @@ int run_gemm(const GemmCall& g) {
 }
 
 }  // namespace
+
+namespace qg {
+
+int fail_hip(hipError_t e, const char* what) { return hip_fail(e, what); }
+
+void set_last_error(const std::string& text) { g_last_error = text; }
+
+int validate_w4a16(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M, int64_t K,
+                   int64_t N) {
+  GemmCall g{QGEMM_FMT_W4A16, A, lda, nullptr, packed, C, ldc, nullptr, M, K, N, nullptr, 0, nullptr};
+  g.dry = true;
+  return run_gemm(g);
+}
+
+}  // namespace qg
 
 extern "C" {
 

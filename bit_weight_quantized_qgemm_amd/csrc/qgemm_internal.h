@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace qg {
 
 constexpr int kGroup = 128;          // k per quantization group
@@ -123,6 +125,14 @@ hipError_t launch_bitplane_lo(const Plan& pl, const GemmArgs& a, int bits, hipSt
 hipError_t launch_bitplane_hi(const Plan& pl, const GemmArgs& a, int bits, hipStream_t s);   // bits 5..8
 
 hipError_t launch_zero_fill(void* dst, size_t bytes, hipStream_t s);
+
+// Error plumbing and argument checks shared by the C-ABI entry points: record
+// a HIP failure (returns QGEMM_ERR_HIP), record an error text, and run every
+// check of qgemm_w4a16 except the workspace's without launching anything.
+int fail_hip(hipError_t e, const char* what);
+void set_last_error(const std::string& text);
+int validate_w4a16(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M, int64_t K,
+                   int64_t N);
 hipError_t launch_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* Q, int64_t ldq,
                               void* S, hipStream_t s);
 hipError_t launch_repack_w4a16(const BlobLayout& L, const void* codes, const void* scales,

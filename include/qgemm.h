@@ -286,6 +286,26 @@ int qgemm_bitplane_a8(const void* A, int64_t lda, const void* a_scale, const voi
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qgemm_w4a16 for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, kernels, plans and results as qgemm_w4a16 minus the workspace:
+ * the split-K arrival counters and partial sums live in a fixed 32 MiB device
+ * array of this library (one per GPU, held until the process ends; its
+ * address is looked up once per device). The call allocates and frees
+ * nothing; the caller still provides A, the blob and C.
+ *   - A call whose plan needs more than 32 MiB of split-K scratch (only forced
+ *     plans: every automatic W4A16 plan needs at most 16 MiB + 64 KiB) returns
+ *     QGEMM_ERR_WORKSPACE before any launch; other errors as qgemm_w4a16.
+ *   - The first call on a device queues a clear of the array's counters on
+ *     `stream` before its GEMM; every completed call leaves them zero again.
+ *   - All calls on one GPU share its array: calls that can overlap (on
+ *     different streams, or concurrent graph replays) race and give wrong
+ *     results. Serialize them, or use qgemm_w4a16 with one workspace each.
+ */
+int qgemm_w4a16_noalloc(const void* A, int64_t lda, const void* packed, void* C, int64_t ldc, int64_t M,
+                        int64_t K, int64_t N, void* stream);
+
+/*
  * Work decomposition used for a call of this shape (for tests and tuning).
  * Fills out10[0..9] = {kernel id (1 streaming, 2 wide, 3 streaming general-grid
  * kernel with per-lane grid entries; 1 there stages them in LDS), 16-row blocks per tile
