@@ -116,6 +116,10 @@ def parse():
     ap.add_argument("--shapes", default="all", choices=["all", "up", "down"])
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other configured workloads (7B layers, W4A8, mixed 2/4-bit)")
+    ap.add_argument("--only-secondary", action="store_true",
+                    help="time only the other configured workloads (for kernel traces of them)")
+    ap.add_argument("--secondary-filter", default="",
+                    help="comma-separated substrings: keep only secondary workloads whose name contains one")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (the known-size "
                          "reference for HBM byte counters)")
@@ -258,7 +262,7 @@ def secondary_bytes_ops(fmt, K, N, M, n4=0, gs=128, zeros=False, name_bits=4):
             alg_flops(M, K, N))
 
 
-def secondary(torch, qg, dev, rotate_mb):
+def secondary(torch, qg, dev, rotate_mb, name_filter=""):
     """The other configured workloads, each timed as replays of a captured HIP
     graph of back-to-back launches over rotating weight copies (kernel time
     without host launch overhead; weights stream from HBM)."""
@@ -266,7 +270,10 @@ def secondary(torch, qg, dev, rotate_mb):
     stream = torch.cuda.current_stream()
     rows = []
     built = {}
+    keep = [f for f in name_filter.split(",") if f]
     for (name, fmt, K, N, M) in SECONDARY:
+        if keep and not any(f in name for f in keep):
+            continue
         key = (fmt, K, N, name if fmt in (6, 8) else "")
         if key not in built:
             if fmt == 8:
@@ -379,8 +386,19 @@ def secondary(torch, qg, dev, rotate_mb):
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "roofline_frac": round(roof_us / us, 4),
                      "bound": "hbm" if byt / (HBM_PEAK_GBS * 1e9) >= ops / (peak * 1e12) else "mfma",
                      "launches_per_graph": n})
+        print(f"[bench] secondary {name} K={K} N={N} M={M}: {us:.2f} us", file=sys.stderr, flush=True)
         del g
     return rows
+
+
+def copy_probe(torch, dev, mib):
+    """One plain device copy of `mib` MiB: the known-size reference for HBM
+    byte counters (FETCH_SIZE, WRITE_SIZE) in profiled runs."""
+    src = torch.ones(mib * 2**20 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -394,6 +412,14 @@ def main():
 
     import bit_weight_quantized_qgemm_amd as qg
     from synth import gen
+
+    if args.only_secondary:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        if args.copy_probe_mib:
+            copy_probe(torch, dev, args.copy_probe_mib)
+        print(json.dumps({"secondary": secondary(torch, qg, dev, 512, args.secondary_filter)}), flush=True)
+        return
 
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
 
@@ -437,12 +463,9 @@ def main():
             launch(cs, i)
 
     if args.copy_probe_mib:
-        src = torch.ones(args.copy_probe_mib * 2**20 // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(torch, dev, args.copy_probe_mib)
 
+    print(f"[bench] inputs resident: {len(cases)} launches per step", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -530,7 +553,7 @@ def main():
                  "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                  "source_sha": source_sha()})
 
-    sec = None if args.no_secondary else secondary(torch, qg, dev, 512)
+    sec = None if args.no_secondary else secondary(torch, qg, dev, 512, args.secondary_filter)
 
     out = {
         "metric": METRIC,

@@ -32,7 +32,9 @@ DT_F16 = 1
 DT_BF16 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libqgemm.so")
+# QGEMM_LIB selects another build of the same library (the host-sanitized
+# build of the CPU test tier); by default the in-tree libqgemm.so
+_LIB_PATH = os.environ.get("QGEMM_LIB") or os.path.join(_HERE, "libqgemm.so")
 _lib = None
 
 EXPORTED_SYMBOLS = (

@@ -216,12 +216,11 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
 namespace {
 const char* const kOccW4A16 = "888555777555";   // 32-row two-block tiles: the M32 policy
 const char* const kOccW4A8 = "888555677444";
-const char* const kOccW2W4 = "677444655444";
+const char* const kOccW2W4 = "666444655444";
 const char* const kOccW4G = "55544434423d";    // grid entries staged in LDS
 const char* const kOccW4GL = "55544434423d";   // grid entries loaded per lane
 const char* const kOccSP24 = "666555555444";
-const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455444",
-                               "67755544433d", "56645534433d", "55544434433d", "55544423d13d"};
+const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455344", "67755544443d", "56645534433d", "55544434433d", "55544423d13d"};
 }  // namespace
 
 KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int kernel) {
@@ -400,6 +399,31 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
             best_s = s;
           }
         }
+      }
+    }
+  }
+  // Small batches (16-row tiles) of W4A16 and W4A8 on layers with between half
+  // as many and as many 64-column tiles as CUs: one workgroup of four K-parts
+  // per tile and no k-split, when the extra bytes each busy CU streams over a
+  // launch on all CUs stay under 96 KB. Measured on MI355X: 4096 x 11008 at
+  // M = 1-16 in 7.9-8.6 us against 10.6-11.2 us with three k-splits (W4A8 at
+  // M = 16: 7.9 against 11.2 us); the cross-workgroup reduction costs more
+  // than the unused CUs there. Layers whose CUs would each stream much more
+  // (28672 x 8192) keep their k-splits.
+  if (have && !force_nb && !force_wpt && !force_splits && pl.mb == 1 &&
+      (fmt == QGEMM_FMT_W4A16 || fmt == QGEMM_FMT_W4A8) && G >= 4) {
+    const int64_t T = N / 64;
+    const double extra = blob * (1.0 / (double)T - 1.0 / (double)cus);
+    if (2 * T >= cus && T <= cus && extra < 96.0 * 1024.0 && !skinny_occupancy(fmt, 1, 1, 4, bits, var).spills) {
+      Plan c = pl;
+      c.kernel = var;
+      c.nb = 1;
+      c.wpt = 16;
+      c.gps = G;
+      if (plan_lds(fmt, c, G, bits, gs, zeros) <= kSkinnyLdsBudget) {
+        best_nb = 1;
+        best_kp = 4;
+        best_s = 1;
       }
     }
   }

@@ -45,11 +45,13 @@ struct PolicyBP : Tile16 {
   template <int NBW>
   struct Stage {
     static constexpr int kVmem = NBW * kLoads;
+    static constexpr int kVmemFirst = NBW * kLoads;
     uint32_t w[NBW][B];
   };
 
   __host__ __device__ static int extra_lds(int, int, int) { return 0; }
-  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
+  static constexpr bool kStageExtra = false;
+  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int, int, int, int) {}
 
   // 4*n bytes at (voff, soff) into w[0..n-1], n = 1..4
   template <int n>
@@ -88,15 +90,15 @@ struct PolicyBP : Tile16 {
       rc = make_rsrc(static_cast<const char*>(p.codes) + ((size_t)gw0 * nbt + bw) * 256 * B,
                      (uint32_t)(nload - 1) * gstep + NBW * 256u * B);
     }
-    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         const uint32_t soff = j * 256u * B + rel * gstep;
-        load_words<(B > 4 ? 4 : B)>(rc, cvoff, soff, st.w[j]);
-        if constexpr (B > 4) load_words<B - 4>(rc, cvoff + 16u, soff, st.w[j] + 4);
+        load_words<(B > 4 ? 4 : B)>(rc, cvoff + oob, soff, st.w[j]);
+        if constexpr (B > 4) load_words<B - 4>(rc, cvoff + 16u + oob, soff, st.w[j] + 4);
       }
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>&, int) const {}
+    __device__ __forceinline__ void load_lds(Stage<NBW>&, int, uint32_t) const {}
   };
 
   // bits 4d..4d+3 of x (d = 0..3, counting from bit `off`) -> bytes 0 or 1

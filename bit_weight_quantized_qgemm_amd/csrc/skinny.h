@@ -72,18 +72,33 @@ __device__ __forceinline__ bool workgroup_arrive_last(uint32_t* counter, uint32_
   return *flag != 0;
 }
 
-// Cooperative copy of the tile's group-scale chunks into LDS: for each of the NB
-// column blocks, n8 chunks of `chunk` bytes starting at chunk c8.
-__device__ __forceinline__ void stage_scales(const void* scales, char* lds, int NB, int G8, int b0,
-                                             int c8, int n8, int chunk) {
-  const int per_blk = n8 * chunk / 16;      // 16-byte pieces per block
-  const int total = NB * per_blk;
-  for (int t = threadIdx.x; t < total; t += blockDim.x) {
-    const int j = t / per_blk, o = t % per_blk;
-    const u32x4* src = static_cast<const u32x4*>(scales) +
-                       ((size_t)(b0 + j) * G8 + c8) * (chunk / 16) + o;
-    reinterpret_cast<u32x4*>(lds)[t] = *src;
+// Direct buffer-to-LDS copy of `pieces` 16-byte pieces to dst .. dst + 16*pieces
+// (dst 16-byte aligned): piece p comes from byte offset src_of(p) of resource
+// r. The workgroup's waves take 1 KB rows of the destination in turn; lanes
+// past the last piece are masked off, so nothing beyond the destination is
+// written. The copies count on the vector memory counter like any load, and
+// become visible to other waves after their issuing wave has waited for them
+// and passed a barrier.
+template <class SrcOf>
+__device__ __forceinline__ void dma16(rsrc_t r, char* dst, int pieces, const SrcOf& src_of, int wave, int nwaves,
+                                      int lane) {
+  const int rows = (pieces + 63) >> 6;
+  for (int t = wave; t < rows; t += nwaves) {
+    const int p = (t << 6) + lane;
+    if (p < pieces) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + (t << 10)), 16, src_of(p), 0, 0, 0);
   }
+}
+
+// The tile's group-scale chunks into LDS by direct loads: for each of the NB
+// column blocks, n8 chunks of `chunk` bytes starting at chunk c8 ([NB][n8][chunk]).
+__device__ __forceinline__ void stage_scales(const void* scales, char* lds, int NB, int G8, int b0,
+                                             int c8, int n8, int chunk, int wave, int nwaves, int lane) {
+  const int per_blk = n8 * chunk / 16;      // 16-byte pieces per block
+  const rsrc_t r = make_rsrc(static_cast<const char*>(scales) + (size_t)b0 * G8 * chunk, (uint32_t)(NB * G8 * chunk));
+  dma16(r, lds, NB * per_blk, [&](int p) {
+    const int j = p / per_blk, o = p - j * per_blk;
+    return (uint32_t)((j * G8 + c8) * chunk + o * 16);
+  }, wave, nwaves, lane);
 }
 
 // Geometry shared by the policies built on 16 x 16 MFMA tiles: the position
@@ -133,6 +148,7 @@ struct SkinnyLds {
 
 template <class F>
 __host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_max, int ng_max, int gs) {
+  constexpr int WD = F::kWeightDepth;
   SkinnyLds L;
   const int NB = 4 * NBW;
   L.scale_bytes = F::kStageScales ? NB * n8_max * F::kScaleChunk : 0;
@@ -140,7 +156,7 @@ __host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_
   const int extra = F::extra_lds(NB, ng_max, gs);
   L.ring_off = (L.extra_off + extra + 255) / 256 * 256;
   L.slot_bytes = MB * F::kFrag * 1024;
-  const int rings = L.ring_off + KP * (F::kWeightDepth + 1) * L.slot_bytes;
+  const int rings = L.ring_off + KP * (WD + 1) * L.slot_bytes;
   const int red = KP * 4 * MB * NBW * 1024;   // one 1 KB fragment of floats per (wave, block)
   L.total = rings > red ? rings : red;
   return L;
@@ -148,6 +164,7 @@ __host__ __device__ inline SkinnyLds skinny_lds(int MB, int NBW, int KP, int n8_
 
 template <class F, int MB, int NBW, int KP>
 __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* flag) {
+  constexpr int WD = F::kWeightDepth;
   using Acc = typename F::Acc;
   using Stage = typename F::template Stage<NBW>;
   using View = typename F::template View<NBW>;
@@ -194,12 +211,12 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
     afrag[q] = fr;
     avoff[q] = F::a_voff(fr, lane, ti.rows, arow);
   }
-  char* ring = lds + L.ring_off + kp * (F::kWeightDepth + 1) * L.slot_bytes;
-  auto issue_a = [&](int rel, int slot) {
+  char* ring = lds + L.ring_off + kp * (WD + 1) * L.slot_bytes;
+  auto issue_a = [&](int rel, int slot, uint32_t oob) {
 #pragma unroll
     for (int q = 0; q < kAPerWave; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(ring + slot * L.slot_bytes + afrag[q] * 1024), 16,
-                                               avoff[q], rel * (128u * F::kAElem), 0, 0);
+                                               avoff[q] + oob, rel * (128u * F::kAElem), 0, 0);
   };
 
   const View v(p, lds, L, ti, ti.b0 + nw * NBW, gk0c, nload, lane);
@@ -211,25 +228,46 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
 
   // ---- prologue. Weights and activations both run kWD = F::kWeightDepth
   // groups ahead, in a register ring of kWD + 1 stages and an LDS ring of
-  // kWD + 1 slots. (For the 16-byte-per-lane formats a deeper weight ring was
-  // measured slower on MI355X: the extra registers cost occupancy.)
-  // The first loads go out before the scale staging.
-  constexpr int kWD = F::kWeightDepth, kWS = kWD + 1, kAS = kWD + 1;
+  // kWD + 1 slots. (A deeper ring measured slower on MI355X: three and four
+  // groups ahead by 0-29 %, and eight groups - every group of a short K-part in
+  // flight at once - by 5-50 % on 4096 x 4096 to 28672 x 8192 layers at
+  // M <= 16, also with its loads past the K-part's end reading nothing.)
+  // The tile's staged data (group scales, grid entries, descriptors) goes to
+  // LDS first, by direct loads, then the first groups' loads; a counted wait
+  // then retires only the staging copies, so the first groups stay in flight
+  // while the barrier publishes the staged data (a full __syncthreads here
+  // would drain every load in flight).
+  constexpr int kWD = WD, kWS = kWD + 1, kAS = kWD + 1;
   static_assert(kWD >= 2, "at least two groups in flight");
+  constexpr bool kStaged = F::kStageScales || F::kStageExtra;
+  // Group g of the K-part (relative to its first): loads past the K-part's last
+  // group keep the fixed count but read nothing: their per-lane offsets move
+  // past the buffer's size (2^31 and up), so the hardware returns zeros
+  // without a memory access (and direct-to-LDS loads write zeros to their
+  // slot, which no later group uses).
   auto wl = [&](int g) { return min(g, nload - 1); };
+  auto oob = [&](int g) { return g >= nload ? 0x80000000u : 0u; };
+  if constexpr (kStaged) {
+    if constexpr (F::kStageScales)
+      stage_scales(p.scales, lds, NB, p.G8, ti.b0, ti.c8, ti.n8, F::kScaleChunk, wave, 4 * KP, lane);
+    F::stage_extra(p, lds + L.extra_off, ti, NB, wave, 4 * KP, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   Stage st[kWS];
 #pragma unroll
   for (int d = 0; d < kWD; ++d) {
-    issue_a(wl(d), d);
+    issue_a(wl(d), d, oob(d));
     __builtin_amdgcn_sched_barrier(0);
-    v.load_vmem(st[d], wl(d));
+    v.load_vmem(st[d], wl(d), oob(d));
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (F::kStageScales) stage_scales(p.scales, lds, NB, p.G8, ti.b0, ti.c8, ti.n8, F::kScaleChunk);
-  F::stage_extra(p, lds + L.extra_off, ti, NB);
-  __syncthreads();
+  if constexpr (kStaged) {
+    // loads issued after the staging copies: kWD groups of activations and weights
+    wait_vmcnt<kWD * (kAPerWave + Stage::kVmemFirst)>();
+    raw_barrier();
+  }
 #pragma unroll
-  for (int d = 0; d < kWD; ++d) v.load_lds(st[d], wl(d));
+  for (int d = 0; d < kWD; ++d) v.load_lds(st[d], wl(d), oob(d));
 
   const typename F::Consts k;
   // Per iteration each wave first issues the weights of group i + kWD (their
@@ -242,21 +280,27 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
   // more), and the counter retires loads in order. Issuing the weights before
   // the wait keeps them in flight while the wave waits at the barrier
   // (measured on MI355X: 3-6 % at M = 4-32 on the down projection).
+  //
+  // Loads keep this fixed count to the end: the last kWD iterations issue
+  // out-of-range loads (see oob) instead of skipping their loads. A variant
+  // that skipped them, with exact smaller waits in those iterations, measured
+  // 5-45 % slower on MI355X (the compiler's own waits around the conditional
+  // loads serialized the ring).
   constexpr int kAfter = Stage::kVmem + (kWD - 1) * (kAPerWave + Stage::kVmem);
   for (int base = 0; base < iters; base += kWS) {
 #pragma unroll
     for (int r = 0; r < kWS; ++r) {
       const int i = base + r;
       if (i < iters) {   // uniform over the workgroup
-        v.load_vmem(st[(r + kWD) % kWS], wl(i + kWD));
+        v.load_vmem(st[(r + kWD) % kWS], wl(i + kWD), oob(i + kWD));
         // the count relies on this order: keep the compiler from moving loads
         // across the wait or between the weights and the activations
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<kAfter>();
         raw_barrier();
-        issue_a(wl(i + kWD), (r + kWD) % kAS);
+        issue_a(wl(i + kWD), (r + kWD) % kAS, oob(i + kWD));
         __builtin_amdgcn_sched_barrier(0);
-        v.load_lds(st[(r + kWD) % kWS], wl(i + kWD));
+        v.load_lds(st[(r + kWD) % kWS], wl(i + kWD), oob(i + kWD));
         F::template compute<MB, NBW>(st[r], ring + (r % kAS) * L.slot_bytes, acc, i < ngk, k, lane);
       }
     }

@@ -57,12 +57,14 @@ struct PolicySP24 {
   template <int NBW>
   struct Stage {
     static constexpr int kVmem = NBW;       // one 12-byte load per column block
+    static constexpr int kVmemFirst = NBW;
     u32x3 rec[NBW];                         // code words 0, 1 and the position word
     uint32_t s[NBW][2];                     // fp16 scales of columns 4h .. 4h+3 (pairs)
   };
 
   __host__ __device__ static int extra_lds(int, int, int) { return 0; }
-  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
+  static constexpr bool kStageExtra = false;
+  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int, int, int, int) {}
 
   template <int NBW>
   struct View {
@@ -82,12 +84,13 @@ struct PolicySP24 {
       sblk = ti.n8 * kScaleChunk;
       sl = lds + (bw - ti.b0) * sblk + 4 * (lane >> 4) * 16;
     }
-    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
-        st.rec[j] = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12u, j * 768u + rel * gstep, 0));
+        st.rec[j] = __builtin_bit_cast(
+            u32x3, __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12u + oob, j * 768u + rel * gstep, 0));
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t) const {
       const int g = gw0 + rel;
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7) * 2;
 #pragma unroll

@@ -41,22 +41,29 @@ struct PolicyW2W4 : Tile16 {
   template <int NBW>
   struct Stage {
     static constexpr int kVmem = 2 * NBW;   // base plane + high plane loads
+    static constexpr int kVmemFirst = NBW;  // load_vmem: the base plane only
     u32x2 base[NBW];
     u32x2 high[NBW];
     uint32_t is4[NBW];
     uint32_t s[NBW];
   };
 
-  // descriptors of the workgroup's chunks, [NB][groups of the split]
+  // descriptors of the workgroup's chunks, [groups of the split][NB], by
+  // direct loads: row i is the NB consecutive descriptors of group G0 + i
+  // (NB * 8 bytes, whole 16-byte pieces)
+  static constexpr bool kStageExtra = true;
   __host__ __device__ static int extra_lds(int NB, int ng, int) { return NB * ng * 8; }
-  __device__ static void stage_extra(const GemmArgs& p, char* dst_, const TileInfo& ti, int NB) {
-    u32x2* dst = reinterpret_cast<u32x2*>(dst_);
-    const u32x2* src = static_cast<const u32x2*>(p.aux);
+  __device__ static void stage_extra(const GemmArgs& p, char* dst, const TileInfo& ti, int NB, int wave,
+                                     int nwaves, int lane) {
     const int ng = ti.G1 - ti.G0;
-    for (int t = threadIdx.x; t < NB * ng; t += blockDim.x) {
-      const int j = t / ng, i = t % ng;
-      dst[t] = src[(size_t)(ti.G0 + i) * (p.N / 16) + ti.b0 + j];
-    }
+    const int ppr = NB / 2;                         // 16-byte pieces per row
+    const uint32_t srow = (uint32_t)(p.N / 16) * 8u;
+    const rsrc_t r = make_rsrc(static_cast<const char*>(p.aux) + (size_t)ti.G0 * srow + (size_t)ti.b0 * 8,
+                               (uint32_t)(ng - 1) * srow + (uint32_t)NB * 8u);
+    dma16(r, dst, ng * ppr, [&](int q) {
+      const int i = q / ppr;
+      return (uint32_t)i * srow + (uint32_t)(q - i * ppr) * 16u;
+    }, wave, nwaves, lane);
   }
 
   template <int NBW>
@@ -64,7 +71,7 @@ struct PolicyW2W4 : Tile16 {
     rsrc_t rb, rh;
     uint32_t bvoff, gstep;
     const char* sl;
-    const u32x2* desc;   // this wave's first block in the [NB][ngw] LDS table
+    const u32x2* desc;   // this wave's first block in the [ngw][NB] LDS table
     uint32_t sblk, below, hoff;
     int gw0, c8, G0, ngw, c;
 
@@ -82,21 +89,21 @@ struct PolicyW2W4 : Tile16 {
       rh = make_rsrc(p.high, 0x7FFFFFF0u);
       sblk = ti.n8 * kScaleChunk;
       sl = lds + (bw - ti.b0) * sblk + c * 16;
-      desc = reinterpret_cast<const u32x2*>(lds + L.extra_off) + (bw - ti.b0) * ngw;
+      desc = reinterpret_cast<const u32x2*>(lds + L.extra_off) + (bw - ti.b0);
       below = (1u << c) - 1u;
       hoff = (lane >> 4) * 8u;
     }
-    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.base[j] = load8(rb, bvoff, j * 512u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.base[j] = load8(rb, bvoff + oob, j * 512u + rel * gstep);
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t oob) const {
       const int g = gw0 + rel;
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const u32x2 d = desc[j * ngw + (g - G0)];
+        const u32x2 d = desc[(g - G0) * (4 * NBW) + j];
         const uint32_t is4 = (d[1] >> c) & 1u;
-        const uint32_t off = is4 ? (d[0] + __builtin_popcount(d[1] & below)) * 32u + hoff : 0x7FFFFFF8u;
+        const uint32_t off = (is4 && !oob) ? (d[0] + __builtin_popcount(d[1] & below)) * 32u + hoff : 0x7FFFFFF8u;
         st.high[j] = load8(rh, off, 0);
         st.is4[j] = is4;
       }

@@ -34,12 +34,14 @@ struct PolicyW4A16 : Tile16 {
   template <int NBW>
   struct Stage {
     static constexpr int kVmem = NBW;   // vector memory operations per stage
+    static constexpr int kVmemFirst = NBW;   // ... issued by load_vmem
     u32x4 code[NBW];
     uint32_t s[NBW];                    // fp16 scale bits in the low half
   };
 
+  static constexpr bool kStageExtra = false;
   __host__ __device__ static int extra_lds(int, int, int) { return 0; }
-  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
+  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int, int, int, int) {}
 
   template <int NBW>
   struct View {
@@ -60,11 +62,11 @@ struct PolicyW4A16 : Tile16 {
       sblk = ti.n8 * kScaleChunk;
       sl = lds + (bw - ti.b0) * sblk + (lane & 15) * 16;
     }
-    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * 1024u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff + oob, j * 1024u + rel * gstep);
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t) const {
       const int g = gw0 + rel;
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7) * 2;
 #pragma unroll
@@ -151,12 +153,14 @@ struct PolicyW4A16M32 {
   struct Stage {
     static_assert(NBW == 2, "one 32-column block per wave");
     static constexpr int kVmem = 3;
+    static constexpr int kVmemFirst = 3;
     u32x4 even, odd;
     uint32_t s;
   };
 
+  static constexpr bool kStageExtra = false;
   __host__ __device__ static int extra_lds(int, int, int) { return 0; }
-  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
+  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int, int, int, int) {}
 
   template <int NBW>
   struct View {
@@ -178,13 +182,13 @@ struct PolicyW4A16M32 {
       rs = make_rsrc(static_cast<const char*>(p.scales) + (size_t)bw * sblk, 2 * sblk);
       svoff = (uint32_t)((c32 >> 4) * sblk + (c32 & 15) * 16);
     }
-    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
-      st.even = load16(rc, cvoff, rel * gstep);
-      st.odd = load16(rc, cvoff + 512u, rel * gstep);
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
+      st.even = load16(rc, cvoff + oob, rel * gstep);
+      st.odd = load16(rc, cvoff + 512u + oob, rel * gstep);
       const int g = gw0 + rel;
-      st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff, (uint32_t)(g >> 3) * 256u + (uint32_t)(g & 7) * 2u, 0);
+      st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff + oob, (uint32_t)(g >> 3) * 256u + (uint32_t)(g & 7) * 2u, 0);
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>&, int) const {}
+    __device__ __forceinline__ void load_lds(Stage<NBW>&, int, uint32_t) const {}
   };
 
   template <int MB, int NBW>

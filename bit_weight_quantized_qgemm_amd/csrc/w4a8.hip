@@ -35,12 +35,14 @@ struct PolicyW4A8 : Tile16 {
   template <int NBW>
   struct Stage {
     static constexpr int kVmem = NBW;
+    static constexpr int kVmemFirst = NBW;
     u32x4 code[NBW];
     int32_t s[NBW];
   };
 
   __host__ __device__ static int extra_lds(int, int, int) { return 0; }
-  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int) {}
+  static constexpr bool kStageExtra = false;
+  __device__ static void stage_extra(const GemmArgs&, char*, const TileInfo&, int, int, int, int) {}
 
   template <int NBW>
   struct View {
@@ -61,11 +63,11 @@ struct PolicyW4A8 : Tile16 {
       sblk = ti.n8 * kScaleChunk;
       sl = lds + (bw - ti.b0) * sblk + (lane & 15) * 8;
     }
-    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * 1024u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff + oob, j * 1024u + rel * gstep);
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t) const {
       const int g = gw0 + rel;
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7);
 #pragma unroll

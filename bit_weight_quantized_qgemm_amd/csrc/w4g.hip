@@ -61,6 +61,7 @@ struct PolicyW4G : Tile16 {
   template <int NBW>
   struct Stage {
     static constexpr int kVmem = kStaged ? NBW : 2 * NBW;   // codes (+ entries when not staged)
+    static constexpr int kVmemFirst = kVmem;
     u32x4 code[NBW];
     u32x2 e[NBW];                                           // entries of the chunk's two 64-k halves
   };
@@ -69,25 +70,29 @@ struct PolicyW4G : Tile16 {
   // its split: [chunk - G0][NB * 16 columns][per] entries, per = 2 (the
   // chunk's two 64-k groups) when gs = 64, else 1 (the group that holds the
   // chunk, repeated for each of its chunks).
+  static constexpr bool kStageExtra = kStaged;
   __host__ __device__ static int extra_lds(int NB, int ng, int gs) {
     return kStaged ? ng * NB * 16 * (gs == 64 ? 2 : 1) * (int)kEntry : 0;
   }
-  __device__ static void stage_extra(const GemmArgs& p, char* dst, const TileInfo& ti, int NB) {
+  // the staged rows by direct loads: row r of the split is entry row (G0 + r)
+  // (group length 64) or (G0 + r) / cpg of the blob, columns b0*16 .. + NB*16
+  __device__ static void stage_extra(const GemmArgs& p, char* dst, const TileInfo& ti, int NB, int wave,
+                                     int nwaves, int lane) {
     if constexpr (kStaged) {
       const int cpg = p.gs == 64 ? 0 : p.gs / 128;
       const int per = cpg ? 1 : 2;
-      const int rowb = NB * 16 * per * (int)kEntry;   // bytes of a staged row (a multiple of 16)
-      const int pieces = rowb / 16;
-      const size_t srow = (size_t)p.N * per * kEntry;
-      const char* src = static_cast<const char*>(p.scales) + (size_t)ti.b0 * 16 * per * kEntry;
+      const int pieces = NB * per * (int)kEntry;      // 16-byte pieces of a staged row
+      const uint32_t srow = (uint32_t)p.N * per * kEntry;
+      const uint32_t nrows = (uint32_t)(cpg ? p.G / cpg : p.G);
+      const rsrc_t r = make_rsrc(p.scales, nrows * srow);
+      const uint32_t col0 = (uint32_t)ti.b0 * 16u * per * kEntry;
       const int ng = ti.G1 - ti.G0;
-      for (int t = threadIdx.x; t < ng * pieces; t += blockDim.x) {
-        const int r = t / pieces, o = t % pieces;
-        const int g = ti.G0 + r;
-        const size_t row = cpg ? (size_t)(g / cpg) : (size_t)g;
-        *reinterpret_cast<u32x4*>(dst + r * rowb + o * 16) =
-            *reinterpret_cast<const u32x4*>(src + row * srow + o * 16);
-      }
+      dma16(r, dst, ng * pieces, [&](int q) {
+        const int i = q / pieces;
+        const int g = ti.G0 + i;
+        const uint32_t row = (uint32_t)(cpg ? g / cpg : g);
+        return row * srow + col0 + (uint32_t)(q - i * pieces) * 16u;
+      }, wave, nwaves, lane);
     }
   }
 
@@ -120,9 +125,9 @@ struct PolicyW4G : Tile16 {
         re = make_rsrc(p.scales, (uint32_t)(p.K / (cpg ? p.gs : 64)) * (uint32_t)p.N * kEntry);
       }
     }
-    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff, j * 1024u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff + oob, j * 1024u + rel * gstep);
       if constexpr (!kStaged) {
         const int g = gw0 + rel;
         // wave-uniform: one load per block either way
@@ -130,7 +135,7 @@ struct PolicyW4G : Tile16 {
           const uint32_t soff = (uint32_t)g * rowb;
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
-            const uint32_t vo = evoff + j * 16u * 2u * kEntry;
+            const uint32_t vo = evoff + j * 16u * 2u * kEntry + oob;
             if (kZ) {
               st.e[j] = load8(re, vo, soff);
             } else {
@@ -142,7 +147,7 @@ struct PolicyW4G : Tile16 {
           const uint32_t soff = (uint32_t)(g / cpg) * rowb;
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
-            const uint32_t vo = evoff + j * 16u * kEntry;
+            const uint32_t vo = evoff + j * 16u * kEntry + oob;
             const uint32_t w = kZ ? __builtin_amdgcn_raw_buffer_load_b32(re, vo, soff, 0)
                                   : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(re, vo, soff, 0);
             st.e[j] = u32x2{w, w};
@@ -150,7 +155,7 @@ struct PolicyW4G : Tile16 {
         }
       }
     }
-    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel) const {
+    __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t) const {
       if constexpr (kStaged) {
         const char* row = el + (gw0 + rel - G0) * srowb;
         // wave-uniform branch
