@@ -195,7 +195,7 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   const int splits = force_splits ? std::min(force_splits, G) : best;
   pl.gps = (G + splits - 1) / splits;
   pl.splits = (G + pl.gps - 1) / pl.gps;
-  pl.workgroups = tiles * pl.splits;
+  pl.workgroups = launch_workgroups(pl.nt, pl.mt, pl.splits);
   pl.waves = pl.workgroups * pl.wpt;
   pl.lds_bytes = wide_lds_bytes(pl);
   if (pl.splits > 1) {
@@ -326,10 +326,11 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   const bool w4a16_big = fmt == QGEMM_FMT_W4A16 && blob >= 64.0 * 1048576.0;
   const int pref_nb = (fmt != QGEMM_FMT_BITPLANE && (M > 4 || w4a16_big) && blob >= big_blob) ? 2 : 1;
   struct Score {
-    int violations, nb_pen, cost, splits;
+    int violations, kp_pen, nb_pen, cost, splits;
     int64_t neg_waves;
     bool operator<(const Score& o) const {
       if (violations != o.violations) return violations < o.violations;
+      if (kp_pen != o.kp_pen) return kp_pen < o.kp_pen;
       if (nb_pen != o.nb_pen) return nb_pen < o.nb_pen;
       if (cost != o.cost) return cost < o.cost;
       if (splits != o.splits) return splits < o.splits;
@@ -390,6 +391,10 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
           sc.cost = s * kp + s;   // fronts + k-splits
           sc.splits = s;
           sc.nb_pen = nb == pref_nb ? 0 : 1;
+          // general grid at 32-row tiles: one K-part per workgroup measured 10-30 %
+          // slower than two or four on every layer of a forced-plan sweep on MI355X
+          // (4096 x 11008 to 57344 x 8192, M = 32..128)
+          sc.kp_pen = (w4g && pl.mb == 2 && kp == 1) ? 1 : 0;
           sc.neg_waves = -waves;
           if (!have || sc < best) {
             have = true;
@@ -409,12 +414,14 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   // M = 1-16 in 7.9-8.6 us against 10.6-11.2 us with three k-splits (W4A8 at
   // M = 16: 7.9 against 11.2 us); the cross-workgroup reduction costs more
   // than the unused CUs there. Layers whose CUs would each stream much more
-  // (28672 x 8192) keep their k-splits.
-  if (have && !force_nb && !force_wpt && !force_splits && pl.mb == 1 &&
-      (fmt == QGEMM_FMT_W4A16 || fmt == QGEMM_FMT_W4A8) && G >= 4) {
+  // (28672 x 8192) keep their k-splits. The general 4-bit grid takes the same
+  // rule at 16- and 32-row tiles (one row tile): its forced-plan sweep on the
+  // same layers ranked the unsplit four-K-part shape first there.
+  if (have && !force_nb && !force_wpt && !force_splits && pl.mt == 1 &&
+      (((fmt == QGEMM_FMT_W4A16 || fmt == QGEMM_FMT_W4A8) && pl.mb == 1) || w4g) && G >= 4) {
     const int64_t T = N / 64;
     const double extra = blob * (1.0 / (double)T - 1.0 / (double)cus);
-    if (2 * T >= cus && T <= cus && extra < 96.0 * 1024.0 && !skinny_occupancy(fmt, 1, 1, 4, bits, var).spills) {
+    if (2 * T >= cus && T <= cus && extra < 96.0 * 1024.0 && !skinny_occupancy(fmt, pl.mb, 1, 4, bits, var).spills) {
       Plan c = pl;
       c.kernel = var;
       c.nb = 1;
@@ -445,7 +452,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   pl.wpt = 4 * kp;
   pl.splits = splits;
   pl.gps = gps;
-  pl.workgroups = tiles * splits;
+  pl.workgroups = launch_workgroups(pl.nt, pl.mt, splits);
   pl.waves = pl.workgroups * pl.wpt;
   pl.lds_bytes = plan_lds(fmt, pl, G, bits, gs, zeros);
   // no shape of the search fits (or a forced shape does not): refuse the call

@@ -74,6 +74,10 @@ struct Plan {
   size_t lds_bytes = 0;  // dynamic LDS the launch requests
 };
 
+// Workgroups of a launch of nt x mt tiles and `splits` k-splits: one per tile
+// and k-split (the kernels' tile_of_block orders them).
+inline int64_t launch_workgroups(int64_t nt, int64_t mt, int64_t splits) { return nt * mt * splits; }
+
 // dynamic LDS of a wide-kernel launch: per K-part of 8 waves, kWideSlots slots
 // of 16*mb rows x 128 k fp16
 inline size_t wide_lds_bytes(const Plan& pl) { return (size_t)(pl.wpt / 8) * kWideSlots * pl.mb * 4 * 1024; }

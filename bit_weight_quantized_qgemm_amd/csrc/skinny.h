@@ -59,6 +59,33 @@ struct TileInfo {
   int n8;      // scale chunks staged per column block
 };
 
+// The tile (column tile, row tile, k-split) of this workgroup. With several row
+// tiles (mt > 1) the row tiles of one column tile and k-split get block indices
+// 8 apart: the hardware hands workgroups to the 8 XCDs in turn, so they run on
+// one XCD, and its L2 serves the repeated reads of the same weights (only speed
+// depends on that order, not results). The (column tile, k-split) pairs past
+// the last whole group of 8 keep the plain order, so the grid is exactly
+// nt x mt x splits and no XCD gets more workgroups than in plain order.
+struct TileIndex {
+  int nt, mt, split;
+};
+__device__ __forceinline__ TileIndex tile_of_block(const GemmArgs& p) {
+  const int b = blockIdx.x;
+  const int pairs = p.nt * p.splits;
+  const int whole = pairs & ~7;
+  int g, r;
+  if (b < whole * p.mt) {
+    const int q = b >> 3;
+    g = (q / p.mt) * 8 + (b & 7);
+    r = q % p.mt;
+  } else {
+    const int j = b - whole * p.mt, rest = pairs - whole;
+    g = whole + j % rest;
+    r = j / rest;
+  }
+  return TileIndex{g % p.nt, r, g / p.nt};
+}
+
 // Returns true in every thread of the workgroup that arrived last.
 __device__ __forceinline__ bool workgroup_arrive_last(uint32_t* counter, uint32_t total, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores are complete
@@ -175,10 +202,8 @@ __device__ __forceinline__ void skinny_body(const GemmArgs& p, char* lds, int* f
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kp = wave >> 2, nw = wave & 3;
   const int c = lane & 15, h = lane >> 4;
-  const int nt = blockIdx.x % p.nt;
-  const int rest = blockIdx.x / p.nt;
-  const int mt = rest % p.mt;
-  const int split = rest / p.mt;
+  const TileIndex tix = tile_of_block(p);
+  const int nt = tix.nt, mt = tix.mt, split = tix.split;
 
   TileInfo ti;
   ti.b0 = nt * NB;

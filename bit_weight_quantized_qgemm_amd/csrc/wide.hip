@@ -72,10 +72,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   const int wave = wave_all % kWideWaves;            // wave within its K-part
   const int wc = wave % NWC, wr = wave / NWC;
   const int c32 = lane & 31, hh = lane >> 5;
-  const int nt = blockIdx.x % p.nt;
-  const int rest = blockIdx.x / p.nt;
-  const int mt = rest % p.mt;
-  const int split = rest / p.mt;
+  const TileIndex tix = tile_of_block(p);
+  const int nt = tix.nt, mt = tix.mt, split = tix.split;
   const int G0s = split * p.gps;
   const int ngw = min(p.G, G0s + p.gps) - G0s;
   // this K-part's groups [G0, G0 + ng); every K-part runs `iters` iterations

@@ -151,12 +151,41 @@ def test_repack_validation_without_gpu(L):
     assert L.qgemm_repack(1, K, N, codes, sc, None, None, _fake(0x10000000 + 4096), nb, None) == ERR_ALIAS
 
 
+def _launch_workgroups(nt, mt, splits):
+    return nt * mt * splits
+
+
+def _blocks_cover_tiles_once(p):
+    # the kernels' block -> (column tile, row tile, k-split) decoding, re-derived:
+    # row tiles of one column tile and k-split sit 8 block indices apart, except
+    # for the pairs past the last whole group of 8
+    nt, mt, s = p["nt"], p["mt"], p["splits"]
+    pairs = nt * s
+    whole = pairs - pairs % 8
+    seen = {}
+    for b in range(p["workgroups"]):
+        if b < whole * mt:
+            q = b // 8
+            g, r = (q // mt) * 8 + b % 8, q % mt
+        else:
+            j = b - whole * mt
+            g, r = whole + j % (pairs - whole), j // (pairs - whole)
+        t = (g % nt, r, g // nt)
+        assert t not in seen
+        seen[t] = b
+    assert len(seen) == nt * mt * s
+    for (n, r, sp), b in seen.items():
+        if (sp * nt + n) < whole:
+            assert all(seen[(n, r2, sp)] % 8 == b % 8 for r2 in range(mt))
+
+
 def _check_plan(p, M, K, N, ws=None, exact_ws=True):
     G = K // 128
     if p["kernel"] == 2:
         assert p["mb"] == 4 and p["nb"] == 4 and p["wpt"] in (8, 16)
         assert p["nt"] * 256 == N and p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
-        assert p["workgroups"] == p["nt"] * p["mt"] * p["splits"]
+        assert p["workgroups"] == _launch_workgroups(p["nt"], p["mt"], p["splits"])
+        _blocks_cover_tiles_once(p)
         cover = np.zeros(G, dtype=int)
         for s in range(p["splits"]):
             G0, G1 = s * p["gps"], min(G, (s + 1) * p["gps"])
@@ -168,8 +197,9 @@ def _check_plan(p, M, K, N, ws=None, exact_ws=True):
     assert p["nt"] * p["nb"] * 64 == N
     assert p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
     assert p["wpt"] in (4, 8, 16) and p["wpt"] // 4 <= p["gps"]
-    assert p["workgroups"] == p["nt"] * p["mt"] * p["splits"]
+    assert p["workgroups"] == _launch_workgroups(p["nt"], p["mt"], p["splits"])
     assert p["waves"] == p["workgroups"] * p["wpt"]
+    _blocks_cover_tiles_once(p)
     # every group of K is streamed by exactly one K-part of each tile
     kp = p["wpt"] // 4
     cover = np.zeros(G, dtype=int)
@@ -437,7 +467,7 @@ def test_every_automatic_plan_fits_lds_and_covers_the_layer(fmt, kw, K, N):
         G = K // 128
         assert p["splits"] * p["gps"] >= G and (p["splits"] - 1) * p["gps"] < G, (M, p)
         tiles = p["mt"] * p["nt"]
-        assert p["workgroups"] == tiles * p["splits"]
+        assert p["workgroups"] == _launch_workgroups(p["nt"], p["mt"], p["splits"])
         if p["splits"] > 1:
             assert p["ws_bytes"] >= max(65536, 4 * tiles), (M, p)
 
