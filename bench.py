@@ -120,6 +120,8 @@ def parse():
                     help="time only the other configured workloads (for kernel traces of them)")
     ap.add_argument("--secondary-filter", default="",
                     help="comma-separated substrings: keep only secondary workloads whose name contains one")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the dense fp16 torch.matmul context line and the achievable-peak probes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (the known-size "
                          "reference for HBM byte counters)")
@@ -391,6 +393,62 @@ def secondary(torch, qg, dev, rotate_mb, name_filter=""):
     return rows
 
 
+def dense_fp16_context(torch, dev, per_m):
+    """The same GEMMs with dense fp16 weights through torch.matmul (the vendor
+    BLAS), for the MARLIN abstract's comparison of the 4-bit kernel with the
+    uncompressed layer; weights rotate over two copies (more than the 256 MB
+    Infinity Cache). Context only: it is run and timed, not inspected."""
+    stream = torch.cuda.current_stream()
+    rows = []
+    for (K, N) in SHAPES:
+        W = [torch.randn(K, N, device=dev, dtype=torch.float16) for _ in range(2)]
+        A_all = torch.randn(128, K, device=dev, dtype=torch.float16)
+        for M in MS:
+            A = A_all[:M].contiguous()
+            for i in range(4):
+                torch.matmul(A, W[i % 2])
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            L = 20
+            a.record(stream)
+            for i in range(L):
+                torch.matmul(A, W[i % 2])
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / L
+            q = next((r["us"] for r in per_m if r["shape"] == f"{K}x{N}" and r["M"] == M), None)
+            rows.append({"shape": f"{K}x{N}", "M": M, "fp16_dense_us": round(us, 2),
+                         "w4a16_us": q, "w4a16_speedup": None if q is None else round(us / q, 2)})
+        del W, A_all
+        torch.cuda.empty_cache()
+    return rows
+
+
+def peak_probes(torch, dev):
+    """Achievable peaks on this GPU: the hand-written probes of
+    libqgemm_probes.so (a streaming read of 2 GiB, more than the Infinity
+    Cache, with its checksum verified; back-to-back matrix-core instructions of
+    each kind the kernels use) and a large dense fp16 GEMM through the vendor
+    BLAS (torch.matmul, 8192^3)."""
+    from bit_weight_quantized_qgemm_amd import probes
+
+    out = probes.measure(torch, dev)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p = torch.randn(8192, 8192, device=dev, dtype=torch.float16)
+    q = torch.randn(8192, 8192, device=dev, dtype=torch.float16)
+    for _ in range(3):
+        torch.matmul(p, q)
+    a.record(stream)
+    for _ in range(10):
+        torch.matmul(p, q)
+    b.record(stream)
+    torch.cuda.synchronize()
+    out["fp16_gemm_torch_matmul_tflops"] = round(2 * 8192**3 * 10 / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+    del p, q
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe(torch, dev, mib):
     """One plain device copy of `mib` MiB: the known-size reference for HBM
     byte counters (FETCH_SIZE, WRITE_SIZE) in profiled runs."""
@@ -554,6 +612,17 @@ def main():
                  "source_sha": source_sha()})
 
     sec = None if args.no_secondary else secondary(torch, qg, dev, 512, args.secondary_filter)
+    context = None
+    if not args.no_context:
+        context = {"dense_fp16_torch_matmul": dense_fp16_context(torch, dev, per_m),
+                   "achievable_peaks": peak_probes(torch, dev)}
+        # the dominant kernel against what the probes sustain on this GPU (context;
+        # `peak` above stays the published figure)
+        pk = context["achievable_peaks"]
+        ach_peak = pk["stream_read_gbs"] if roof["bound"] == "hbm" else \
+            pk["mfma_v_mfma_f32_32x32x16_f16_2_waves_per_simd_tops"]
+        roof["achievable_peak"] = ach_peak
+        roof["frac_of_achievable"] = round(roof["achieved"] / ach_peak, 4)
 
     out = {
         "metric": METRIC,
@@ -577,6 +646,7 @@ def main():
         "per_m": per_m,
         "cpu_baseline": cpu,
         "secondary": sec,
+        "context": context,
     }
     print(json.dumps(out), flush=True)
 

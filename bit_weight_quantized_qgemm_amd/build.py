@@ -1,8 +1,9 @@
-"""Builds the gfx950 HIP library ``libqgemm.so`` in-tree with hipcc.
+"""Builds the gfx950 HIP library ``libqgemm.so`` in-tree with hipcc, and the
+measurement probes ``libqgemm_probes.so`` beside it.
 
 Usage: ``python -m bit_weight_quantized_qgemm_amd.build`` (or ``build()``).
 Every source is compiled on each call; objects go to ``_build/`` next to this
-file and the shared library to ``libqgemm.so`` beside it.
+file and the shared libraries beside it.
 """
 
 from __future__ import annotations
@@ -18,6 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqgemm.so")
+PROBES_LIB = os.path.join(HERE, "libqgemm_probes.so")
+PROBES_SOURCES = ["probes.hip"]
 SOURCES = ["api.cpp", "repack.hip", "w4a16.hip", "w4a8.hip", "w2w4.hip", "wide.hip", "quant.hip", "w4g.hip", "sp24.hip",
            "bitplane_lo.hip", "bitplane_hi.hip", "noalloc.hip"]
 ARCH = "gfx950"
@@ -47,18 +50,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBES_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBES_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBES_LIB}")
     return LIB
 
 
