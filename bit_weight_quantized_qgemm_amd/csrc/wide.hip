@@ -7,8 +7,8 @@
 // other's matrix operations) form a grid of NWC column waves x 8/NWC row waves,
 // each owning 256/NWC columns and 16*MBW*NWC/8 rows. Each weight is dequantized
 // by the 8/NWC row waves of its columns and reused by all of their rows. The products
-// run on v_mfma_f32_32x32x16_f16, which on gfx950 sustains nearly twice the
-// throughput of the 16x16x32 form for the same operand bytes:
+// run on v_mfma_f32_32x32x16_f16, which does twice the work of the 16x16x32 form
+// for the same operand bytes and sustains a higher rate on gfx950:
 //   * operands of one 32x32x16 step: lane l holds row (A) or column (B) l % 32
 //     and k = 8*(l/32) .. +7 of the 16-k step; the result's element i of lane l
 //     is row 8*(i/4) + 4*(l/32) + i%4, column l % 32;
