@@ -57,19 +57,19 @@ struct PolicyBP : Tile16 {
   template <int n>
   __device__ __forceinline__ static void load_words(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
     if constexpr (n == 1) {
-      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+      w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamPolicy);
     } else if constexpr (n == 2) {
-      const u32x2 v = load8(r, voff, soff);
+      const u32x2 v = load8_stream(r, voff, soff);
       w[0] = v[0];
       w[1] = v[1];
     } else if constexpr (n == 3) {
       typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-      const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
+      const u32x3 v = __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, kStreamPolicy));
       w[0] = v[0];
       w[1] = v[1];
       w[2] = v[2];
     } else {
-      const u32x4 v = load16(r, voff, soff);
+      const u32x4 v = load16_stream(r, voff, soff);
       w[0] = v[0];
       w[1] = v[1];
       w[2] = v[2];

@@ -88,7 +88,7 @@ struct PolicySP24 {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
         st.rec[j] = __builtin_bit_cast(
-            u32x3, __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12u + oob, j * 768u + rel * gstep, 0));
+            u32x3, __builtin_amdgcn_raw_buffer_load_b96(rc, lane * 12u + oob, j * 768u + rel * gstep, kStreamPolicy));
     }
     __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t) const {
       const int g = gw0 + rel;

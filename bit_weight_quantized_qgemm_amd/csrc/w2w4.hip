@@ -95,7 +95,7 @@ struct PolicyW2W4 : Tile16 {
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.base[j] = load8(rb, bvoff + oob, j * 512u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.base[j] = load8_stream(rb, bvoff + oob, j * 512u + rel * gstep);
     }
     __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t oob) const {
       const int g = gw0 + rel;
@@ -104,7 +104,7 @@ struct PolicyW2W4 : Tile16 {
         const u32x2 d = desc[(g - G0) * (4 * NBW) + j];
         const uint32_t is4 = (d[1] >> c) & 1u;
         const uint32_t off = (is4 && !oob) ? (d[0] + __builtin_popcount(d[1] & below)) * 32u + hoff : 0x7FFFFFF8u;
-        st.high[j] = load8(rh, off, 0);
+        st.high[j] = load8_stream(rh, off, 0);
         st.is4[j] = is4;
       }
       const int off = ((g >> 3) - c8) * kScaleChunk + (g & 7) * 2;

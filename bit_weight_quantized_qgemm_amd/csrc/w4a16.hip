@@ -64,7 +64,7 @@ struct PolicyW4A16 : Tile16 {
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff + oob, j * 1024u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16_stream(rc, cvoff + oob, j * 1024u + rel * gstep);
     }
     __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t) const {
       const int g = gw0 + rel;
@@ -183,8 +183,8 @@ struct PolicyW4A16M32 {
       svoff = (uint32_t)((c32 >> 4) * sblk + (c32 & 15) * 16);
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
-      st.even = load16(rc, cvoff + oob, rel * gstep);
-      st.odd = load16(rc, cvoff + 512u + oob, rel * gstep);
+      st.even = load16_stream(rc, cvoff + oob, rel * gstep);
+      st.odd = load16_stream(rc, cvoff + 512u + oob, rel * gstep);
       const int g = gw0 + rel;
       st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff + oob, (uint32_t)(g >> 3) * 256u + (uint32_t)(g & 7) * 2u, 0);
     }

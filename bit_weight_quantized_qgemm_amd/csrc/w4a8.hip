@@ -65,7 +65,7 @@ struct PolicyW4A8 : Tile16 {
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff + oob, j * 1024u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16_stream(rc, cvoff + oob, j * 1024u + rel * gstep);
     }
     __device__ __forceinline__ void load_lds(Stage<NBW>& st, int rel, uint32_t) const {
       const int g = gw0 + rel;

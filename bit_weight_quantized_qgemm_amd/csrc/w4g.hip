@@ -127,7 +127,7 @@ struct PolicyW4G : Tile16 {
     }
     __device__ __forceinline__ void load_vmem(Stage<NBW>& st, int rel, uint32_t oob) const {
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) st.code[j] = load16(rc, cvoff + oob, j * 1024u + rel * gstep);
+      for (int j = 0; j < NBW; ++j) st.code[j] = load16_stream(rc, cvoff + oob, j * 1024u + rel * gstep);
       if constexpr (!kStaged) {
         const int g = gw0 + rel;
         // wave-uniform: one load per block either way
