@@ -11,7 +11,8 @@ the C ABI (16 launches). Inputs are seeded synthetic tensors with the workload's
 distributions (fp16 A ~ N(0,1); uint4 codes uniform with zero point 8; fp16
 group scales uniform in [0.005, 0.02], g = 128), resident in HBM before timing.
 The weight blob rotates over several copies (more bytes than the 256 MB
-Infinity Cache) so every launch streams its weights from HBM.
+Infinity Cache), one copy further at every launch of its shape, so every launch
+streams its weights from HBM.
 
 Prints one JSON line. ``value`` is the aggregate TFLOP/s of the timed steps;
 ``per_m`` gives each launch's mean duration over a burst of back-to-back
@@ -508,8 +509,17 @@ def main():
                               plan=qg.plan(qg.FMT_W4A16, M, K, N)))
     torch.cuda.synchronize()
 
-    def launch(cs, i):
-        b = cs["blobs"][i % len(cs["blobs"])]
+    # Every launch reads another copy of its layer's blob than the launch before
+    # it: the k-th launch of a shape takes copy k mod copies, so a copy is read
+    # again only after the other copies (more than the 256 MB Infinity Cache in
+    # between) and the weights stream from HBM in the timed steps as in bursts.
+    shape_launches = {}
+
+    def launch(cs, i=None):
+        key = (cs["K"], cs["N"])
+        k = shape_launches.get(key, 0)
+        shape_launches[key] = k + 1
+        b = cs["blobs"][k % len(cs["blobs"])]
         st = L.qgemm_w4a16(ctypes.c_void_p(cs["A"].data_ptr()), cs["K"], ctypes.c_void_p(b.data_ptr()),
                            ctypes.c_void_p(cs["C"].data_ptr()), cs["N"], cs["M"], cs["K"], cs["N"],
                            ctypes.c_void_p(cs["ws"].data_ptr()), cs["ws"].numel(), sptr)

@@ -195,6 +195,33 @@ def test_w4a16_forced_splits(force, M):
     _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, (force, M))
 
 
+@pytest.mark.parametrize("M,N,force", [(100, 704, (1, 8, 3)), (100, 1408, (2, 8, 3)), (64, 704, (1, 4, 5)),
+                                     (129, 1408, (2, 16, 1)), (50, 704, (1, 8, 0))])
+def test_row_tiles_block_order(M, N, force):
+    """Several row tiles: their block indices follow the XCD-grouped order, with
+    (column tile, split) pairs in whole groups of 8 and a ragged rest."""
+    K = 2048
+    qg.set_plan_override(*force)
+    pl = qg.plan(qg.FMT_W4A16, M, K, N)
+    pairs = pl["nt"] * pl["splits"]
+    _say("row-tile order", M, N, force, pl)
+    assert pl["mt"] > 1 and pairs >= 8
+    p = gen.w4a16_problem(M, K, N, seed=M + N)
+    A = _t(p["A"])
+    blob = upload_w4a16(p)
+    C1 = qg.w4a16(A, blob, K, N)
+    C2 = qg.w4a16(A, blob, K, N)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    _ok(C1.cpu().numpy(), ref.gemm_w4a16(p["A"], p["codes"], p["scales"]), K, ("row tiles", M, N, force))
+    # W4A8 under the same forced decomposition: exact accumulators
+    q = gen.w4a8_problem(M, K, N, seed=M + N + 1)
+    C, acc = _w4a8_run(q)
+    acc_ref, C_ref = ref.gemm_w4a8(q["A"], q["codes"], q["group_scales"], q["a_scale"], q["chan_scales"])
+    assert np.array_equal(acc.astype(np.int64), acc_ref)
+    _ok(C, C_ref, K, ("row tiles w4a8", M, N, force))
+
+
 def test_w4a16_strided_and_guard_bands():
     _say("w4a16 strides + guards")
     M, K, N = 9, 1024, 256
