@@ -327,6 +327,22 @@ def test_w2w4_config_layer(M):
     _ok(C, ref.gemm_w2w4(p["A"], p["codes"], p["bitmap"], p["scales"]), K, ("w2w4", M))
 
 
+@pytest.mark.parametrize("K,N", [(8192, 28672), (28672, 8192)])
+def test_w2w4_70b_layer_sampled(K, N):
+    """The mixed format on the 70B-class layer in its automatic plans (16-wave
+    two-block tiles on the up projection at M <= 32), one column per 16-column
+    block."""
+    p = gen.w2w4_problem(64, K, N, seed=3)
+    blob = upload_w2w4(p)
+    cols = block_cols(N, seed=K + 1)
+    Cref = ref.gemm_w2w4(p["A"], p["codes"], p["bitmap"], p["scales"], cols=cols)
+    for M in (1, 16, 32, 64):
+        _say("w2w4 70B layer", M, K, N, qg.plan(qg.FMT_W2W4, M, K, N))
+        C = qg.w2w4_mixed(_t(p["A"][:M]), blob, K, N).cpu().numpy()
+        assert np.all(np.isfinite(C))
+        _ok(C[:, cols], Cref[:M], K, ("w2w4 70B", M, K, N))
+
+
 @pytest.mark.parametrize("M,frac,force", [(3, 0.0, None), (17, 1.0, None), (20, 0.3, (1, 8, 2)),
                                           (9, 0.5, (2, 4, 4)), (33, 0.1, (2, 16, 1)),
                                           (5, 0.2, (1, 4, 16))])
