@@ -321,17 +321,21 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   // 16-wave two-block tiles without k-splits keep 7.7 MB in flight on the 70B
   // up projection and measured 18-25 % faster at M = 1-32 than the three-split
   // plans an 8 MB target chose; with several row tiles 8 MB stayed 2-4 %
-  // faster); the other formats keep the 8 MB of their sweep
+  // faster); W4A8 16-row tiles on blobs of 64 MB also 7 MB (8-wave two-block
+  // tiles on the 70B up projection: 20.8 against 21.9-22.6 us at M = 1-16); the
+  // other formats keep the 8 MB of their sweep
   const bool mixed = fmt == QGEMM_FMT_W2W4;
-  const double inflight_target =
-      std::min((fmt == QGEMM_FMT_W4A16 || (mixed && pl.mt == 1) ? 7.0 : 8.0) * 1048576.0, blob / 2);
+  const bool big64 = blob >= 64.0 * 1048576.0;
+  const bool target7 = fmt == QGEMM_FMT_W4A16 || (mixed && pl.mt == 1) ||
+                       (fmt == QGEMM_FMT_W4A8 && pl.mb == 1 && big64);
+  const double inflight_target = std::min((target7 ? 7.0 : 8.0) * 1048576.0, blob / 2);
   // the bit-plane kernel is bound by its plane unpacking: one-block tiles (twice
   // the waves) measured faster on every layer and batch
   // (W4A16 also at M <= 4 once the blob reaches 64 MB: 21.7 vs 22.5 us on the 70B
   // up projection at M = 1-4)
   // (mixed 2/4-bit on blobs of 64 MB: 24.1 against 34.4 us for one-block tiles
-  // on the 70B up projection at M = 1)
-  const bool w4a16_big = (fmt == QGEMM_FMT_W4A16 || mixed) && blob >= 64.0 * 1048576.0;
+  // on the 70B up projection at M = 1; W4A8 20.8 against 22.6 us)
+  const bool w4a16_big = (fmt == QGEMM_FMT_W4A16 || mixed || fmt == QGEMM_FMT_W4A8) && big64;
   const int pref_nb = (fmt != QGEMM_FMT_BITPLANE && (M > 4 || w4a16_big) && blob >= big_blob) ? 2 : 1;
   struct Score {
     int violations, kp_pen, nb_pen, cost, splits;

@@ -267,6 +267,25 @@ def _w4a8_run(p, M=None, acc=True):
     return C.cpu().numpy(), (acc_out.cpu().numpy() if acc else None)
 
 
+def test_w4a8_70b_up_projection_sampled():
+    """W4A8 on the 70B-class up projection (K = 8192, the largest K of the
+    format's exact-accumulator range that the 70B layers use) in its automatic
+    plans: exact int32 accumulators on one column per 16-column block."""
+    K, N = 8192, 28672
+    p = gen.w4a8_problem(64, K, N, seed=4)
+    blob = upload_w4a8(p)
+    cols = block_cols(N, seed=K + 2)
+    acc_ref, C_ref = ref.gemm_w4a8(p["A"], p["codes"], p["group_scales"], p["a_scale"], p["chan_scales"],
+                                   cols=cols)
+    for M in (1, 16, 32, 64):
+        _say("w4a8 70B up", M, qg.plan(qg.FMT_W4A8, M, K, N))
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=DEV)
+        C = qg.w4a8(_t(p["A"][:M]), _t(p["a_scale"][:M]), blob, K, N, acc_out=acc_out).cpu().numpy()
+        acc = acc_out.cpu().numpy()
+        assert np.array_equal(acc[:, cols].astype(np.int64), acc_ref[:M])
+        _ok(C[:, cols], C_ref[:M], K, ("w4a8 70B", M))
+
+
 @pytest.mark.parametrize("M", [16, 64, 128])
 def test_w4a8_config_layer(M):
     K, N = 4096, 11008
