@@ -89,6 +89,18 @@ def measure(torch, dev, read_gib: float = 2.0, reps: int = 10) -> dict:
         raise RuntimeError(f"stream-read probe checksum {got} != {expect}")
     out["stream_read_gbs_by_order_and_workgroups"] = reads
     out["stream_read_gbs"] = max(reads.values())
+    # the floor of a short streaming launch: 1 MiB read by 256 workgroups,
+    # back-to-back launches on one stream (time per launch)
+    small = x[: 2**18]
+    for _ in range(3):
+        stream_read(torch, small, 256, sink, True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(50):
+        stream_read(torch, small, 256, sink, True)
+    b.record(stream)
+    torch.cuda.synchronize()
+    out["stream_read_1mib_us_per_launch"] = round(a.elapsed_time(b) * 1e3 / 50, 2)
     del x
     # 2048 workgroups of 4 waves: 8 waves per SIMD; 512: 2 waves per SIMD
     iters = 2048
