@@ -234,6 +234,7 @@ SECONDARY = (
     + [(f"bit-plane w{b}a8", 8, 4096, 11008, M) for b in (1, 2, 3, 4, 8) for M in (1, 16)]
     + [(name, 6, 4096, 11008, M) for name in ("w4g g64 fp16", "w4g g128 zeros fp16", "w4g per-channel fp16",
                                               "w4g g128 bf16", "w4g g128 zeros bf16") for M in (1, 16)]
+    + [("w4g g128 zeros fp16", 6, K, N, M) for (K, N) in [(8192, 28672), (28672, 8192)] for M in (16, 64, 128)]
 )
 # general-grid variants: name -> (group size (0 = K), stored zero points, activation type)
 W4G_VARIANTS = {"w4g g64 fp16": (64, False, "fp16"), "w4g g128 zeros fp16": (128, True, "fp16"),

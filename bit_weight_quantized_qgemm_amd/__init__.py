@@ -90,8 +90,9 @@ def lib() -> ctypes.CDLL:
         L.qgemm_bitplane_repack.argtypes = [i64, i64, i32, vp, vp, vp, ctypes.c_size_t, vp]
         L.qgemm_bitplane_a8.argtypes = [vp, i64, vp, vp, vp, i64, vp, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
         L.qgemm_bitplane_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(ctypes.c_int64)]
-        L.qgemm_w4g_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_int64)]
-        L.qgemm_plan_info.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.qgemm_w4g_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+        L.qgemm_plan_info.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, i32,
+                                      ctypes.POINTER(ctypes.c_int64)]
         L.qgemm_w4a16_noalloc.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp]
         for name in ("qgemm_packed_bytes", "qgemm_workspace_bytes", "qgemm_repack", "qgemm_w4a16",
                      "qgemm_w4a8", "qgemm_w2w4_mixed", "qgemm_plan", "qgemm_set_plan_override",
@@ -143,25 +144,27 @@ def workspace_bytes(fmt: int, M: int, K: int, N: int) -> int:
 _PLAN_KEYS = ("kernel", "mb", "nb", "wpt", "splits", "gps", "mt", "nt", "workgroups", "waves")
 
 
-def plan(fmt: int, M: int, K: int, N: int, bits: int = 4, group_size: int = 128, zeros: bool = True) -> dict:
+def plan(fmt: int, M: int, K: int, N: int, bits: int = 4, group_size: int = 128, zeros: bool = True,
+         act_dtype: int = 1) -> dict:
     """Work decomposition of a call of this shape (bits: bit-plane width, used
-    only for FMT_BITPLANE; group_size / zeros: the grid, used only for FMT_W4G)."""
+    only for FMT_BITPLANE; group_size / zeros / act_dtype (DT_F16 or DT_BF16):
+    the grid and activation type, used only for FMT_W4G)."""
     arr = (ctypes.c_int64 * 10)()
     if fmt == FMT_BITPLANE:
         _check(lib().qgemm_bitplane_plan(M, K, N, bits, arr), "qgemm_bitplane_plan")
     elif fmt == FMT_W4G:
-        _check(lib().qgemm_w4g_plan(M, K, N, group_size, int(zeros), arr), "qgemm_w4g_plan")
+        _check(lib().qgemm_w4g_plan(M, K, N, group_size, int(zeros), act_dtype, arr), "qgemm_w4g_plan")
     else:
         _check(lib().qgemm_plan(fmt, M, K, N, arr), "qgemm_plan")
     return dict(zip(_PLAN_KEYS, list(arr)))
 
 
 def plan_info(fmt: int, M: int, K: int, N: int, bits: int = 4, group_size: int = 128,
-              zeros: bool = True) -> dict:
+              zeros: bool = True, act_dtype: int = 1) -> dict:
     """The plan of ``plan()`` plus the call's workspace bytes and the dynamic LDS
     bytes per workgroup its launch requests."""
     arr = (ctypes.c_int64 * 12)()
-    _check(lib().qgemm_plan_info(fmt, M, K, N, bits, group_size, int(zeros), arr), "qgemm_plan_info")
+    _check(lib().qgemm_plan_info(fmt, M, K, N, bits, group_size, int(zeros), act_dtype, arr), "qgemm_plan_info")
     return dict(zip(_PLAN_KEYS + ("ws_bytes", "lds_bytes"), list(arr)))
 
 

@@ -272,10 +272,11 @@ int device_cu_count() {
   return cus;
 }
 
-Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool zeros) {
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool zeros, bool act_bf16) {
   const int force_kernel = g_force_kernel.load();
   const int cus = device_cu_count();
-  const bool wide_ok = fmt == QGEMM_FMT_W4A16 && N % kWideCols == 0;
+  // the wide kernel: W4A16, and the general grid with fp16 activations
+  const bool wide_ok = (fmt == QGEMM_FMT_W4A16 || (fmt == QGEMM_FMT_W4G && !act_bf16)) && N % kWideCols == 0;
   if (wide_ok && (force_kernel == 2 || (force_kernel == 0 && M >= kWideMinM))) {
     // The wide tile (256 columns, all rows of the batch) needs many k-splits on
     // narrow layers, and their partial sums then cost more than re-streaming
@@ -564,17 +565,19 @@ int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* 
 }
 
 int qgemm_plan_info(int fmt, int64_t M, int64_t K, int64_t N, int32_t bits, int32_t group_size,
-                    int32_t has_zeros, int64_t* out12) {
+                    int32_t has_zeros, int32_t act_dtype, int64_t* out12) {
   if (!valid_fmt(fmt) && fmt != QGEMM_FMT_W4G && fmt != QGEMM_FMT_BITPLANE) return QGEMM_ERR_FORMAT;
   if (!out12) return QGEMM_ERR_NULL;
   int st = check_kn(fmt, K, N);
   if (st) return st;
   if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
   if (fmt == QGEMM_FMT_BITPLANE && (bits < 1 || bits > 8)) return QGEMM_ERR_RANGE;
-  if (fmt == QGEMM_FMT_W4G && (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1)))
+  if (fmt == QGEMM_FMT_W4G && (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1) ||
+                               (act_dtype != QGEMM_DT_F16 && act_dtype != QGEMM_DT_BF16)))
     return QGEMM_ERR_RANGE;
   const qg::Plan pl = qg::make_plan(fmt, M, K, N, fmt == QGEMM_FMT_BITPLANE ? bits : 4,
-                                    fmt == QGEMM_FMT_W4G ? group_size : qg::kGroup, has_zeros != 0);
+                                    fmt == QGEMM_FMT_W4G ? group_size : qg::kGroup, has_zeros != 0,
+                                    fmt == QGEMM_FMT_W4G && act_dtype == QGEMM_DT_BF16);
   if (pl.kernel == 0) return no_plan();
   const int64_t v[12] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps, pl.mt, pl.nt,
                          pl.workgroups, pl.waves, (int64_t)pl.ws_bytes, (int64_t)pl.lds_bytes};
@@ -709,7 +712,7 @@ int run_gemm(const GemmCall& g) {
   if (g.ldc < g.N || g.ldc % 8 != 0) return QGEMM_ERR_ALIGN;
   if (g.a_scale && !aligned(g.a_scale, 2)) return QGEMM_ERR_ALIGN;
   if (g.acc_out && !aligned(g.acc_out, 4)) return QGEMM_ERR_ALIGN;
-  const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N, g.bits, g.gs, g.zeros);
+  const qg::Plan pl = qg::make_plan(g.fmt, g.M, g.K, g.N, g.bits, g.gs, g.zeros, g.bf16);
   if (pl.kernel == 0) return no_plan();
   if (pl.ws_bytes > 0 && !g.dry) {
     if (!g.ws) return QGEMM_ERR_NULL;
@@ -772,7 +775,8 @@ int run_gemm(const GemmCall& g) {
   }
   if (g.fmt == QGEMM_FMT_W4A16) e = pl.kernel == 2 ? qg::launch_w4a16_wide(pl, a, s) : qg::launch_w4a16(pl, a, s);
   else if (g.fmt == QGEMM_FMT_W4A8) e = qg::launch_w4a8(pl, a, s);
-  else if (g.fmt == QGEMM_FMT_W4G) e = qg::launch_w4g(pl, a, g.bf16, g.zeros, s);
+  else if (g.fmt == QGEMM_FMT_W4G)
+    e = pl.kernel == 2 ? qg::launch_w4g_wide(pl, a, g.zeros, s) : qg::launch_w4g(pl, a, g.bf16, g.zeros, s);
   else if (g.fmt == QGEMM_FMT_W4A16_SP24) e = qg::launch_sp24(pl, a, s);
   else if (g.fmt == QGEMM_FMT_BITPLANE)
     e = g.bits <= 4 ? qg::launch_bitplane_lo(pl, a, g.bits, s) : qg::launch_bitplane_hi(pl, a, g.bits, s);
@@ -841,22 +845,28 @@ int qgemm_w4g_workspace_bytes(int64_t M, int64_t K, int64_t N, size_t* bytes) {
   int st = check_kn(QGEMM_FMT_W4G, K, N);
   if (st) return st;
   if (M < 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
-  // the plan depends on the grid; size for every grid (a grid with no plan
-  // that fits is refused by the GEMM call itself)
+  // the plan depends on the grid and the activation type; size for every
+  // grid and type (a grid with no plan that fits is refused by the GEMM call)
   size_t ws = 0;
   for (int gs : {64, 128})
-    for (bool z : {false, true}) ws = std::max(ws, M == 0 ? 0 : qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, gs, z).ws_bytes);
+    for (bool z : {false, true})
+      for (bool bf : {false, true})
+        ws = std::max(ws, M == 0 ? 0 : qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, gs, z, bf).ws_bytes);
   *bytes = ws;
   return QGEMM_OK;
 }
 
-int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zeros, int64_t* out10) {
+int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zeros, int32_t act_dtype,
+                   int64_t* out10) {
   if (!out10) return QGEMM_ERR_NULL;
   int st = check_kn(QGEMM_FMT_W4G, K, N);
   if (st) return st;
-  if (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1)) return QGEMM_ERR_RANGE;
+  if (!valid_group_size(K, group_size) || (has_zeros != 0 && has_zeros != 1) ||
+      (act_dtype != QGEMM_DT_F16 && act_dtype != QGEMM_DT_BF16))
+    return QGEMM_ERR_RANGE;
   if (M <= 0 || M > kMaxM) return QGEMM_ERR_SHAPE;
-  const qg::Plan pl = qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, group_size, has_zeros != 0);
+  const qg::Plan pl =
+      qg::make_plan(QGEMM_FMT_W4G, M, K, N, 4, group_size, has_zeros != 0, act_dtype == QGEMM_DT_BF16);
   if (pl.kernel == 0) return no_plan();
   const int64_t v[10] = {pl.kernel, pl.mb, pl.nb, pl.wpt, pl.splits, pl.gps,
                          pl.mt, pl.nt, pl.workgroups, pl.waves};

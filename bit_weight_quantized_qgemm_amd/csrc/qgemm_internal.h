@@ -84,8 +84,10 @@ inline size_t wide_lds_bytes(const Plan& pl) { return (size_t)(pl.wpt / 8) * kWi
 
 // bits: planes per weight of the bit-plane format (ignored by the others)
 // gs / zeros: the general-grid format's group length and zero points (its
-// staged grid entries size the LDS); ignored by the other formats
-Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits = 4, int gs = 128, bool zeros = true);
+// staged grid entries size the LDS); act_bf16: its activation type (fp16 calls
+// may take the wide kernel); ignored by the other formats
+Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits = 4, int gs = 128, bool zeros = true,
+               bool act_bf16 = false);
 struct KernelOccupancy {
   int waves_per_simd;
   bool spills;
@@ -121,6 +123,8 @@ size_t lds_bytes_sp24(const Plan& pl, int G);
 size_t lds_bytes_bitplane(const Plan& pl, int G);
 hipError_t launch_w4a16(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s);
+// general grid, fp16 activations, on the wide kernel (kernel 2)
+hipError_t launch_w4g_wide(const Plan& pl, const GemmArgs& a, bool zeros, hipStream_t s);
 hipError_t launch_w4a8(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w2w4(const Plan& pl, const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4g(const Plan& pl, const GemmArgs& a, bool bf16, bool zeros, hipStream_t s);

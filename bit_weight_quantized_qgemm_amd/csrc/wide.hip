@@ -1,6 +1,8 @@
 // W4A16 GEMM for larger batches (M > 32) on gfx950: the compute-bound end of the
 // batch range of the MARLIN abstract, where its speedup shrinks with batch size
-// but persists up to 64-128.
+// but persists up to 64-128. The same kernel runs the general 4-bit grid with
+// fp16 activations (per group and column a scale and optionally a zero point;
+// the page on 2-bit LLMs on GPUs quantizes by groups and leaves the length open).
 //
 // Each workgroup owns a tile of 16*MBW = 64 rows x 256 columns; its eight
 // waves (two per SIMD, so one wave's dequantization and LDS reads overlap the
@@ -27,7 +29,8 @@
 //     slot written next is the one all waves finished reading before that
 //     barrier.
 // Weights stream per wave into a register ring (kDepth groups ahead) together
-// with the lane's fp16 group scales; dequantization is exact to fp16 (q - 8),
+// with the lane's fp16 group scales (or grid entries); dequantization is exact
+// to fp16 (q - 8, or q - z),
 // then one packed multiply by the scale rounds once (the scale cannot be applied
 // after the MFMA here without doubling the accumulators). Accumulation is fp32.
 // When a layer has too few tiles for the chip, K is also split across workgroups
@@ -36,6 +39,7 @@
 
 #include <mutex>
 #include <set>
+#include <utility>
 
 namespace qg {
 namespace {
@@ -46,16 +50,27 @@ constexpr int kWideWaves = 8;
 constexpr int kDepth = 3;                              // groups of loads in flight ahead
 constexpr int kASlots = kDepth + 1;                    // LDS slots and register stages
 
+// Weight formats of the wide kernel: the W4A16 blob, or the general-grid blob
+// (the same code chunks, then one 16-bit scale or 32-bit scale | zero-point
+// entry per (group, column)) with fp16 activations, as one kernel per entry
+// layout: group length a multiple of 128 (one entry per chunk-column) or 64
+// (two, adjacent), without or with zero points. A compile-time layout keeps
+// the stage loads free of branches and of register copies, either of which
+// makes the compiler wait for the load at issue (a full drain of the ring).
+enum WideFmt { kWideW4A16 = 0, kWideGrid = 1, kWideGridZ = 2, kWideGrid64 = 3, kWideGrid64Z = 4 };
+
 template <int JB>
 struct WideStage {
   u32x4 even[JB];   // words t = k-steps 2t of each 32-column block
   u32x4 odd[JB];    // words t = k-steps 2t + 1
-  uint32_t s[JB];   // fp16 group scale of the lane's column (low half)
+  u32x2 s[JB];      // W4A16 and grid groups of 128+ k: the lane's fp16 scale or
+                    // entry in [0]; group length 64: both entries of the chunk
+                    // (in [0] as two 16-bit scales, or in [0] and [1])
 };
 
 }  // namespace
 
-template <int MBW, int NWC, int KPW>
+template <int MBW, int NWC, int KPW, int WF = kWideW4A16>
 __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* flag) {
   constexpr int NWR = kWideWaves / NWC;             // row waves
   constexpr int kWideJB = kWideCols / 32 / NWC;     // 32-column blocks per wave
@@ -115,12 +130,29 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
 #pragma unroll
   for (int jb = 0; jb < kWideJB; ++jb)
     cvoff[jb] = (uint32_t)((2 * jb + (c32 >> 4)) * 1024 + (16 * hh + (c32 & 15)) * 16);
+  // W4A16 scales [NB][G8][16][8] fp16; grid entries [row][N][per] of kEntry
+  // bytes, row = the group (per = 2: the chunk's two 64-k groups, group length
+  // 64) or the group that holds the chunk (per = 1)
+  constexpr bool kGrid = WF != kWideW4A16;
+  constexpr bool kG64 = WF == kWideGrid64 || WF == kWideGrid64Z;
+  constexpr bool kZero = WF == kWideGridZ || WF == kWideGrid64Z;
+  constexpr uint32_t kEntry = kZero ? 4u : 2u;
+  constexpr uint32_t per = kG64 ? 2u : 1u;
+  // chunks per group (groups of 128+ k); the group of chunk g is
+  // (g * cmag) >> 31 with cmag = ceil(2^31 / cpg), exact while g * cpg < 2^31
+  // (g < 2^13 chunks)
+  const uint32_t cpg = (kGrid && !kG64) ? (uint32_t)p.gs / 128u : 1u;
+  const uint32_t cmag = 0x7FFFFFFFu / cpg + 1u;
   const uint32_t sblk = (uint32_t)p.G8 * 256u;
-  const rsrc_t rs = make_rsrc(static_cast<const char*>(p.scales) + (size_t)bw * p.G8 * 256,
-                              2 * kWideJB * sblk);
+  const uint32_t erow = (uint32_t)p.N * per * kEntry;   // bytes per entry row
+  const rsrc_t rs = kGrid ? make_rsrc(p.scales, (kG64 ? (uint32_t)p.G : (uint32_t)p.G / cpg) * erow)
+                          : make_rsrc(static_cast<const char*>(p.scales) + (size_t)bw * p.G8 * 256,
+                                      2 * kWideJB * sblk);
   uint32_t svoff[kWideJB];
 #pragma unroll
-  for (int jb = 0; jb < kWideJB; ++jb) svoff[jb] = (uint32_t)((2 * jb + (c32 >> 4)) * sblk + (c32 & 15) * 16);
+  for (int jb = 0; jb < kWideJB; ++jb)
+    svoff[jb] = kGrid ? (uint32_t)((bw + 2 * jb) * 16 + c32) * per * kEntry
+                      : (uint32_t)((2 * jb + (c32 >> 4)) * sblk + (c32 & 15) * 16);
   auto issue_b = [&](Stage& st, int rel) {
 #pragma unroll
     for (int jb = 0; jb < kWideJB; ++jb) {
@@ -128,9 +160,27 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
       st.odd[jb] = load16(rc, cvoff[jb] + 512u, rel * gstep);
     }
     const int g = G0 + rel;
-    const uint32_t soff = (uint32_t)(g >> 3) * 256u + (uint32_t)(g & 7) * 2u;
+    if constexpr (!kGrid) {
+      const uint32_t soff = (uint32_t)(g >> 3) * 256u + (uint32_t)(g & 7) * 2u;
 #pragma unroll
-    for (int jb = 0; jb < kWideJB; ++jb) st.s[jb] = __builtin_amdgcn_raw_buffer_load_b16(rs, svoff[jb], soff, 0);
+      for (int jb = 0; jb < kWideJB; ++jb)
+        st.s[jb] = u32x2{__builtin_amdgcn_raw_buffer_load_b16(rs, svoff[jb], soff, 0), 0u};
+    } else {
+      // one load per block in every layout, so the counted waits see the
+      // same number of loads; loaded words are used as they are (unpacked at
+      // the dequantization)
+      const uint32_t row = kG64 ? (uint32_t)g : (uint32_t)(((uint64_t)(uint32_t)g * cmag) >> 31);
+      const uint32_t soff = row * erow;
+#pragma unroll
+      for (int jb = 0; jb < kWideJB; ++jb) {
+        if constexpr (WF == kWideGrid64Z)
+          st.s[jb] = load8(rs, svoff[jb], soff);
+        else if constexpr (WF == kWideGrid)
+          st.s[jb] = u32x2{__builtin_amdgcn_raw_buffer_load_b16(rs, svoff[jb], soff, 0), 0u};
+        else
+          st.s[jb] = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs, svoff[jb], soff, 0), 0u};
+      }
+    }
   };
   constexpr int kBPerGroup = 3 * kWideJB;           // vector memory operations of issue_b
 
@@ -165,14 +215,26 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   constexpr int kAfter = kBPerGroup + (kDepth - 1) * (kAPerWave + kBPerGroup);
   static_assert(kAfter < 64, "vmcnt range");
 
-  // B operand of k-step u for both 32-column blocks, scaled
+  // B operand of k-step u for both 32-column blocks, scaled. The grid formats
+  // take the zero point and scale of the k-step's 64-k half (k-steps 0-3 and
+  // 4-7) from the lane's entry: -(1024 + z) and -(64 + z) are exact fp16
+  // patterns (the ulp is 1 at 1024 and 1/16 at 64).
   auto dequant_step = [&](const Stage& cur, int u, f16x8 (&bf)[kWideJB]) {
 #pragma unroll
     for (int jb = 0; jb < kWideJB; ++jb) {
       const uint32_t w = (u & 1) ? cur.odd[jb][u >> 1] : cur.even[jb][u >> 1];
-      const f16 sh = as_h2(cur.s[jb])[0];
+      // the k-step's entry: steps 0-3 and 4-7 are the chunk's two 64-k halves
+      const uint32_t e = WF == kWideGrid64 ? ((u >> 2) ? cur.s[jb][0] >> 16 : cur.s[jb][0])
+                                           : cur.s[jb][WF == kWideGrid64Z ? (u >> 2) : 0];
+      const f16 sh = as_h2(e & 0xFFFFu)[0];
       const f16x8 sc8 = {sh, sh, sh, sh, sh, sh, sh, sh};
-      bf[jb] = dequant_u4x8(w, lo_off, hi_off, magic) * sc8;
+      if constexpr (kZero) {
+        const uint32_t z = (e >> 16) & 0xFu;
+        const uint32_t zz = z | (z << 16);
+        bf[jb] = dequant_u4x8(w, as_h2(zz | 0xE400E400u), as_h2((zz << 4) | 0xD400D400u), magic) * sc8;
+      } else {
+        bf[jb] = dequant_u4x8(w, lo_off, hi_off, magic) * sc8;
+      }
     }
   };
   auto read_a = [&](const char* slot, int u, f16x8 (&a)[R32]) {
@@ -359,6 +421,20 @@ __global__ void __launch_bounds__(1024) w4a16_wide_m64_kp2(GemmArgs p) {
   wide_body<4, 8, 2>(p, lds, &flag);
 }
 
+// the general grid with fp16 activations (WF: the entry layout)
+template <int WF>
+__global__ void __launch_bounds__(512) w4g_wide_m64(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int flag;
+  wide_body<4, 8, 1, WF>(p, lds, &flag);
+}
+template <int WF>
+__global__ void __launch_bounds__(1024) w4g_wide_m64_kp2(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int flag;
+  wide_body<4, 8, 2, WF>(p, lds, &flag);
+}
+
 
 
 namespace {
@@ -371,17 +447,17 @@ hipError_t launch_wide_k(void (*kernel)(GemmArgs), int mbw, const Plan& pl, cons
   const size_t lds = wide_lds_bytes(pl);
   if (lds != (size_t)KPW * kASlots * mbw * 4 * 1024) return hipErrorInvalidValue;
   static std::mutex mu;
-  static std::set<int> done;
+  static std::set<std::pair<const void*, int>> done;   // (kernel, device) pairs opted in
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   {
+    const void* key = reinterpret_cast<const void*>(kernel);
     std::lock_guard<std::mutex> lk(mu);
-    if (!done.count(dev)) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+    if (!done.count({key, dev})) {
+      e = hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
-      done.insert(dev);
+      done.insert({key, dev});
     }
   }
   hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * kWideWaves * KPW), lds, s, a);
@@ -397,6 +473,21 @@ hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s) {
     case 16: return launch_wide_k<2>(w4a16_wide_m64_kp2, 4, pl, a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+namespace {
+template <int WF>
+hipError_t launch_w4g_wide_f(const Plan& pl, const GemmArgs& a, hipStream_t s) {
+  if (pl.wpt == 8) return launch_wide_k<1>(w4g_wide_m64<WF>, 4, pl, a, s);
+  if (pl.wpt == 16) return launch_wide_k<2>(w4g_wide_m64_kp2<WF>, 4, pl, a, s);
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_w4g_wide(const Plan& pl, const GemmArgs& a, bool zeros, hipStream_t s) {
+  if (pl.mb != 4 || (a.gs != 64 && a.gs % 128 != 0)) return hipErrorInvalidValue;
+  if (a.gs == 64) return zeros ? launch_w4g_wide_f<kWideGrid64Z>(pl, a, s) : launch_w4g_wide_f<kWideGrid64>(pl, a, s);
+  return zeros ? launch_w4g_wide_f<kWideGridZ>(pl, a, s) : launch_w4g_wide_f<kWideGrid>(pl, a, s);
 }
 
 }  // namespace qg

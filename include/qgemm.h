@@ -233,7 +233,7 @@ int qgemm_quantize_a8(const void* A, int64_t lda, int64_t M, int64_t K, void* A_
  *
  * qgemm_w4g_packed_bytes: blob size (has_zeros 0 or 1).
  * qgemm_w4g_workspace_bytes: workspace for a call of this shape with any grid
- *   (otherwise the contract of qgemm_workspace_bytes).
+ *   and activation type (otherwise the contract of qgemm_workspace_bytes).
  * qgemm_w4g_repack: codes uint32[K/8][N] (as W4A16), scales 16-bit
  *   [K/group_size][N] in the activation type (copied bit for bit), zeros
  *   uint8[K/group_size][N] or NULL (implicit 8; only the low 4 bits of each
@@ -312,22 +312,23 @@ int qgemm_w4a16_noalloc(const void* A, int64_t lda, const void* packed, void* C,
  * (per wave for kernel 2), 16-column blocks per wave, waves per workgroup,
  * k-splits across workgroups, groups per k-split, m-tiles, n-tiles,
  * workgroups, waves}. fmt may also be QGEMM_FMT_W4G: the plan for group length
- * 128 with zero points (qgemm_w4g_plan gives it for any grid). Host-only: its
- * only HIP calls are the cached device-property queries.
+ * 128 with zero points and fp16 activations (qgemm_w4g_plan gives it for any
+ * grid and type). Host-only: its only HIP calls are the cached device-property
+ * queries.
  */
 int qgemm_plan(int fmt, int64_t M, int64_t K, int64_t N, int64_t* out10);
 
 /*
  * The work decomposition of a call of any format (fmt QGEMM_FMT_BITPLANE uses
- * `bits`, QGEMM_FMT_W4G uses `group_size` and `has_zeros`; the others ignore
- * them) with the launch's resources: out12[0..9] as qgemm_plan, out12[10] =
+ * `bits`, QGEMM_FMT_W4G uses `group_size`, `has_zeros` and `act_dtype`; the
+ * others ignore them) with the launch's resources: out12[0..9] as qgemm_plan, out12[10] =
  * workspace bytes the call needs, out12[11] = dynamic LDS bytes per workgroup
  * the launch requests (at most 160 KB - 256). QGEMM_ERR_SHAPE when no launch
  * shape fits; argument rules as for the format's GEMM entry point. Host-only:
  * its only HIP calls are the cached device-property queries.
  */
 int qgemm_plan_info(int fmt, int64_t M, int64_t K, int64_t N, int32_t bits, int32_t group_size,
-                    int32_t has_zeros, int64_t* out12);
+                    int32_t has_zeros, int32_t act_dtype, int64_t* out12);
 
 /*
  * The work decomposition of a bit-plane W_b A8 call (qgemm_bitplane_a8) of
@@ -338,20 +339,22 @@ int qgemm_plan_info(int fmt, int64_t M, int64_t K, int64_t N, int32_t bits, int3
 int qgemm_bitplane_plan(int64_t M, int64_t K, int64_t N, int32_t bits, int64_t* out10);
 
 /*
- * The work decomposition of a general-grid call (qgemm_w4g) of this shape and
- * grid, in the layout of qgemm_plan; the grid sets the size of the grid
- * entries that the kernel can stage in LDS, so it enters the choice. An
- * invalid group_size or has_zeros: QGEMM_ERR_RANGE; shape rules as for
- * qgemm_w4g. Host-only (cached device-property queries only).
+ * The work decomposition of a general-grid call (qgemm_w4g) of this shape,
+ * grid and activation type, in the layout of qgemm_plan; the grid sets the
+ * size of the grid entries that the kernel can stage in LDS, and fp16 calls
+ * with N a multiple of 256 may run on the wide kernel (kernel id 2), so both
+ * enter the choice. An invalid group_size, has_zeros or act_dtype:
+ * QGEMM_ERR_RANGE; shape rules as for qgemm_w4g. Host-only (cached
+ * device-property queries only).
  */
 int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t has_zeros,
-                   int64_t* out10);
+                   int32_t act_dtype, int64_t* out10);
 
 /*
  * Override the automatic plan for later calls of this process: kernel (1 =
- * streaming kernel for every format, 2 = wide W4A16 kernel for N a multiple of
- * 256, 3 = general-grid streaming kernel with per-lane grid entries; other
- * cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or
+ * streaming kernel for every format, 2 = wide kernel for W4A16 and for the
+ * general grid with fp16 activations, N a multiple of 256, 3 = general-grid
+ * streaming kernel with per-lane grid entries; other cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or
  * 2; 4 is taken as 2), waves per workgroup (kernel 1: 4, 8 or 16; kernel 2:
  * 16 runs two K-parts of 8 waves, 4 or 8 one part of 8) and
  * k-splits across workgroups (1..4096); 0 keeps the automatic choice for that

@@ -316,27 +316,40 @@ def test_w4g_validation_without_gpu(L):
         assert st in (ERR_HIP, ERR_DEV)
 
 
-@pytest.mark.parametrize("K,N", [(4096, 11008), (11008, 4096), (1024, 1024), (8192, 28672)])
+@pytest.mark.parametrize("K,N", [(4096, 11008), (11008, 4096), (1024, 1024), (8192, 28672), (28672, 8192)])
 @pytest.mark.parametrize("M", [1, 16, 32, 64, 128])
 @pytest.mark.parametrize("gs,zeros", [(128, True), (64, True), (64, False), (None, False)])
-def test_w4g_plan_covers_every_unit_once(K, N, M, gs, zeros):
+@pytest.mark.parametrize("act", [qg.DT_F16, qg.DT_BF16])
+def test_w4g_plan_covers_every_unit_once(K, N, M, gs, zeros, act):
     gs = gs or K   # None: one group per column
-    p = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
-    assert p["kernel"] in (1, 3)   # grid entries staged in LDS / loaded per lane
-    # the workspace query covers every grid, so it may exceed this plan's need
+    p = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros, act_dtype=act)
+    if act == qg.DT_BF16 or N % 256:
+        assert p["kernel"] in (1, 3)   # grid entries staged in LDS / loaded per lane
+    else:
+        assert p["kernel"] in (1, 2, 3)   # fp16 may take the wide kernel
+    if p["kernel"] == 2:
+        assert M >= 33
+        assert p == {k: v for k, v in qg.plan(qg.FMT_W4A16, M, K, N).items()}   # the W4A16 wide plan
+    # the workspace query covers every grid and type, so it may exceed this plan's need
+    info = qg.plan_info(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros, act_dtype=act)
+    assert info["ws_bytes"] <= qg.workspace_bytes_w4g(M, K, N)
     _check_plan(p, M, K, N, ws=qg.workspace_bytes_w4g(M, K, N), exact_ws=False)
-    if (gs, zeros) == (128, True):
+    if (gs, zeros, act) == (128, True, qg.DT_F16):
         assert p == qg.plan(qg.FMT_W4G, M, K, N)   # the grid qgemm_plan reports
 
 
 def test_w4g_plan_validation(L):
     out = (ctypes.c_int64 * 10)()
-    assert L.qgemm_w4g_plan(16, 4096, 4096, 128, 1, None) == ERR_NULL
-    assert L.qgemm_w4g_plan(16, 4096, 4096, 96, 1, out) == ERR_RANGE
-    assert L.qgemm_w4g_plan(16, 4096, 4096, 128, 2, out) == ERR_RANGE
-    assert L.qgemm_w4g_plan(16, 4096, 4096, 8192, 0, out) == ERR_RANGE   # does not divide K
-    assert L.qgemm_w4g_plan(0, 4096, 4096, 128, 1, out) == ERR_SHAPE
-    assert L.qgemm_w4g_plan(16, 4096, 4096, 4096, 0, out) == OK
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 128, 1, 1, None) == ERR_NULL
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 96, 1, 1, out) == ERR_RANGE
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 128, 2, 1, out) == ERR_RANGE
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 128, 1, 3, out) == ERR_RANGE   # activation type
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 8192, 0, 1, out) == ERR_RANGE   # does not divide K
+    assert L.qgemm_w4g_plan(0, 4096, 4096, 128, 1, 1, out) == ERR_SHAPE
+    assert L.qgemm_w4g_plan(16, 4096, 4096, 4096, 0, 2, out) == OK
+    out12 = (ctypes.c_int64 * 12)()
+    assert L.qgemm_plan_info(qg.FMT_W4G, 16, 4096, 4096, 4, 128, 1, 0, out12) == ERR_RANGE
+    assert L.qgemm_plan_info(qg.FMT_W4A16, 16, 4096, 4096, 4, 128, 1, 0, out12) == OK   # ignored there
 
 
 def _w4g_lds_bytes(p, K, gs, zeros):
@@ -344,7 +357,10 @@ def _w4g_lds_bytes(p, K, gs, zeros):
     layout: staged grid entries (kernel 1: per column and chunk of the split,
     two entries for group length 64, else one; 4 bytes with zero points, else
     2), then K-parts x 3 activation slots of 4 KB per 16 rows; the reduction
-    buffer reuses the start."""
+    buffer reuses the start. The wide kernel (kernel 2) holds only its
+    activation ring: K-parts x 4 slots of 16 KB (64 rows x 128 k fp16)."""
+    if p["kernel"] == 2:
+        return (p["wpt"] // 8) * 4 * 16 * 1024
     ng = min(K // 128, p["gps"])
     nb_blocks, kp = 4 * p["nb"], p["wpt"] // 4
     extra = ng * nb_blocks * 16 * (2 if gs == 64 else 1) * (4 if zeros else 2) if p["kernel"] == 1 else 0
@@ -357,9 +373,13 @@ def test_w4g_plans_leave_room_for_static_lds(K, N):
     # A launch's LDS is this dynamic part plus the kernel's 16-byte arrival flag;
     # a dynamic part of the full 160 KB made the queue abort (28672 x 8192, M = 64).
     for gs, zeros in [(64, True), (64, False), (128, True), (128, False)]:
-        for M in range(1, 129, 7):
-            p = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
-            assert _w4g_lds_bytes(p, K, gs, zeros) <= 160 * 1024 - 256, (M, gs, zeros, p)
+        for act in (qg.DT_F16, qg.DT_BF16):
+            for M in range(1, 129, 7):
+                p = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros, act_dtype=act)
+                lds = _w4g_lds_bytes(p, K, gs, zeros)
+                assert lds <= 160 * 1024 - 256, (M, gs, zeros, act, p)
+                info = qg.plan_info(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros, act_dtype=act)
+                assert info["lds_bytes"] == lds, (M, gs, zeros, act, p, info)
 
 
 # --------------------------------------------------------------------------- 2:4 sparse
@@ -474,10 +494,22 @@ def test_every_automatic_plan_fits_lds_and_covers_the_layer(fmt, kw, K, N):
 
 def test_counter_region_grows_past_the_fixed_region():
     # W4G 16384 x 57344 x 8192 with group 64 and zero points: the case that
-    # once returned a plan needing 253,952 B of staged entries
-    p = qg.plan_info(qg.FMT_W4G, 16384, 57344, 8192, group_size=64, zeros=True)
+    # once returned a plan needing 253,952 B of staged entries (bf16
+    # activations: the streaming kernel, which fp16 calls of this width leave
+    # for the wide kernel)
+    p = qg.plan_info(qg.FMT_W4G, 16384, 57344, 8192, group_size=64, zeros=True, act_dtype=qg.DT_BF16)
     assert p["lds_bytes"] <= _LDS_BUDGET
     tiles = p["mt"] * p["nt"]
     assert tiles > 16384 and p["splits"] > 1
     assert p["ws_bytes"] >= (tiles * 4 + 255) // 256 * 256
     assert qg.workspace_bytes_w4g(16384, 57344, 8192) >= p["ws_bytes"]
+
+
+def test_w4g_takes_the_wide_kernel_on_70b_layers_with_fp16_activations():
+    # the wide kernel reads fp16 activations only: bf16 calls stay on the
+    # streaming kernels
+    for K, N in [(8192, 28672), (28672, 8192)]:
+        for M in (48, 64, 128):
+            for gs, zeros in [(64, True), (128, True), (128, False), (K, True)]:
+                assert qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)["kernel"] == 2
+                assert qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros, act_dtype=qg.DT_BF16)["kernel"] != 2

@@ -228,3 +228,68 @@ def test_w4g_matches_w4a16_on_its_grid():
     C_ref = ref.gemm_w4a16(p["A"], p["codes"], p["scales"])
     _ok(Cg, C_ref, K, "fp16", "w4g")
     _ok(C16, C_ref, K, "fp16", "w4a16")
+
+
+# ----------------------------------------------------------------------------- wide kernel
+# fp16 activations on layers whose width is a multiple of 256 may take the wide
+# kernel (64 x 256 tiles, 32 x 32 x 16 MFMAs); these cases force it.
+
+@pytest.mark.parametrize("gs,zeros,M,force", [(64, True, 33, (0, 8, 0)), (64, False, 70, (0, 16, 3)),
+                                              (128, True, 130, (0, 8, 2)), (256, False, 64, (0, 16, 0)),
+                                              (1024, True, 40, (0, 8, 5)), (1024, False, 97, (0, 8, 1))])
+def test_w4g_wide_one_hot_bit_exact(gs, zeros, M, force):
+    K, N, act = 1024, 512, "fp16"
+    _say("w4g wide one-hot", gs, zeros, M, force)
+    rng = np.random.default_rng(M * 5 + gs)
+    p = gen.w4g_problem(1, K, N, gs, zeros, act, seed=M + 2 * K, activations=False)
+    A, ks = _one_hot(M, K, rng, act)
+    qg.set_plan_override(*force, kernel=2)
+    assert qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)["kernel"] == 2
+    C = _run(p, A)
+    q = ref.unpack_u4(p["codes"])
+    z = 8 if p["zeros"] is None else p["zeros"][ks // gs].astype(np.int64)
+    w = (q[ks] - z).astype(np.float64) * ref.act_to_f64(p["scales"], act)[ks // gs]
+    assert np.array_equal(C.view(np.uint16), w.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("gs", [64, 128, 512])
+def test_w4g_wide_codes_at_zero_points_give_zero(gs):
+    K, N, M = 1024, 256, 45
+    _say("w4g wide zero", gs)
+    p = gen.w4g_problem(M, K, N, gs, True, "fp16", seed=6)
+    p = dict(p, codes=gen.pack_nibbles_u32(np.repeat(p["zeros"], gs, axis=0)))
+    qg.set_plan_override(kernel=2)
+    C = _run(p)
+    assert np.all(C.view(np.uint16) & 0x7FFF == 0)
+
+
+@pytest.mark.parametrize("gs,zeros", [(64, False), (64, True), (128, False), (128, True), (384, True), (2048, False)])
+@pytest.mark.parametrize("M,force", [(33, (0, 8, 0)), (64, (0, 16, 4)), (100, (0, 8, 1)), (128, (0, 16, 0))])
+def test_w4g_wide_gemm(gs, zeros, M, force):
+    K, N, act = 3072, 768, "fp16"
+    if K % gs:
+        pytest.skip("group length does not divide K")
+    _say("w4g wide gemm", gs, zeros, M, force)
+    p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=M * 11 + gs)
+    qg.set_plan_override(*force, kernel=2)
+    pl = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
+    assert pl["kernel"] == 2
+    C = _run(p)
+    _ok(C, ref.gemm_w4g(p["A"], p["codes"], p["scales"], p["zeros"], gs, act), K, act, (gs, zeros, M, pl))
+
+
+@pytest.mark.parametrize("gs,zeros", [(128, True), (64, False)])
+def test_w4g_wide_70b_down_projection_m128_sampled(gs, zeros):
+    # 28672 x 8192 at M = 128 in the automatic plan (two row tiles of the wide
+    # kernel, 16 waves); one column of every 16-column block plus a whole
+    # 256-column tile against the oracle
+    K, N, M, act = 28672, 8192, 128, "fp16"
+    pl = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
+    _say("w4g wide 70b down m128", gs, zeros, pl)
+    assert pl["kernel"] == 2
+    p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=79)
+    C = _run(p)
+    cols = np.unique(np.concatenate([np.arange(5 * 256, 6 * 256), block_cols(N, seed=9)]))
+    z = None if p["zeros"] is None else p["zeros"][:, cols]
+    ref_cols = ref.gemm_w4g(p["A"], p["codes"][:, cols], p["scales"][:, cols], z, gs, act)
+    _ok(C[:, cols], ref_cols, K, act, ("70b down m128", gs, zeros))
