@@ -47,6 +47,26 @@ __global__ void __launch_bounds__(kThreads) stream_read(const void* src, uint32_
   if (lane == 0) atomicAdd(sink, s);
 }
 
+// Per-lane pseudo-random operands (xorshift32): fp16 uniform in [-1, 1) and
+// int8 uniform in [-128, 127], as a GEMM on real data feeds the matrix cores.
+struct LaneRandom {
+  uint32_t x;
+  __device__ explicit LaneRandom(uint32_t seed) : x(seed * 2654435761u + 0x9E3779B9u) {}
+  __device__ uint32_t next() {
+    x ^= x << 13;
+    x ^= x >> 17;
+    x ^= x << 5;
+    return x;
+  }
+  __device__ f16x8 halves() {
+    f16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (f16)((float)(next() & 0xFFFF) * (1.0f / 32768.0f) - 1.0f);
+    return r;
+  }
+  __device__ i32x4 bytes() { return i32x4{(int)next(), (int)next(), (int)next(), (int)next()}; }
+};
+
 template <int KIND>
 __global__ void __launch_bounds__(kThreads) mfma_loop(uint32_t* sink, int iters) {
   const int lane = threadIdx.x & 63;
@@ -56,7 +76,42 @@ __global__ void __launch_bounds__(kThreads) mfma_loop(uint32_t* sink, int iters)
   const f16x8 a = {h, h, h, h, h, h, h, h};
   const i32x4 ai = {lane & 3, 1, 0, (lane >> 2) & 1};
   uint32_t out = 0;
-  if constexpr (KIND == 0) {
+  if constexpr (KIND == 5) {
+    // random operands: four A fragments, two B fragments alternating per step
+    LaneRandom g((uint32_t)(blockIdx.x * kThreads + threadIdx.x));
+    f16x8 ra[4], rb[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = g.halves();
+    rb[0] = g.halves();
+    rb[1] = g.halves();
+    f32x16 acc[4] = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[j & 3], rb[(j >> 2) & 1], acc[j & 3], 0, 0, 0);
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t += acc[j][0] + acc[j][15];
+    out = __float_as_uint(t);
+  } else if constexpr (KIND == 6) {
+    LaneRandom g((uint32_t)(blockIdx.x * kThreads + threadIdx.x));
+    i32x4 ra[4], rb[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ra[j] = g.bytes();
+    rb[0] = g.bytes();
+    rb[1] = g.bytes();
+    i32x4 acc[4] = {};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[j & 3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ra[j & 3], rb[(j >> 2) & 1], acc[j & 3], 0, 0, 0);
+    }
+    int t = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t += acc[j][0] + acc[j][3];
+    out = (uint32_t)t;
+  } else if constexpr (KIND == 0) {
     f32x16 acc[4] = {};
     for (int i = 0; i < iters; ++i) {
 #pragma unroll
@@ -153,7 +208,9 @@ int64_t qgemm_probe_mfma_ops(int kind) {
     case 1: return 16LL * 16 * 32 * 2;
     case 2: return 16LL * 16 * 64 * 2;
     case 3:
-    case 4: return 32LL * 32 * 16 * 2;
+    case 4:
+    case 5: return 32LL * 32 * 16 * 2;
+    case 6: return 16LL * 16 * 64 * 2;
     default: return 0;
   }
 }
@@ -169,6 +226,8 @@ int qgemm_probe_mfma(void* sink, int64_t sink_words, int workgroups, int iters, 
     case 1: hipLaunchKernelGGL(mfma_loop<1>, dim3((unsigned)workgroups), dim3(kThreads), 0, s, out, iters); break;
     case 2: hipLaunchKernelGGL(mfma_loop<2>, dim3((unsigned)workgroups), dim3(kThreads), 0, s, out, iters); break;
     case 3: hipLaunchKernelGGL(mfma_lds_loop<1>, dim3((unsigned)workgroups), dim3(kThreads), 0, s, out, iters); break;
+    case 5: hipLaunchKernelGGL(mfma_loop<5>, dim3((unsigned)workgroups), dim3(kThreads), 0, s, out, iters); break;
+    case 6: hipLaunchKernelGGL(mfma_loop<6>, dim3((unsigned)workgroups), dim3(kThreads), 0, s, out, iters); break;
     default: hipLaunchKernelGGL(mfma_lds_loop<2>, dim3((unsigned)workgroups), dim3(kThreads), 0, s, out, iters); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : kErrHip;

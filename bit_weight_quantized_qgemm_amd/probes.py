@@ -14,7 +14,8 @@ from bit_weight_quantized_qgemm_amd import build as _b
 SYMBOLS = ("qgemm_probe_stream_read", "qgemm_probe_mfma", "qgemm_probe_mfma_ops")
 KINDS = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_16x16x32_f16", 2: "v_mfma_i32_16x16x64_i8",
          3: "v_mfma_f32_32x32x16_f16_a_from_lds_1kb_per_mfma",
-         4: "v_mfma_f32_32x32x16_f16_a_from_lds_1kb_per_2_mfma"}
+         4: "v_mfma_f32_32x32x16_f16_a_from_lds_1kb_per_2_mfma",
+         5: "v_mfma_f32_32x32x16_f16_random_operands", 6: "v_mfma_i32_16x16x64_i8_random_operands"}
 _lib = None
 
 

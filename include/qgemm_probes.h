@@ -37,7 +37,10 @@ int qgemm_probe_stream_read(const void* src, int64_t bytes, void* sink, int work
  * v_mfma_f32_16x16x32_f16 (16384); kind 2: v_mfma_i32_16x16x64_i8 (32768
  * integer ops); kinds 3 and 4: v_mfma_f32_32x32x16_f16 whose A operand is
  * read from LDS, one 1 KB wave read (ds_read_b128) per instruction (kind 3)
- * or per two instructions (kind 4), with 16 KB of LDS per workgroup. Each
+ * or per two instructions (kind 4), with 16 KB of LDS per workgroup; kinds 5
+ * and 6: kinds 0 and 2 on pseudo-random operands (fp16 uniform in [-1, 1),
+ * int8 uniform over its range; kinds 0-4 feed small constants, and the rate
+ * the chip sustains depends on the operand data). Each
  * wave writes one 32-bit word of its accumulators to
  * `sink` (at least 4 * workgroups 32-bit words, given as `sink_words`) so no
  * instruction is dead. */

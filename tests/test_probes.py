@@ -28,7 +28,9 @@ def test_probe_argument_checks_need_no_gpu():
     assert L.qgemm_probe_mfma_ops(2) == 32768
     assert L.qgemm_probe_mfma_ops(3) == 32768
     assert L.qgemm_probe_mfma_ops(4) == 32768
-    assert L.qgemm_probe_mfma_ops(5) == 0
+    assert L.qgemm_probe_mfma_ops(5) == 32768
+    assert L.qgemm_probe_mfma_ops(6) == 32768
+    assert L.qgemm_probe_mfma_ops(7) == 0
     # rejected before any HIP call: null pointers, sizes, alignment, 32-bit offset range
     assert L.qgemm_probe_stream_read(None, 1024, 16, 8, 0, None) == -1
     assert L.qgemm_probe_stream_read(16, 1000, 16, 8, 0, None) == -1
@@ -37,7 +39,7 @@ def test_probe_argument_checks_need_no_gpu():
     assert L.qgemm_probe_stream_read(16, 4 << 30, 16, 8, 0, None) == -1
     assert L.qgemm_probe_stream_read(16, 1024, 16, 8, 2, None) == -1
     assert L.qgemm_probe_mfma(16, 31, 8, 1, 0, None) == -1   # sink smaller than 4 words per workgroup
-    assert L.qgemm_probe_mfma(16, 32, 8, 1, 5, None) == -1   # unknown kind
+    assert L.qgemm_probe_mfma(16, 32, 8, 1, 7, None) == -1   # unknown kind
     assert L.qgemm_probe_mfma(16, 32, 8, 0, 0, None) == -1
 
 
