@@ -170,7 +170,9 @@ BlobLayout blob_layout_bitplane(int64_t K, int64_t N, int bits) {
 // workgroups until about one workgroup per CU is busy: measured on MI355X, a
 // second resident workgroup per CU does not pay for the extra partial-sum
 // traffic of the splits it needs.
-Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
+// nb = 4: 256-column tiles of 8-wave K-parts; nb = 2: 128-column tiles of two
+// 4-wave K-parts (the same 64 x 32 wave tile)
+Plan make_wide_plan_nb(int64_t M, int64_t K, int64_t N, int nb) {
   Plan pl;
   const int G = (int)(K / kGroup);
   pl.kernel = 2;
@@ -179,7 +181,7 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   // than taller tiles that would need more k-splits (measured on MI355X:
   // 128 x 8192 x 28672 in 78 us as 2 x 64 rows vs 93 us as one 128-row tile)
   pl.mb = 4;
-  pl.nb = 4;
+  pl.nb = nb;
   // 8 waves (two per SIMD), or 16 as two K-parts of 8: on layers of at least
   // 2^27 weights at M > 64 (two row tiles) the extra waves hide more of the
   // weight stream (measured on MI355X, 70B layers: 48.3 vs 52.1 us at M = 96,
@@ -187,8 +189,9 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
   // M, 8 waves were faster: 21.7 vs 23.3 us at 128 x 4096 x 11008)
   const int fw = g_force_wpt.load();
   pl.wpt = fw == 16 ? 16 : fw != 0 ? 8 : (M > 64 && K * N >= (int64_t(1) << 27) ? 16 : 8);
+  if (nb == 2) pl.wpt = 8;
   pl.mt = (int)((M + 16 * pl.mb - 1) / (16 * pl.mb));
-  pl.nt = (int)(N / kWideCols);
+  pl.nt = (int)(N / (64 * nb));
   const int64_t tiles = (int64_t)pl.mt * pl.nt;
   const int force_splits = g_force_splits.load();
   const int best = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(1, G / 2), device_cu_count() / tiles));
@@ -204,6 +207,23 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
     pl.ws_bytes = pl.counter_bytes + align256((size_t)pl.splits * pl.mt * 16 * pl.mb * N * 4);
   }
   return pl;
+}
+
+// The 256-column plan, or the 128-column one where it needs fewer k-splits for
+// at most one workgroup per CU while the 256-column plan runs 8 waves: the
+// same workgroups with fewer partial sums (measured on MI355X in one process:
+// 128 x 4096 x 11008 22.5 against 25.6 us, 28672 x 8192 at M = 48 / 64 48.1 /
+// 45.9 against 50.0 / 47.0 us, 8192 x 28672 at M = 48 / 64 50.8 / 52.0 against
+// 52.1 / 52.3 us; where the 256-column plan runs 16 waves, at M > 64 on the
+// 70B layers, the 128-column tiles were 5-21 % slower).
+Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
+  const int fnb = g_force_nb.load();
+  if (fnb == 2 || fnb == 4) return make_wide_plan_nb(M, K, N, fnb);
+  const Plan p256 = make_wide_plan_nb(M, K, N, 4);
+  if (p256.wpt != 8 || p256.splits == 1) return p256;
+  const Plan p128 = make_wide_plan_nb(M, K, N, 2);
+  if ((int64_t)p128.mt * p128.nt <= device_cu_count() && p128.splits < p256.splits) return p128;
+  return p256;
 }
 
 // Waves per SIMD that the register use of each streaming kernel allows, as
@@ -282,8 +302,10 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
     // narrow layers, and their partial sums then cost more than re-streaming
     // the weights once per 32-row tile of the streaming kernel (measured on
     // MI355X: 7B-class layers at M = 64..128 and N = 8192 at M = 128).
-    const Plan wide = make_wide_plan(M, K, N);
-    if (force_kernel == 2 || wide.splits <= 4 || (K * N >= (int64_t(1) << 27) && M <= 64)) return wide;
+    // (decided on the 256-column plan's k-splits)
+    const Plan wide = make_wide_plan_nb(M, K, N, 4);
+    if (force_kernel == 2 || wide.splits <= 4 || (K * N >= (int64_t(1) << 27) && M <= 64))
+      return make_wide_plan(M, K, N);
   }
   // Streaming kernel: 4*KP-wave workgroups own 16*mb x 64*nb tiles; the 4
   // column waves of each of the KP K-parts share activations through LDS.

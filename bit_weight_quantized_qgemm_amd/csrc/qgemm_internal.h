@@ -22,7 +22,7 @@ constexpr int kMaxWavesPerTile = 16;
 // and a launch whose total exceeds the limit aborts the queue.
 constexpr size_t kLdsPerWorkgroup = 160 * 1024;
 constexpr size_t kSkinnyLdsBudget = kLdsPerWorkgroup - 256;
-constexpr int kWideCols = 256;        // columns per tile of the wide kernel
+constexpr int kWideCols = 256;        // columns per tile of the wide kernel (also 128: plan nb = 2)
 constexpr int kWideSlots = 4;         // activation LDS slots per K-part of the wide kernel
 constexpr int kWideMinM = 33;         // batches from which the wide kernel is used
 // Split-K arrival counters live in a fixed region at the start of every
@@ -53,7 +53,8 @@ BlobLayout blob_layout(int fmt, int64_t K, int64_t N, int64_t n4);
 
 // Work decomposition of one GEMM call. Kernel 1: workgroups of wpt = 4*KP
 // waves own tiles of 16*mb rows x 64*nb columns, KP K-parts of 4 column waves;
-// kernel 2: 4-wave workgroups own 16*mb x 256 tiles. `splits` > 1 additionally
+// kernel 2: wpt-wave workgroups own 16*mb x 64*nb tiles as K-parts of 2*nb
+// column waves of 32 columns. `splits` > 1 additionally
 // splits K across workgroups.
 struct Plan {
   // 1 = streaming skinny kernel, 2 = wide (large-M) W4A16 kernel, 3 = streaming
@@ -80,7 +81,10 @@ inline int64_t launch_workgroups(int64_t nt, int64_t mt, int64_t splits) { retur
 
 // dynamic LDS of a wide-kernel launch: per K-part of 8 waves, kWideSlots slots
 // of 16*mb rows x 128 k fp16
-inline size_t wide_lds_bytes(const Plan& pl) { return (size_t)(pl.wpt / 8) * kWideSlots * pl.mb * 4 * 1024; }
+// K-parts of 2*nb waves (nb = 4: 256-column tiles, 2: 128-column tiles)
+inline size_t wide_lds_bytes(const Plan& pl) {
+  return (size_t)(pl.wpt / (2 * pl.nb)) * kWideSlots * pl.mb * 4 * 1024;
+}
 
 // bits: planes per weight of the bit-plane format (ignored by the others)
 // gs / zeros: the general-grid format's group length and zero points (its

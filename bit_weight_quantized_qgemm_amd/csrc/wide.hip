@@ -4,10 +4,12 @@
 // fp16 activations (per group and column a scale and optionally a zero point;
 // the page on 2-bit LLMs on GPUs quantizes by groups and leaves the length open).
 //
-// Each workgroup owns a tile of 16*MBW = 64 rows x 256 columns; its eight
+// Each workgroup owns a tile of 16*MBW = 64 rows x TC = 256 columns; its eight
 // waves (two per SIMD, so one wave's dequantization and LDS reads overlap the
 // other's matrix operations) form a grid of NWC column waves x 8/NWC row waves,
-// each owning 256/NWC columns and 16*MBW*NWC/8 rows. Each weight is dequantized
+// each owning 256/NWC columns and 16*MBW*NWC/8 rows. Layers whose 256-column
+// tiles would need more k-splits take 64 x 128 tiles, whose eight waves are
+// two K-parts of four (WPK) 32-column waves. Each weight is dequantized
 // by the 8/NWC row waves of its columns and reused by all of their rows. The products
 // run on v_mfma_f32_32x32x16_f16, which does twice the work of the 16x16x32 form
 // for the same operand bytes and sustains a higher rate on gfx950:
@@ -70,21 +72,21 @@ struct WideStage {
 
 }  // namespace
 
-template <int MBW, int NWC, int KPW, int WF = kWideW4A16>
+template <int MBW, int NWC, int KPW, int WF = kWideW4A16, int WPK = kWideWaves, int TC = kWideCols>
 __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* flag) {
-  constexpr int NWR = kWideWaves / NWC;             // row waves
-  constexpr int kWideJB = kWideCols / 32 / NWC;     // 32-column blocks per wave
+  constexpr int NWR = WPK / NWC;                    // row waves
+  constexpr int kWideJB = TC / 32 / NWC;            // 32-column blocks per wave
   constexpr int R32T = MBW / 2;                     // 32-row blocks of the tile
   constexpr int R32 = R32T / NWR;                   // 32-row blocks per wave
   static_assert(R32 >= 1 && kWideJB >= 1, "wave grid");
   constexpr int kSlotBytes = R32T * 8 * 1024;       // 32-row blocks x 8 k-steps x 1 KB
-  constexpr int kAPerWave = R32T * 8 / kWideWaves;  // 1 KB activation loads per wave per group
+  constexpr int kAPerWave = R32T * 8 / WPK;         // 1 KB activation loads per wave per group
   using Stage = WideStage<kWideJB>;
 
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kpi = wave_all / kWideWaves;             // K-part of this wave
-  const int wave = wave_all % kWideWaves;            // wave within its K-part
+  const int kpi = wave_all / WPK;                    // K-part of this wave
+  const int wave = wave_all % WPK;                   // wave within its K-part
   const int wc = wave % NWC, wr = wave / NWC;
   const int c32 = lane & 31, hh = lane >> 5;
   const TileIndex tix = tile_of_block(p);
@@ -99,7 +101,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   const int G0 = ng > 0 ? gk0 : G0s;                 // an empty K-part re-reads the first group
   const int row0 = mt * MBW * 16;
   const int rows = min(MBW * 16, p.M - row0);
-  const int bw = nt * (kWideCols / 16) + wc * 2 * kWideJB;     // first 16-column block of the wave
+  const int bw = nt * (TC / 16) + wc * 2 * kWideJB;     // first 16-column block of the wave
   const int rw0 = wr * R32 * 32;                                // first tile row of the wave
 
   // activations: rows of the tile from k = 128*G0; rows beyond M re-read a valid row
@@ -289,7 +291,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
     __syncthreads();
     constexpr int kAcc4 = R32 * kWideJB * 4;         // f32x4 per lane
     f32x4* red = reinterpret_cast<f32x4*>(lds);
-    auto at = [&](int q, int e4) -> f32x4& { return red[(((q - 1) * kWideWaves + wave) * kAcc4 + e4) * 64 + lane]; };
+    auto at = [&](int q, int e4) -> f32x4& { return red[(((q - 1) * WPK + wave) * kAcc4 + e4) * 64 + lane]; };
     if (kpi > 0) {
 #pragma unroll
       for (int rb = 0; rb < R32; ++rb)
@@ -342,7 +344,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs& p, char* lds, int* fla
   // 16-byte device-coherent buffer operation. Region of (split, tile):
   // kWideWaves * R32 * kWideJB * 4 KB.
   constexpr int kFrag = R32 * kWideJB * 4;
-  constexpr uint32_t kRegion = kWideWaves * kFrag * 1024;
+  constexpr uint32_t kRegion = WPK * kFrag * 1024;
   const size_t tile_id = (size_t)mt * p.nt + nt;
   const size_t ntiles = (size_t)p.mt * p.nt;
   auto region = [&](int q) {
@@ -421,6 +423,14 @@ __global__ void __launch_bounds__(1024) w4a16_wide_m64_kp2(GemmArgs p) {
   wide_body<4, 8, 2>(p, lds, &flag);
 }
 
+// 64 x 128 tiles: two K-parts of four 32-column waves (two waves per SIMD),
+// for layers where 256-column tiles would need more k-splits
+__global__ void __launch_bounds__(512) w4a16_wide_m64_n128(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int flag;
+  wide_body<4, 4, 2, kWideW4A16, 4, 128>(p, lds, &flag);
+}
+
 // the general grid with fp16 activations (WF: the entry layout)
 template <int WF>
 __global__ void __launch_bounds__(512) w4g_wide_m64(GemmArgs p) {
@@ -434,6 +444,12 @@ __global__ void __launch_bounds__(1024) w4g_wide_m64_kp2(GemmArgs p) {
   __shared__ int flag;
   wide_body<4, 8, 2, WF>(p, lds, &flag);
 }
+template <int WF>
+__global__ void __launch_bounds__(512) w4g_wide_m64_n128(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ int flag;
+  wide_body<4, 4, 2, WF, 4, 128>(p, lds, &flag);
+}
 
 
 
@@ -441,7 +457,7 @@ namespace {
 
 // KPW K-parts of eight waves; the LDS size is fixed per kernel: opt in to it
 // (above 64 KiB) once per kernel and device
-template <int KPW>
+template <int KPW, int WPK = kWideWaves>
 hipError_t launch_wide_k(void (*kernel)(GemmArgs), int mbw, const Plan& pl, const GemmArgs& a, hipStream_t s) {
   static_assert(kASlots == kWideSlots, "the planner sizes the LDS ring");
   const size_t lds = wide_lds_bytes(pl);
@@ -460,7 +476,7 @@ hipError_t launch_wide_k(void (*kernel)(GemmArgs), int mbw, const Plan& pl, cons
       done.insert({key, dev});
     }
   }
-  hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * kWideWaves * KPW), lds, s, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)pl.workgroups), dim3(kWave * WPK * KPW), lds, s, a);
   return hipGetLastError();
 }
 
@@ -468,6 +484,8 @@ hipError_t launch_wide_k(void (*kernel)(GemmArgs), int mbw, const Plan& pl, cons
 
 hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s) {
   if (pl.mb != 4) return hipErrorInvalidValue;
+  if (pl.nb == 2) return pl.wpt == 8 ? launch_wide_k<2, 4>(w4a16_wide_m64_n128, 4, pl, a, s) : hipErrorInvalidValue;
+  if (pl.nb != 4) return hipErrorInvalidValue;
   switch (pl.wpt) {
     case 8: return launch_wide_k<1>(w4a16_wide_m64, 4, pl, a, s);
     case 16: return launch_wide_k<2>(w4a16_wide_m64_kp2, 4, pl, a, s);
@@ -478,6 +496,8 @@ hipError_t launch_w4a16_wide(const Plan& pl, const GemmArgs& a, hipStream_t s) {
 namespace {
 template <int WF>
 hipError_t launch_w4g_wide_f(const Plan& pl, const GemmArgs& a, hipStream_t s) {
+  if (pl.nb == 2) return pl.wpt == 8 ? launch_wide_k<2, 4>(w4g_wide_m64_n128<WF>, 4, pl, a, s) : hipErrorInvalidValue;
+  if (pl.nb != 4) return hipErrorInvalidValue;
   if (pl.wpt == 8) return launch_wide_k<1>(w4g_wide_m64<WF>, 4, pl, a, s);
   if (pl.wpt == 16) return launch_wide_k<2>(w4g_wide_m64_kp2<WF>, 4, pl, a, s);
   return hipErrorInvalidValue;

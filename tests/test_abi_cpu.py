@@ -182,8 +182,9 @@ def _blocks_cover_tiles_once(p):
 def _check_plan(p, M, K, N, ws=None, exact_ws=True):
     G = K // 128
     if p["kernel"] == 2:
-        assert p["mb"] == 4 and p["nb"] == 4 and p["wpt"] in (8, 16)
-        assert p["nt"] * 256 == N and p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
+        # 256-column tiles of 8 or 16 waves, or 128-column tiles of 8 (two K-parts of 4)
+        assert p["mb"] == 4 and (p["nb"], p["wpt"]) in ((4, 8), (4, 16), (2, 8))
+        assert p["nt"] * 64 * p["nb"] == N and p["mt"] * p["mb"] * 16 >= M > (p["mt"] - 1) * p["mb"] * 16
         assert p["workgroups"] == _launch_workgroups(p["nt"], p["mt"], p["splits"])
         _blocks_cover_tiles_once(p)
         cover = np.zeros(G, dtype=int)
@@ -268,6 +269,12 @@ def test_plan_override(L):
         qg.set_plan_override(kernel=2, k_splits=3)
         p = qg.plan(qg.FMT_W4A16, 8, 8192, 28672)
         assert p["kernel"] == 2 and p["splits"] == 3
+        # tile width of the wide kernel: nb 4 (256 columns) or 2 (128 columns)
+        for nb, wpt in [(4, 16), (4, 8), (2, 8), (2, 16)]:
+            qg.set_plan_override(nb, wpt, 0, kernel=2)
+            p = qg.plan(qg.FMT_W4A16, 64, 8192, 28672)
+            assert (p["kernel"], p["nb"], p["nt"]) == (2, nb, 28672 // (64 * nb))
+            assert p["wpt"] == (wpt if nb == 4 else 8)
     finally:
         qg.set_plan_override()
 
@@ -358,9 +365,10 @@ def _w4g_lds_bytes(p, K, gs, zeros):
     two entries for group length 64, else one; 4 bytes with zero points, else
     2), then K-parts x 3 activation slots of 4 KB per 16 rows; the reduction
     buffer reuses the start. The wide kernel (kernel 2) holds only its
-    activation ring: K-parts x 4 slots of 16 KB (64 rows x 128 k fp16)."""
+    activation ring: K-parts (of 8 waves for 256-column tiles, of 4 for
+    128-column tiles) x 4 slots of 16 KB (64 rows x 128 k fp16)."""
     if p["kernel"] == 2:
-        return (p["wpt"] // 8) * 4 * 16 * 1024
+        return (p["wpt"] // (2 * p["nb"])) * 4 * 16 * 1024
     ng = min(K // 128, p["gps"])
     nb_blocks, kp = 4 * p["nb"], p["wpt"] // 4
     extra = ng * nb_blocks * 16 * (2 if gs == 64 else 1) * (4 if zeros else 2) if p["kernel"] == 1 else 0
@@ -513,3 +521,16 @@ def test_w4g_takes_the_wide_kernel_on_70b_layers_with_fp16_activations():
             for gs, zeros in [(64, True), (128, True), (128, False), (K, True)]:
                 assert qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)["kernel"] == 2
                 assert qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros, act_dtype=qg.DT_BF16)["kernel"] != 2
+
+
+def test_wide_plans_take_128_column_tiles_where_they_save_k_splits():
+    # the 70B layers at M = 33-64 and 7B-class layers at M = 96-128 (8-wave
+    # 256-column plans with k-splits); M > 64 on the 70B layers keeps the
+    # 16-wave 256-column tiles
+    for (K, N, M, nb, splits) in [(8192, 28672, 33, 2, 1), (8192, 28672, 64, 2, 1), (28672, 8192, 48, 2, 4),
+                                  (28672, 8192, 64, 2, 4), (4096, 11008, 128, 2, 1), (8192, 28672, 128, 4, 1),
+                                  (28672, 8192, 128, 4, 4), (8192, 28672, 96, 4, 1)]:
+        p = qg.plan(qg.FMT_W4A16, M, K, N)
+        assert (p["kernel"], p["nb"], p["splits"]) == (2, nb, splits), (K, N, M, p)
+        assert qg.plan(qg.FMT_W4G, M, K, N) == p
+        _check_plan(p, M, K, N)

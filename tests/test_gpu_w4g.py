@@ -234,9 +234,11 @@ def test_w4g_matches_w4a16_on_its_grid():
 # fp16 activations on layers whose width is a multiple of 256 may take the wide
 # kernel (64 x 256 tiles, 32 x 32 x 16 MFMAs); these cases force it.
 
-@pytest.mark.parametrize("gs,zeros,M,force", [(64, True, 33, (0, 8, 0)), (64, False, 70, (0, 16, 3)),
-                                              (128, True, 130, (0, 8, 2)), (256, False, 64, (0, 16, 0)),
-                                              (1024, True, 40, (0, 8, 5)), (1024, False, 97, (0, 8, 1))])
+@pytest.mark.parametrize("gs,zeros,M,force", [(64, True, 33, (4, 8, 0)), (64, False, 70, (4, 16, 3)),
+                                              (128, True, 130, (4, 8, 2)), (256, False, 64, (4, 16, 0)),
+                                              (1024, True, 40, (4, 8, 5)), (1024, False, 97, (4, 8, 1)),
+                                              (64, True, 50, (2, 8, 0)), (64, False, 128, (2, 8, 3)),
+                                              (128, False, 33, (2, 8, 1)), (512, True, 100, (2, 8, 2))])
 def test_w4g_wide_one_hot_bit_exact(gs, zeros, M, force):
     K, N, act = 1024, 512, "fp16"
     _say("w4g wide one-hot", gs, zeros, M, force)
@@ -244,7 +246,8 @@ def test_w4g_wide_one_hot_bit_exact(gs, zeros, M, force):
     p = gen.w4g_problem(1, K, N, gs, zeros, act, seed=M + 2 * K, activations=False)
     A, ks = _one_hot(M, K, rng, act)
     qg.set_plan_override(*force, kernel=2)
-    assert qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)["kernel"] == 2
+    pl = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
+    assert pl["kernel"] == 2 and pl["nb"] == force[0]
     C = _run(p, A)
     q = ref.unpack_u4(p["codes"])
     z = 8 if p["zeros"] is None else p["zeros"][ks // gs].astype(np.int64)
@@ -264,7 +267,8 @@ def test_w4g_wide_codes_at_zero_points_give_zero(gs):
 
 
 @pytest.mark.parametrize("gs,zeros", [(64, False), (64, True), (128, False), (128, True), (384, True), (2048, False)])
-@pytest.mark.parametrize("M,force", [(33, (0, 8, 0)), (64, (0, 16, 4)), (100, (0, 8, 1)), (128, (0, 16, 0))])
+@pytest.mark.parametrize("M,force", [(33, (4, 8, 0)), (64, (4, 16, 4)), (100, (4, 8, 1)), (128, (4, 16, 0)),
+                                     (48, (2, 8, 0)), (128, (2, 8, 2))])
 def test_w4g_wide_gemm(gs, zeros, M, force):
     K, N, act = 3072, 768, "fp16"
     if K % gs:
@@ -273,7 +277,7 @@ def test_w4g_wide_gemm(gs, zeros, M, force):
     p = gen.w4g_problem(M, K, N, gs, zeros, act, seed=M * 11 + gs)
     qg.set_plan_override(*force, kernel=2)
     pl = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=zeros)
-    assert pl["kernel"] == 2
+    assert pl["kernel"] == 2 and pl["nb"] == force[0]
     C = _run(p)
     _ok(C, ref.gemm_w4g(p["A"], p["codes"], p["scales"], p["zeros"], gs, act), K, act, (gs, zeros, M, pl))
 
