@@ -308,8 +308,9 @@ int qgemm_w4a16_noalloc(const void* A, int64_t lda, const void* packed, void* C,
 /*
  * Work decomposition used for a call of this shape (for tests and tuning).
  * Fills out10[0..9] = {kernel id (1 streaming, 2 wide, 3 streaming general-grid
- * kernel with per-lane grid entries; 1 there stages them in LDS), 16-row blocks per tile
- * (per wave for kernel 2), 16-column blocks per wave, waves per workgroup,
+ * kernel with per-lane grid entries; 1 there stages them in LDS), 16-row blocks per tile,
+ * 16-column blocks per wave (kernel 2: the tile width in 64-column units, 4
+ * or 2), waves per workgroup,
  * k-splits across workgroups, groups per k-split, m-tiles, n-tiles,
  * workgroups, waves}. fmt may also be QGEMM_FMT_W4G: the plan for group length
  * 128 with zero points and fp16 activations (qgemm_w4g_plan gives it for any
@@ -354,9 +355,12 @@ int qgemm_w4g_plan(int64_t M, int64_t K, int64_t N, int32_t group_size, int32_t 
  * Override the automatic plan for later calls of this process: kernel (1 =
  * streaming kernel for every format, 2 = wide kernel for W4A16 and for the
  * general grid with fp16 activations, N a multiple of 256, 3 = general-grid
- * streaming kernel with per-lane grid entries; other cases keep kernel 1), 16-column blocks per wave of kernel 1 (1 or
- * 2; 4 is taken as 2), waves per workgroup (kernel 1: 4, 8 or 16; kernel 2:
- * 16 runs two K-parts of 8 waves, 4 or 8 one part of 8) and
+ * streaming kernel with per-lane grid entries; other cases keep kernel 1),
+ * nb: 16-column blocks per wave of kernel 1 (1 or 2; 4 is taken as 2), or the
+ * tile width of kernel 2 in 64-column units (4: 256 columns, 2: 128 columns
+ * as two K-parts of 4 waves, which fixes 8 waves; 1: automatic), waves per
+ * workgroup (kernel 1: 4, 8 or 16; kernel 2 with 256 columns: 16 runs two
+ * K-parts of 8 waves, 4 or 8 one part of 8) and
  * k-splits across workgroups (1..4096); 0 keeps the automatic choice for that
  * field. Values a shape cannot use are clamped (no more K-parts than groups).
  * For tests of the split-K reductions and for tuning sweeps; affects
