@@ -41,10 +41,11 @@ __global__ void __launch_bounds__(kThreads) stream_read(const void* src, uint32_
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) s += v[u][0] + v[u][1] + v[u][2] + v[u][3];
   }
-  // wave sum, then one atomic add per wave
+  // wave sum into the wave's own slot (no atomics: thousands of them on one
+  // address serialize at the end of the read and would be timed with it)
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d);
-  if (lane == 0) atomicAdd(sink, s);
+  if (lane == 0) sink[wave] = s;
 }
 
 // Per-lane pseudo-random operands (xorshift32): fp16 uniform in [-1, 1) and
@@ -185,9 +186,11 @@ __global__ void __launch_bounds__(kThreads) mfma_lds_loop(uint32_t* sink, int it
 
 extern "C" {
 
-int qgemm_probe_stream_read(const void* src, int64_t bytes, void* sink, int workgroups, int chunked, void* stream) {
+int qgemm_probe_stream_read(const void* src, int64_t bytes, void* sink, int64_t sink_words, int workgroups,
+                            int chunked, void* stream) {
   if (!src || !sink || bytes <= 0 || bytes % 16 || bytes > (int64_t(3) << 30) || workgroups <= 0 ||
-      workgroups > 65536 || (reinterpret_cast<uintptr_t>(src) & 15) || (chunked != 0 && chunked != 1))
+      workgroups > 65536 || (reinterpret_cast<uintptr_t>(src) & 15) || (chunked != 0 && chunked != 1) ||
+      sink_words < (int64_t)workgroups * (kThreads / 64))
     return kErrArg;
   // every offset a lane forms (the last round's included) stays below 2^32:
   // bytes + kInFlight * grid bytes bounds them in both orders

@@ -26,10 +26,12 @@ extern "C" {
  * multiple of 16, at most 3 GiB) with 16-byte vector loads, eight in flight
  * per lane, from `workgroups` workgroups of 256 threads striding over the
  * buffer: with chunked = 0 a wave's eight 1 KB loads of a round lie one grid
- * width apart, with chunked = 1 they are 8 consecutive KB. Adds the 32-bit
- * words of the buffer, modulo 2^32, into the device uint32 at `sink` (which
- * the caller clears first), so that the result proves every byte was read. */
-int qgemm_probe_stream_read(const void* src, int64_t bytes, void* sink, int workgroups, int chunked, void* stream);
+ * width apart, with chunked = 1 they are 8 consecutive KB. Each wave writes
+ * the sum of the 32-bit words it read, modulo 2^32, to its own uint32 of
+ * `sink` (4 * workgroups words, given as `sink_words`; wave w of the grid at
+ * sink[w]), so that the sum of the slots proves every byte was read. */
+int qgemm_probe_stream_read(const void* src, int64_t bytes, void* sink, int64_t sink_words, int workgroups,
+                            int chunked, void* stream);
 
 /* Issues `iters` x 8 matrix-core instructions per wave (x 16 for kind 4),
  * four independent accumulators per wave, from `workgroups` workgroups of 256
