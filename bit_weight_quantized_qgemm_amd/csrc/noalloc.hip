@@ -22,7 +22,8 @@
 namespace {
 
 // counters (64 KiB) plus partial sums: covers every automatic W4A16 plan
-// (the largest, 16 MiB + 64 KiB, is the wide kernel at M = 48 on 28672 x 8192)
+// (the largest, 16 MiB + 64 KiB, is the wide kernel's four k-splits at M = 65-128
+// on 28672 x 8192)
 constexpr size_t kScratchBytes = size_t(32) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 

@@ -44,10 +44,10 @@ def _reset_plan():
 
 
 def test_noalloc_matches_workspace_entry_point_twice_second_smaller():
-    # first: the down projection at M = 48, whose wide plan needs the largest
-    # split-K scratch of the automatic W4A16 plans (8 k-splits, 16 MiB of
-    # partials); second: a 7B-class layer at M = 16 (4 k-splits)
-    for (K, N, M, seed) in [(28672, 8192, 48, 5), (4096, 4096, 16, 6)]:
+    # first: the down projection at M = 128, whose wide plan needs the largest
+    # split-K scratch of the automatic W4A16 plans (4 k-splits of 128 x 8192
+    # fp32 partials, 16 MiB); second: a 7B-class layer at M = 16 (4 k-splits)
+    for (K, N, M, seed) in [(28672, 8192, 128, 5), (4096, 4096, 16, 6)]:
         pl = qg.plan_info(qg.FMT_W4A16, M, K, N)
         _say("noalloc", M, K, N, pl)
         assert pl["splits"] > 1
