@@ -2,7 +2,8 @@
 // batch range of the MARLIN abstract, where its speedup shrinks with batch size
 // but persists up to 64-128. The same kernel runs the general 4-bit grid with
 // fp16 activations (per group and column a scale and optionally a zero point;
-// the page on 2-bit LLMs on GPUs quantizes by groups and leaves the length open).
+// the abstract of the "Enabling Fast 2-bit LLM on GPUs" page quantizes weights
+// by groups without fixing their length).
 //
 // Each workgroup owns a tile of 16*MBW = 64 rows x TC = 256 columns; its eight
 // waves (two per SIMD, so one wave's dequantization and LDS reads overlap the
@@ -10,7 +11,7 @@
 // each owning 256/NWC columns and 16*MBW*NWC/8 rows. Layers whose 256-column
 // tiles would need more k-splits take 64 x 128 tiles, whose eight waves are
 // two K-parts of four (WPK) 32-column waves. Each weight is dequantized
-// by the 8/NWC row waves of its columns and reused by all of their rows. The products
+// by the WPK/NWC row waves of its columns and reused by all of their rows. The products
 // run on v_mfma_f32_32x32x16_f16, which does twice the work of the 16x16x32 form
 // for the same operand bytes and sustains a higher rate on gfx950:
 //   * operands of one 32x32x16 step: lane l holds row (A) or column (B) l % 32
