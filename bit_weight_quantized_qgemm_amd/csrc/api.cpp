@@ -449,11 +449,13 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   // M = 1-16 in 7.9-8.6 us against 10.6-11.2 us with three k-splits (W4A8 at
   // M = 16: 7.9 against 11.2 us); the cross-workgroup reduction costs more
   // than the unused CUs there. Layers whose CUs would each stream much more
-  // (28672 x 8192) keep their k-splits. The general 4-bit grid takes the same
-  // rule at 16- and 32-row tiles (one row tile): its forced-plan sweep on the
-  // same layers ranked the unsplit four-K-part shape first there.
+  // (28672 x 8192) keep their k-splits. W4A16 and the general 4-bit grid take
+  // the same rule at 32-row tiles (one row tile): 4096 x 11008 at M = 32 in
+  // 10.7 against 14.4 us with three k-splits (W4A16, one process), and the
+  // general grid's forced-plan sweep on the same layers ranked the unsplit
+  // four-K-part shape first there.
   if (have && !force_nb && !force_wpt && !force_splits && pl.mt == 1 &&
-      (((fmt == QGEMM_FMT_W4A16 || fmt == QGEMM_FMT_W4A8) && pl.mb == 1) || w4g) && G >= 4) {
+      ((fmt == QGEMM_FMT_W4A16 && pl.mb <= 2) || (fmt == QGEMM_FMT_W4A8 && pl.mb == 1) || w4g) && G >= 4) {
     const int64_t T = N / 64;
     const double extra = blob * (1.0 / (double)T - 1.0 / (double)cus);
     if (2 * T >= cus && T <= cus && extra < 96.0 * 1024.0 && !skinny_occupancy(fmt, pl.mb, 1, 4, bits, var).spills) {
