@@ -292,6 +292,21 @@ int device_cu_count() {
   return cus;
 }
 
+namespace {
+// Two 32-row tiles (M = 33..64) of W4A16, W4A8 and the 2:4 sparse format on a
+// layer of 128-column tiles whose 2 x N/128 workgroups cover between half and
+// all of the CUs, with each busy CU streaming under 96 KB more than on a launch
+// over every CU: one workgroup per tile and no k-split (see make_plan).
+bool two_row_tiles_unsplit(int fmt, int64_t M, int64_t K, int64_t N, double chunk, int cus) {
+  if (fmt != QGEMM_FMT_W4A16 && fmt != QGEMM_FMT_W4A8 && fmt != QGEMM_FMT_W4A16_SP24) return false;
+  if (M <= 32 || M > 64 || N % 128 != 0 || K / kGroup < 4) return false;
+  const int64_t T = 2 * (N / 128);
+  const double blob = (double)(K / kGroup) * (double)(N / 16) * chunk;
+  const double extra = 2.0 * blob * (1.0 / (double)T - 1.0 / (double)cus);
+  return 2 * T >= cus && T <= cus && extra < 96.0 * 1024.0;
+}
+}  // namespace
+
 Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool zeros, bool act_bf16) {
   const int force_kernel = g_force_kernel.load();
   const int cus = device_cu_count();
@@ -302,9 +317,14 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
     // narrow layers, and their partial sums then cost more than re-streaming
     // the weights once per 32-row tile of the streaming kernel (measured on
     // MI355X: 7B-class layers at M = 64..128 and N = 8192 at M = 128).
-    // (decided on the 256-column plan's k-splits)
+    // (decided on the 256-column plan's k-splits). On layers below 2^27
+    // weights at M <= 64 whose two 32-row tiles take the unsplit streaming
+    // plan, that plan measured faster (4096 x 14336 at M = 48-64: 16.3-16.4
+    // against 22.7-23.2 us; 5120 x 13824: 19.8-19.9 against 24.1-25.2 us).
     const Plan wide = make_wide_plan_nb(M, K, N, 4);
-    if (force_kernel == 2 || wide.splits <= 4 || (K * N >= (int64_t(1) << 27) && M <= 64))
+    const bool big = K * N >= (int64_t(1) << 27);
+    const bool unsplit32 = fmt == QGEMM_FMT_W4A16 && !big && two_row_tiles_unsplit(fmt, M, K, N, 1024.0, cus);
+    if (force_kernel == 2 || (!unsplit32 && (wide.splits <= 4 || (big && M <= 64))))
       return make_wide_plan(M, K, N);
   }
   // Streaming kernel: 4*KP-wave workgroups own 16*mb x 64*nb tiles; the 4
@@ -453,9 +473,11 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   // the same rule at 32-row tiles (one row tile): 4096 x 11008 at M = 32 in
   // 10.7 against 14.4 us with three k-splits (W4A16, one process), and the
   // general grid's forced-plan sweep on the same layers ranked the unsplit
-  // four-K-part shape first there.
+  // four-K-part shape first there. The 2:4 format takes it at 16-row tiles
+  // (4096 x 11008 at M = 16: 7.7 against 9.4 us with four k-splits).
   if (have && !force_nb && !force_wpt && !force_splits && pl.mt == 1 &&
-      ((fmt == QGEMM_FMT_W4A16 && pl.mb <= 2) || (fmt == QGEMM_FMT_W4A8 && pl.mb == 1) || w4g) && G >= 4) {
+      ((fmt == QGEMM_FMT_W4A16 && pl.mb <= 2) ||
+       ((fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W4A16_SP24) && pl.mb == 1) || w4g) && G >= 4) {
     const int64_t T = N / 64;
     const double extra = blob * (1.0 / (double)T - 1.0 / (double)cus);
     if (2 * T >= cus && T <= cus && extra < 96.0 * 1024.0 && !skinny_occupancy(fmt, pl.mb, 1, 4, bits, var).spills) {
@@ -469,6 +491,26 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
         best_kp = 4;
         best_s = 1;
       }
+    }
+  }
+  // Two 32-row tiles on such layers (M = 33..64): the same unsplit shape with
+  // two-block tiles, 8 waves for W4A16 (its 32 x 32 wave tiles) and 16 for
+  // W4A8 and the 2:4 format. Measured on MI355X in one process against the
+  // scored plans: 4096 x 11008 at M = 33-64 15.8-16.1 against 17.2-17.5 us
+  // (W4A16), 14.2-14.6 against 16.3-17.1 (W4A8), 13.6-14.0 against 17.4-17.8
+  // (2:4); 4096 x 14336 W4A8 14.6-15.0 against 21.7-22.4 us.
+  if (have && !force_nb && !force_wpt && !force_splits && pl.mb == 2 && pl.mt == 2 &&
+      two_row_tiles_unsplit(fmt, M, K, N, chunk, cus)) {
+    const int kp2 = fmt == QGEMM_FMT_W4A16 ? 2 : 4;
+    Plan c = pl;
+    c.kernel = var;
+    c.nb = 2;
+    c.wpt = 4 * kp2;
+    c.gps = G;
+    if (plan_lds(fmt, c, G, bits, gs, zeros) <= kSkinnyLdsBudget && !skinny_occupancy(fmt, 2, 2, kp2, bits, var).spills) {
+      best_nb = 2;
+      best_kp = kp2;
+      best_s = 1;
     }
   }
   if (!have) {   // a forced shape outside the search space: fall back to its literal values
