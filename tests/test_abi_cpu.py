@@ -534,3 +534,27 @@ def test_wide_plans_take_128_column_tiles_where_they_save_k_splits():
         assert (p["kernel"], p["nb"], p["splits"]) == (2, nb, splits), (K, N, M, p)
         assert qg.plan(qg.FMT_W4G, M, K, N) == p
         _check_plan(p, M, K, N)
+
+
+def test_unsplit_plans_on_7b_class_layers():
+    # layers whose tiles cover half to all of the CUs: one workgroup per tile and
+    # no k-split at M = 17-32 (W4A16, one 32-row tile), M = 33-64 (two 32-row
+    # tiles of W4A16, W4A8 and the 2:4 format) and M <= 16 (2:4)
+    K, N = 4096, 11008
+    for M in (17, 24, 32):
+        p = qg.plan(qg.FMT_W4A16, M, K, N)
+        assert (p["kernel"], p["mb"], p["nb"], p["wpt"], p["splits"]) == (1, 2, 1, 16, 1), (M, p)
+    for fmt, wpt in [(qg.FMT_W4A16, 8), (qg.FMT_W4A8, 16), (qg.FMT_W4A16_SP24, 16)]:
+        for M in (33, 48, 64):
+            p = qg.plan(fmt, M, K, N)
+            assert (p["kernel"], p["mb"], p["nb"], p["wpt"], p["splits"], p["mt"]) == (1, 2, 2, wpt, 1, 2), (fmt, M, p)
+            _check_plan(p, M, K, N)
+    p = qg.plan(qg.FMT_W4A16_SP24, 16, K, N)
+    assert (p["nb"], p["wpt"], p["splits"]) == (1, 16, 1)
+    # W4A16 layers below 2^27 weights leave the wide kernel for that plan
+    assert qg.plan(qg.FMT_W4A16, 48, 4096, 14336)["kernel"] == 1
+    # the 70B layers keep theirs: the wide kernel, and k-splits where each CU
+    # would stream far more than its share
+    assert qg.plan(qg.FMT_W4A16, 48, 28672, 8192)["kernel"] == 2
+    assert qg.plan(qg.FMT_W4A16_SP24, 48, 28672, 8192)["splits"] > 1
+    assert qg.plan(qg.FMT_W4A16, 16, 28672, 8192)["splits"] > 1
