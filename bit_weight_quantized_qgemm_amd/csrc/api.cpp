@@ -231,29 +231,45 @@ Plan make_wide_plan(int64_t M, int64_t K, int64_t N) {
 // whether the kernel spills to scratch. Rows: format; characters: tile shape
 // (mb, nb) = (1,1) (1,2) (2,1) (2,2), each for kp = 1, 2, 4 waves per column
 // block; 'a'..'h' = 1..8 waves and spilled, '1'..'8' = not spilled. The
-// general-grid entries are the minimum over its four variants (fp16 / bf16,
-// with or without zero points), the bit-plane rows are b = 1..8.
+// general-grid rows are per activation type, each the minimum over the
+// variants with and without zero points; the bit-plane rows are b = 1..8.
+// For the general grid the planner takes the spill flag of the call's type
+// and the waves per SIMD of the lower type: residency counted with the fp16
+// rows alone moved plans that then measured 6-12 % slower on MI355X
+// (11008 x 4096 at M = 80, 8192 x 28672 at M = 1-4), while excluding only the
+// type's own spilling instances admits the 16-wave two-block fp16 tiles
+// (8192 x 28672 at M = 24-32: 32.8-33.3 against 36.0-36.9 us).
 namespace {
 const char* const kOccW4A16 = "888555777555";   // 32-row two-block tiles: the M32 policy
 const char* const kOccW4A8 = "888555677444";
 const char* const kOccW2W4 = "666444655444";
-const char* const kOccW4G = "55544434423d";    // grid entries staged in LDS
-const char* const kOccW4GL = "55544434423d";   // grid entries loaded per lane
+const char* const kOccW4GH = "677455455344";   // fp16, grid entries staged in LDS
+const char* const kOccW4GLH = "677445455344";  // fp16, grid entries loaded per lane
+const char* const kOccW4GB = "55544434423d";   // bf16, staged
+const char* const kOccW4GLB = "55544434423d";  // bf16, per lane
 const char* const kOccSP24 = "666555555444";
 const char* const kOccBP[8] = {"888888888777", "888888788555", "888777566444", "788566455344", "67755544443d", "56645534433d", "55544434433d", "55544423d13d"};
 }  // namespace
 
-KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int kernel) {
+KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int kernel, bool act_bf16) {
+  const int idx = ((mb - 1) * 2 + (nb - 1)) * 3 + (kp == 1 ? 0 : kp == 2 ? 1 : 2);
+  auto waves = [](char ch) { return ch >= 'a' ? ch - 'a' + 1 : ch - '0'; };
+  KernelOccupancy o;
+  if (fmt == QGEMM_FMT_W4G) {
+    const char* own = kernel == 3 ? (act_bf16 ? kOccW4GLB : kOccW4GLH) : (act_bf16 ? kOccW4GB : kOccW4GH);
+    const char* other = kernel == 3 ? (act_bf16 ? kOccW4GLH : kOccW4GLB) : (act_bf16 ? kOccW4GH : kOccW4GB);
+    o.spills = own[idx] >= 'a';
+    o.waves_per_simd = std::min(waves(own[idx]), waves(other[idx]));
+    return o;
+  }
   const char* row = fmt == QGEMM_FMT_W4A16 ? kOccW4A16
                     : fmt == QGEMM_FMT_W4A8 ? kOccW4A8
                     : fmt == QGEMM_FMT_W2W4 ? kOccW2W4
-                    : fmt == QGEMM_FMT_W4G ? (kernel == 3 ? kOccW4GL : kOccW4G)
                     : fmt == QGEMM_FMT_W4A16_SP24 ? kOccSP24
                     : kOccBP[std::min(std::max(bits, 1), 8) - 1];
-  const char ch = row[((mb - 1) * 2 + (nb - 1)) * 3 + (kp == 1 ? 0 : kp == 2 ? 1 : 2)];
-  KernelOccupancy o;
+  const char ch = row[idx];
   o.spills = ch >= 'a';
-  o.waves_per_simd = o.spills ? ch - 'a' + 1 : ch - '0';
+  o.waves_per_simd = waves(ch);
   return o;
 }
 
@@ -293,12 +309,14 @@ int device_cu_count() {
 }
 
 namespace {
-// Two 32-row tiles (M = 33..64) of W4A16, W4A8 and the 2:4 sparse format on a
-// layer of 128-column tiles whose 2 x N/128 workgroups cover between half and
-// all of the CUs, with each busy CU streaming under 96 KB more than on a launch
-// over every CU: one workgroup per tile and no k-split (see make_plan).
+// Two 32-row tiles (M = 33..64) of W4A16, W4A8, the 2:4 sparse format and the
+// general grid on a layer of 128-column tiles whose 2 x N/128 workgroups cover
+// between half and all of the CUs, with each busy CU streaming under 96 KB more
+// than on a launch over every CU: one workgroup per tile and no k-split (see
+// make_plan).
 bool two_row_tiles_unsplit(int fmt, int64_t M, int64_t K, int64_t N, double chunk, int cus) {
-  if (fmt != QGEMM_FMT_W4A16 && fmt != QGEMM_FMT_W4A8 && fmt != QGEMM_FMT_W4A16_SP24) return false;
+  if (fmt != QGEMM_FMT_W4A16 && fmt != QGEMM_FMT_W4A8 && fmt != QGEMM_FMT_W4A16_SP24 && fmt != QGEMM_FMT_W4G)
+    return false;
   if (M <= 32 || M > 64 || N % 128 != 0 || K / kGroup < 4) return false;
   const int64_t T = 2 * (N / 128);
   const double blob = (double)(K / kGroup) * (double)(N / 16) * chunk;
@@ -411,7 +429,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
       for (int kp = 1; kp <= 4; kp *= 2) {
         if (force_wpt && kp != std::max(1, force_wpt / 4)) continue;
         if (kp > G) continue;
-        const KernelOccupancy occ = skinny_occupancy(fmt, pl.mb, nb, kp, bits, var);
+        const KernelOccupancy occ = skinny_occupancy(fmt, pl.mb, nb, kp, bits, var, act_bf16);
         if (occ.spills && !force_wpt) continue;
         const int smax = std::min(G, 64);
         for (int s0 = 1; s0 <= smax; ++s0) {
@@ -480,7 +498,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
        ((fmt == QGEMM_FMT_W4A8 || fmt == QGEMM_FMT_W4A16_SP24) && pl.mb == 1) || w4g) && G >= 4) {
     const int64_t T = N / 64;
     const double extra = blob * (1.0 / (double)T - 1.0 / (double)cus);
-    if (2 * T >= cus && T <= cus && extra < 96.0 * 1024.0 && !skinny_occupancy(fmt, pl.mb, 1, 4, bits, var).spills) {
+    if (2 * T >= cus && T <= cus && extra < 96.0 * 1024.0 && !skinny_occupancy(fmt, pl.mb, 1, 4, bits, var, act_bf16).spills) {
       Plan c = pl;
       c.kernel = var;
       c.nb = 1;
@@ -498,7 +516,9 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   // W4A8 and the 2:4 format. Measured on MI355X in one process against the
   // scored plans: 4096 x 11008 at M = 33-64 15.8-16.1 against 17.2-17.5 us
   // (W4A16), 14.2-14.6 against 16.3-17.1 (W4A8), 13.6-14.0 against 17.4-17.8
-  // (2:4); 4096 x 14336 W4A8 14.6-15.0 against 21.7-22.4 us.
+  // (2:4); 4096 x 14336 W4A8 14.6-15.0 against 21.7-22.4 us; the general grid
+  // (group 128, zero points, fp16) 18.1-18.4 against 21.3-21.5 us. Its bf16
+  // 16-wave two-block instance spills and keeps the scored plan.
   if (have && !force_nb && !force_wpt && !force_splits && pl.mb == 2 && pl.mt == 2 &&
       two_row_tiles_unsplit(fmt, M, K, N, chunk, cus)) {
     const int kp2 = fmt == QGEMM_FMT_W4A16 ? 2 : 4;
@@ -507,7 +527,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
     c.nb = 2;
     c.wpt = 4 * kp2;
     c.gps = G;
-    if (plan_lds(fmt, c, G, bits, gs, zeros) <= kSkinnyLdsBudget && !skinny_occupancy(fmt, 2, 2, kp2, bits, var).spills) {
+    if (plan_lds(fmt, c, G, bits, gs, zeros) <= kSkinnyLdsBudget && !skinny_occupancy(fmt, 2, 2, kp2, bits, var, act_bf16).spills) {
       best_nb = 2;
       best_kp = kp2;
       best_s = 1;

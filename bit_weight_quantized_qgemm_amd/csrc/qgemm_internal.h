@@ -97,8 +97,8 @@ struct KernelOccupancy {
   bool spills;
 };
 // register-limited occupancy of a streaming-kernel instance (tile 16*mb x 64*nb,
-// kp waves per SIMD per workgroup)
-KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int kernel);
+// kp waves per SIMD per workgroup; act_bf16 selects the general grid's bf16 rows)
+KernelOccupancy skinny_occupancy(int fmt, int mb, int nb, int kp, int bits, int kernel, bool act_bf16);
 
 // Arguments of every GEMM kernel (passed by value).
 struct GemmArgs {

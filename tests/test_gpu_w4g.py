@@ -295,3 +295,21 @@ def test_w4g_wide_70b_down_projection_m128_sampled(gs, zeros):
     z = None if p["zeros"] is None else p["zeros"][:, cols]
     ref_cols = ref.gemm_w4g(p["A"], p["codes"][:, cols], p["scales"][:, cols], z, gs, act)
     _ok(C[:, cols], ref_cols, K, act, ("70b down m128", gs, zeros))
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_w4g_7b_layer_two_row_tiles_automatic_plan(act):
+    # 4096 x 11008 at M = 48: fp16 takes the unsplit plan of two 32-row tiles
+    # (16-wave two-block workgroups); bf16, whose instance of that shape spills,
+    # keeps its scored plan. One column of every 16-column block plus a whole
+    # 128-column tile against the oracle.
+    K, N, M, gs = 4096, 11008, 48, 128
+    pl = qg.plan(qg.FMT_W4G, M, K, N, group_size=gs, zeros=True, act_dtype=qg.DT_F16 if act == "fp16" else qg.DT_BF16)
+    _say("w4g 7b two row tiles", act, pl)
+    if act == "fp16":
+        assert (pl["kernel"], pl["mb"], pl["nb"], pl["wpt"], pl["splits"]) == (1, 2, 2, 16, 1)
+    p = gen.w4g_problem(M, K, N, gs, True, act, seed=83)
+    C = _run(p)
+    cols = np.unique(np.concatenate([np.arange(7 * 128, 8 * 128), block_cols(N, seed=10)]))
+    ref_cols = ref.gemm_w4g(p["A"], p["codes"][:, cols], p["scales"][:, cols], p["zeros"][:, cols], gs, act)
+    _ok(C[:, cols], ref_cols, K, act, ("7b two row tiles", act))

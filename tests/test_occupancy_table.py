@@ -67,10 +67,12 @@ def test_occupancy_table_matches_compiler():
                 kp, pol, mb, nb = int(m.group(1)), m.group(2), int(m.group(3)), int(m.group(4))
                 kernels.setdefault(pol, {})[(mb, nb, kp)] = rep[mangled]
     policies = {"W4A16": ["PolicyW4A16"], "W4A8": ["PolicyW4A8"], "W2W4": ["PolicyW2W4"], "SP24": ["PolicySP24"],
-                "W4G": [p for p in kernels if p.startswith("PolicyW4G<") and p.endswith("true>")],
-                "W4GL": [p for p in kernels if p.startswith("PolicyW4G<") and p.endswith("false>")]}
+                "W4GH": [p for p in kernels if p.startswith("PolicyW4G<false,") and p.endswith("true>")],
+                "W4GLH": [p for p in kernels if p.startswith("PolicyW4G<false,") and p.endswith("false>")],
+                "W4GB": [p for p in kernels if p.startswith("PolicyW4G<true,") and p.endswith("true>")],
+                "W4GLB": [p for p in kernels if p.startswith("PolicyW4G<true,") and p.endswith("false>")]}
     policies.update({f"BP{b}": [f"PolicyBP<{b}>"] for b in range(1, 9)})
-    assert len(policies["W4G"]) == 4 and len(policies["W4GL"]) == 4
+    assert all(len(policies[r]) == 2 for r in ("W4GH", "W4GLH", "W4GB", "W4GLB"))
     table = _table()
     assert set(table) == set(policies)
     for row, pols in policies.items():
@@ -85,21 +87,23 @@ def test_occupancy_table_matches_compiler():
         assert table[row] == want, (row, table[row], want)
 
 
-@pytest.mark.parametrize("row", ["W4A16", "W4A8", "W2W4", "W4G", "SP24"] + [f"BP{b}" for b in range(1, 9)])
+@pytest.mark.parametrize("row", ["W4A16", "W4A8", "W2W4", "W4G", "W4G-bf16", "SP24"] + [f"BP{b}" for b in range(1, 9)])
 def test_automatic_plans_avoid_spilling_kernels(row):
     import bit_weight_quantized_qgemm_amd as qg
-    fmt = {"W4A16": qg.FMT_W4A16, "W4A8": qg.FMT_W4A8, "W2W4": qg.FMT_W2W4, "W4G": qg.FMT_W4G,
+    fmt = {"W4A16": qg.FMT_W4A16, "W4A8": qg.FMT_W4A8, "W2W4": qg.FMT_W2W4, "W4G": qg.FMT_W4G, "W4G-bf16": qg.FMT_W4G,
            "SP24": qg.FMT_W4A16_SP24}.get(row, qg.FMT_BITPLANE)
+    act = qg.DT_BF16 if row == "W4G-bf16" else qg.DT_F16
     bits = int(row[2:]) if row.startswith("BP") else 4
     for K, N in [(1024, 1024), (4096, 11008), (11008, 4096), (8192, 28672), (28672, 8192)]:
         if fmt == qg.FMT_W4A8 and K > 16384:
             continue
         for M in (1, 8, 16, 17, 32, 64, 100, 128):
-            p = qg.plan(fmt, M, K, N, bits=bits)
+            p = qg.plan(fmt, M, K, N, bits=bits, act_dtype=act)
             if p["kernel"] == 2:
                 continue
-            if row == "W4G" and p["kernel"] == 3:
-                occ = _table()["W4GL"]   # the per-lane entry variant
+            if row.startswith("W4G"):
+                h = "B" if act == qg.DT_BF16 else "H"
+                occ = _table()[("W4GL" if p["kernel"] == 3 else "W4G") + h]
             else:
                 occ = _table()[row]
             kp = p["wpt"] // 4
