@@ -513,7 +513,7 @@ Plan make_plan(int fmt, int64_t M, int64_t K, int64_t N, int bits, int gs, bool 
   }
   // Two 32-row tiles on such layers (M = 33..64): the same unsplit shape with
   // two-block tiles, 8 waves for W4A16 (its 32 x 32 wave tiles) and 16 for
-  // W4A8 and the 2:4 format. Measured on MI355X in one process against the
+  // the other formats. Measured on MI355X in one process against the
   // scored plans: 4096 x 11008 at M = 33-64 15.8-16.1 against 17.2-17.5 us
   // (W4A16), 14.2-14.6 against 16.3-17.1 (W4A8), 13.6-14.0 against 17.4-17.8
   // (2:4); 4096 x 14336 W4A8 14.6-15.0 against 21.7-22.4 us; the general grid
