@@ -23,9 +23,10 @@ steps measure that steady state.
 Prints one JSON line. ``value`` is the aggregate TFLOP/s of the timed steps;
 ``per_m`` gives each launch's mean duration over a burst of back-to-back
 launches (HIP events around the burst), its TFLOP/s and roofline fractions;
-``roofline`` describes the kernel with the largest share of the timed steps
-(algorithmic work of its launches / their time between the events that bracket
-each kernel's group of launches inside the timed steps), with
+``roofline`` describes the kernel with the largest share of a step (found in
+the warm-up steps; algorithmic work of its launches in the timed steps / their
+time between the two events that bracket its group of launches in every timed
+step), with
 ``traffic`` = HBM bytes per launch from the committed counter summary when it
 was taken on the current kernel sources; ``cpu_baseline`` times the NumPy oracle
 on a bounded sample of the same work.
@@ -544,40 +545,56 @@ def main():
         copy_probe(torch, dev, args.copy_probe_mib)
 
     print(f"[bench] inputs resident: {len(cases)} launches per step", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # ---- timed steps. Launches of one kernel run back to back (the step's
-    # order groups them), and one event closes each group, so the dominant
-    # kernel's duration comes from the timed steps themselves at a cost of a
-    # few events per step.
+    # Launches of one kernel run back to back (the step's order groups them).
+    # The warm-up steps close every group with an event to find the kernel with
+    # the largest share of a step (the last half of them, past most of the
+    # start-of-load transient); the timed steps then record two events per step
+    # only, after that kernel's group (first in the step) and at the end of the
+    # step: each timestamped event holds the next launch back by about 6 us,
+    # which one event per group would add to the step time four times over.
     groups = {}
     for j, cs in enumerate(cases):
         groups.setdefault(kernel_label(cs["plan"]), []).append(j)
     glist = list(groups.items())
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    bounds = [[ev() for _ in glist] for _ in range(args.steps)]
+    wbounds = [[ev() for _ in glist] for _ in range(args.warmup)]
+    w0 = ev()
+    w0.record(stream)
+    for i in range(args.warmup):
+        for gi, (_, idx) in enumerate(glist):
+            for j in idx:
+                launch(cases[j], i)
+            wbounds[i][gi].record(stream)
+    torch.cuda.synchronize()
+    warm_us = {}
+    for i in range(args.warmup // 2, args.warmup):
+        for gi, (label, _) in enumerate(glist):
+            start = wbounds[i][gi - 1] if gi else (wbounds[i - 1][-1] if i else w0)
+            warm_us[label] = warm_us.get(label, 0.0) + start.elapsed_time(wbounds[i][gi]) * 1e3
+    dom_label = max(warm_us, key=warm_us.get) if warm_us else glist[0][0]
+    order = [g for g in glist if g[0] == dom_label] + [g for g in glist if g[0] != dom_label]
+
+    # ---- timed steps
+    dom_end = [ev() for _ in range(args.steps)]
+    step_end = [ev() for _ in range(args.steps)]
     e0 = ev()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        for gi, (_, idx) in enumerate(glist):
+        for gi, (_, idx) in enumerate(order):
             for j in idx:
                 launch(cases[j], i)
-            bounds[i][gi].record(stream)
-    e1 = bounds[-1][-1]
+            if gi == 0:
+                dom_end[i].record(stream)
+        step_end[i].record(stream)
+    e1 = step_end[-1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     step_ms = e0.elapsed_time(e1) / args.steps
     step_flops = sum(alg_flops(c["M"], c["K"], c["N"]) for c in cases)
     value = step_flops / (step_ms * 1e-3) / 1e12
-    kernel_us = {}
-    for i in range(args.steps):
-        for gi, (label, idx) in enumerate(glist):
-            start = bounds[i][gi - 1] if gi else (bounds[i - 1][-1] if i else e0)
-            kernel_us[label] = kernel_us.get(label, 0.0) + start.elapsed_time(bounds[i][gi]) * 1e3
+    dom_us = sum((step_end[i - 1] if i else e0).elapsed_time(dom_end[i]) * 1e3 for i in range(args.steps))
 
     # ---- per-launch table: bursts of back-to-back launches of each case
     per_m = []
@@ -602,17 +619,17 @@ def main():
                       "roofline_frac": round(roof_us / us, 4), "kernel": kernel_label(cs["plan"]),
                       "plan": {k: cs["plan"][k] for k in ("mb", "nb", "wpt", "splits", "mt", "waves")}})
 
-    # ---- roofline of the dominant kernel: the one with the largest share of
-    # the timed steps; algorithmic work of its launches / their event time
-    by_kernel = {}
+    # ---- roofline of the dominant kernel (the largest share of the warm-up
+    # steps): algorithmic work of its launches in the timed steps / their
+    # event time there
+    dom = {"us": dom_us, "n": 0, "bytes": 0, "flops": 0}
     for cs in cases:
-        label = kernel_label(cs["plan"])
-        k = by_kernel.setdefault(label, {"us": kernel_us[label], "n": 0, "bytes": 0, "flops": 0})
+        if kernel_label(cs["plan"]) != dom_label:
+            continue
         M, K, N = cs["M"], cs["K"], cs["N"]
-        k["n"] += args.steps
-        k["bytes"] += alg_bytes(M, K, N) * args.steps
-        k["flops"] += alg_flops(M, K, N) * args.steps
-    dom_label, dom = max(by_kernel.items(), key=lambda kv: kv[1]["us"])
+        dom["n"] += args.steps
+        dom["bytes"] += alg_bytes(M, K, N) * args.steps
+        dom["flops"] += alg_flops(M, K, N) * args.steps
     mfma_bound = dom["flops"] / (FP16_PEAK_TFLOPS * 1e12) > dom["bytes"] / (HBM_PEAK_GBS * 1e9)
     traffic = measured_traffic(dom_label)
     if mfma_bound:
